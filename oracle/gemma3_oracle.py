@@ -1,0 +1,257 @@
+"""Plain fp64 CPU oracle of the Gemma 3 attention-block forward.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the product path.
+
+Sources (the study-note pages on Gemma 3):
+  * "Gemma 3 Attention Block", How it works: projections, QK-norm -> RoPE ->
+    query scale, left-aligned cache, the scores sum, GQA reshape, sliding mask,
+    K_MASK fill, softmax, PV, attn_vec_einsum, routing of (theta, scale).
+  * "QK-Norm", How it works: the RMSNorm equation with (1 + gamma) and
+    eps = 1e-6 over the last axis; norm before RoPE; scale after RoPE; V is
+    left alone.
+  * "Global vs Local Layer Routing", How it works: the six-slot pattern tiled
+    over depth with a prefix remainder; per-type (theta, scale).
+
+Everything is computed in float64. Inputs of any float dtype are read as their
+exact values (bf16 and fp32 are exactly representable in fp64). The method is
+exact (no approximation), so this module is the definition written out; tiled,
+online or split-KV evaluation on the GPU reaches the same result up to rounding.
+
+Readings where the pages leave a step open (each listed with its reason in the
+project's design notes):
+  * RoPE pairs channel i with channel i + d_h/2 ("half-split"), with angle
+    (p / scale) * theta^(-2i/d_h). The pages name RoPE and its (theta, scale)
+    pair but never write its formula; the pair layout is therefore a chosen
+    convention and is parity-unpinned against the pages.
+  * The RoPE scale divides the position (it is described as a positional
+    interpolation factor).
+  * gamma_Q and gamma_K are vectors of length d_h shared by all heads,
+    positions and batch rows.
+  * Query head h reads KV head h // G (the [.., H_kv, G, d_h] reshape).
+  * Prefill masks are written in token indices t, s; in decode slot s holds
+    position s (left-aligned) and the query sits at segment_pos.
+  * Weights are stored output-major: w_q [H*d_h, D], w_kv [2*H_kv*d_h, D]
+    (K heads first, then V heads), w_o [D, H*d_h]; so Q = x @ w_q.T.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Fill value for blocked logits ("Gemma 3 Attention Block", How it works, Scores).
+K_MASK = -2.3819763e38
+# RMSNorm epsilon ("QK-Norm", How it works, RMSNorm equation).
+RMS_EPS = 1e-6
+
+# AttentionType values ("Global vs Local Layer Routing", How it works).
+LOCAL_SLIDING = "LOCAL_SLIDING"
+GLOBAL = "GLOBAL"
+# Six-slot tile that starts local: (L, L, L, L, L, G).
+ATTENTION_PATTERN = (LOCAL_SLIDING,) * 5 + (GLOBAL,)
+
+
+# --------------------------------------------------------------------------
+# Routing ("Global vs Local Layer Routing", How it works)
+# --------------------------------------------------------------------------
+def layer_attn_type(layer: int, num_layers: int) -> str:
+    """type(l) = P[l mod |P|] for l = 0..N-1 (closed form on the routing page)."""
+    if not 0 <= layer < num_layers:
+        raise ValueError(f"layer {layer} out of range for depth {num_layers}")
+    return ATTENTION_PATTERN[layer % len(ATTENTION_PATTERN)]
+
+
+def layer_attn_types(num_layers: int) -> list:
+    """Whole-depth list built the way the routing page says the official config
+    does it: the pattern repeated, then a prefix pattern[:N % 6] for the rest."""
+    p = list(ATTENTION_PATTERN)
+    full, rem = divmod(num_layers, len(p))
+    return p * full + p[:rem]
+
+
+# --------------------------------------------------------------------------
+# QK-norm ("QK-Norm", How it works: RMSNorm equation)
+# --------------------------------------------------------------------------
+def rms_norm(v, gamma, eps: float = RMS_EPS):
+    """v / sqrt(mean(v^2 over the last axis) + eps) * (1 + gamma). No centring."""
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps) * (1.0 + g)
+
+
+# --------------------------------------------------------------------------
+# RoPE ("Gemma 3 Attention Block", How it works; routing page for theta/scale)
+# --------------------------------------------------------------------------
+def rope(v, pos, theta: float, scale: float):
+    """Rotate each (i, i + d_h/2) channel pair by (pos / scale) * theta^(-2i/d_h).
+
+    v: [..., d_h]; pos: broadcastable to v.shape[:-1] (integer positions).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    d_h = v.shape[-1]
+    if d_h % 2:
+        raise ValueError("RoPE needs an even head dimension")
+    half = d_h // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / d_h)
+    p = np.asarray(pos, dtype=np.float64) / scale
+    phi = p[..., None] * inv_freq
+    c, s = np.cos(phi), np.sin(phi)
+    x1, x2 = v[..., :half], v[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Projections ("Gemma 3 Attention Block", How it works: q_einsum / kv_einsum)
+# --------------------------------------------------------------------------
+def project_qkv(x, w_q, w_kv, num_heads: int, num_kv_heads: int, head_dim: int):
+    """Q [B,T,H,d_h], K and V [B,T,H_kv,d_h] from x [B,T,D]."""
+    x = np.asarray(x, dtype=np.float64)
+    w_q = np.asarray(w_q, dtype=np.float64)
+    w_kv = np.asarray(w_kv, dtype=np.float64)
+    B, T, _ = x.shape
+    q = (x @ w_q.T).reshape(B, T, num_heads, head_dim)
+    kv = x @ w_kv.T
+    n_k = num_kv_heads * head_dim
+    k = kv[..., :n_k].reshape(B, T, num_kv_heads, head_dim)
+    v = kv[..., n_k:].reshape(B, T, num_kv_heads, head_dim)
+    return q, k, v
+
+
+# --------------------------------------------------------------------------
+# Mask ("Gemma 3 Attention Block", How it works: sliding-mask equation)
+# --------------------------------------------------------------------------
+def allowed_mask(t_idx, s_idx, attn_type: str, window: int, kv_len):
+    """Boolean [len(t_idx), len(s_idx)]: causal, key padding, and on local layers
+    the sliding mask 1[s > t - W] * 1[s < t + W]."""
+    t = np.asarray(t_idx)[:, None]
+    s = np.asarray(s_idx)[None, :]
+    ok = (s <= t) & (s < kv_len)
+    if attn_type == LOCAL_SLIDING:
+        ok &= (s > t - window) & (s < t + window)
+    elif attn_type != GLOBAL:
+        raise ValueError(f"unknown attention type {attn_type!r}")
+    return ok
+
+
+def attention_core(q, k, v, allowed):
+    """One KV head and the query heads of its group.
+
+    q: [Tq, G, d_h] (already normalised, rotated and scaled), k, v: [S, d_h],
+    allowed: [Tq, S]. Blocked logits are filled with K_MASK, then a softmax over
+    s weights the rows of V. Returns o [Tq, G, d_h].
+    """
+    logits = np.einsum("tgc,sc->tgs", q, k)
+    logits = np.where(allowed[:, None, :], logits, K_MASK)
+    m = np.max(logits, axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    p = e / np.sum(e, axis=-1, keepdims=True)
+    return np.einsum("tgs,sc->tgc", p, v)
+
+
+# --------------------------------------------------------------------------
+# Prefill (the whole attention block, no cache)
+# --------------------------------------------------------------------------
+def prefill(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, *,
+            num_heads: int, num_kv_heads: int, head_dim: int,
+            attn_type: str, window: int, rope_theta: float, rope_scale: float,
+            query_scale: float, kv_valid_len=None, return_intermediates=False,
+            q_block: int = 512):
+    """y [B,T,D] of one attention layer; optionally the intermediates.
+
+    Order: projections -> RMSNorm_Q / RMSNorm_K -> RoPE -> query scale ->
+    grouped scores -> mask with K_MASK fill -> softmax -> PV -> output
+    projection ("Gemma 3 Attention Block" and "QK-Norm", How it works).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, _ = x.shape
+    H, Hk, d_h = num_heads, num_kv_heads, head_dim
+    if H % Hk:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    G = H // Hk
+    pos = np.asarray(segment_pos, dtype=np.int64).reshape(B, T)
+    lens = (np.full(B, T, dtype=np.int64) if kv_valid_len is None
+            else np.asarray(kv_valid_len, dtype=np.int64).reshape(B))
+
+    q, k, v = project_qkv(x, w_q, w_kv, H, Hk, d_h)
+    q_hat = rms_norm(q, gamma_q)
+    k_hat = rms_norm(k, gamma_k)
+    q_rope = rope(q_hat, pos[:, :, None], rope_theta, rope_scale)
+    k_rope = rope(k_hat, pos[:, :, None], rope_theta, rope_scale)
+    q_tilde = query_scale * q_rope
+
+    o = np.empty((B, T, H, d_h), dtype=np.float64)
+    s_idx = np.arange(T)
+    for b in range(B):
+        for kh in range(Hk):
+            kb = k_rope[b, :, kh, :]
+            vb = v[b, :, kh, :]
+            for t0 in range(0, T, q_block):
+                t_idx = np.arange(t0, min(T, t0 + q_block))
+                ok = allowed_mask(t_idx, s_idx, attn_type, window, lens[b])
+                qb = q_tilde[b, t_idx, kh * G:(kh + 1) * G, :]
+                o[b, t_idx, kh * G:(kh + 1) * G, :] = attention_core(qb, kb, vb, ok)
+
+    y = o.reshape(B, T, H * d_h) @ np.asarray(w_o, dtype=np.float64).T
+    if not return_intermediates:
+        return y
+    return y, dict(q=q, k=k, v=v, q_hat=q_hat, k_hat=k_hat, q_rope=q_rope,
+                   k_rope=k_rope, q_tilde=q_tilde, o=o)
+
+
+# --------------------------------------------------------------------------
+# Decode: one token against a left-aligned cache
+# ("Gemma 3 Attention Block", How it works: Cache)
+# --------------------------------------------------------------------------
+def decode(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, k_cache, v_cache, *,
+           num_heads: int, num_kv_heads: int, head_dim: int,
+           attn_type: str, window: int, rope_theta: float, rope_scale: float,
+           query_scale: float, return_intermediates=False):
+    """One decode step.
+
+    x [B,1,D]; segment_pos [B,1] = query position t_b = the slot it writes;
+    k_cache, v_cache [B,S,H_kv,d_h] hold rotated keys and values at slots
+    0..t_b-1 (slot = position). The new token's rotated key and its value go
+    to slot t_b; it then attends to slots s <= t_b (and s > t_b - W on local
+    layers). Slots past t_b get zero weight under the mask, so only slots
+    0..t_b are read. Returns y [B,1,D] and the (k, v) written at slot t_b.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, _ = x.shape
+    if T != 1:
+        raise ValueError("decode takes one token per row")
+    H, Hk, d_h = num_heads, num_kv_heads, head_dim
+    G = H // Hk
+    pos = np.asarray(segment_pos, dtype=np.int64).reshape(B)
+    S = k_cache.shape[1]
+
+    q, k, v = project_qkv(x, w_q, w_kv, H, Hk, d_h)
+    q_hat = rms_norm(q, gamma_q)
+    k_hat = rms_norm(k, gamma_k)
+    q_rope = rope(q_hat, pos[:, None, None], rope_theta, rope_scale)
+    k_rope = rope(k_hat, pos[:, None, None], rope_theta, rope_scale)
+    q_tilde = query_scale * q_rope
+
+    o = np.empty((B, 1, H, d_h), dtype=np.float64)
+    for b in range(B):
+        t = int(pos[b])
+        if not 0 <= t < S:
+            raise ValueError(f"position {t} outside the cache of length {S}")
+        s_idx = np.arange(t + 1)
+        ok = allowed_mask(np.array([t]), s_idx, attn_type, window, t + 1)
+        for kh in range(Hk):
+            kb = np.empty((t + 1, d_h), dtype=np.float64)
+            vb = np.empty((t + 1, d_h), dtype=np.float64)
+            kb[:t] = np.asarray(k_cache[b, :t, kh, :], dtype=np.float64)
+            vb[:t] = np.asarray(v_cache[b, :t, kh, :], dtype=np.float64)
+            kb[t] = k_rope[b, 0, kh]
+            vb[t] = v[b, 0, kh]
+            qb = q_tilde[b, :, kh * G:(kh + 1) * G, :]
+            o[b, :, kh * G:(kh + 1) * G, :] = attention_core(qb, kb, vb, ok)
+
+    y = o.reshape(B, 1, H * d_h) @ np.asarray(w_o, dtype=np.float64).T
+    k_new, v_new = k_rope[:, 0], v[:, 0]
+    if not return_intermediates:
+        return y, k_new, v_new
+    return y, k_new, v_new, dict(q=q, q_hat=q_hat, q_tilde=q_tilde, o=o)
