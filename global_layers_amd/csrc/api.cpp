@@ -1,0 +1,293 @@
+// C ABI of the attention library: host-side validation, workspace planning
+// and the launch sequence of each call ("Gemma 3 Attention Block", How it
+// works: projections -> QK-norm -> RoPE -> query scale -> masked grouped
+// softmax attention -> output projection; decode adds the cache write).
+//
+// Every check runs before the first enqueue, so a validation error leaves
+// the stream untouched. The library keeps no state between calls.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/gemma3_attn.h"
+#include "../../include/gemma3_attn_stages.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTokPad = 64;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int dtype) { return dtype == GEMMA3_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape / scalar validation shared by prefill and decode (S == 0: prefill).
+int check_desc(const gemma3_attn_desc *d, int32_t S) {
+  if (!d) return GEMMA3_ERR_NULL;
+  if (d->B <= 0 || d->T <= 0 || d->D <= 0 || d->H <= 0 || d->H_kv <= 0 || d->d_h <= 0)
+    return GEMMA3_ERR_SHAPE;
+  if (d->H % d->H_kv != 0 || d->d_h % 2 != 0) return GEMMA3_ERR_SHAPE;
+  if (S < 0) return GEMMA3_ERR_SHAPE;
+  if (S > 0 && d->T != 1) return GEMMA3_ERR_SHAPE;
+  if (d->dtype != GEMMA3_F32 && d->dtype != GEMMA3_BF16) return GEMMA3_ERR_DTYPE;
+  if (d->attn_type != GEMMA3_ATTN_GLOBAL && d->attn_type != GEMMA3_ATTN_LOCAL_SLIDING)
+    return GEMMA3_ERR_DTYPE;
+  if (d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING && d->window < 1) return GEMMA3_ERR_WINDOW;
+  if (!isfinite(d->rope_theta) || !isfinite(d->rope_scale) || !isfinite(d->query_scale) ||
+      d->rope_theta <= 0.f || d->rope_scale <= 0.f)
+    return GEMMA3_ERR_ROPE;
+  // int32 index budget of the kernels
+  const long n_qkv = (long)(d->H + 2 * d->H_kv) * d->d_h;
+  const long widest = n_qkv > d->D ? n_qkv : d->D;
+  const long M = (long)d->B * d->T;
+  if (M * widest >= (1L << 31) || (long)d->H * d->d_h >= (1L << 31)) return GEMMA3_ERR_UNSUPPORTED;
+  if ((long)d->T + kTokPad >= (1L << 31)) return GEMMA3_ERR_UNSUPPORTED;
+  if (d->dtype == GEMMA3_BF16) {
+    if (d->d_h != 64 && d->d_h != 128 && d->d_h != 256) return GEMMA3_ERR_UNSUPPORTED;
+    if (d->D % 64 != 0 || (d->H * d->d_h) % 64 != 0) return GEMMA3_ERR_UNSUPPORTED;
+  } else {
+    if (d->d_h > 256) return GEMMA3_ERR_UNSUPPORTED;
+  }
+  if (S > 0 && d->d_h % 64 != 0) return GEMMA3_ERR_UNSUPPORTED;  // decode: 32 channels per lane
+  return GEMMA3_OK;
+}
+
+int layout(const gemma3_attn_desc *d, int32_t S, gemma3_ws_layout *L) {
+  int st = check_desc(d, S);
+  if (st != GEMMA3_OK) return st;
+  memset(L, 0, sizeof(*L));
+  const size_t esz = elem_size(d->dtype);
+  const size_t n_qkv = (size_t)(d->H + 2 * d->H_kv) * d->d_h;
+  size_t off = 0;
+  if (S == 0) {
+    const size_t M = (size_t)d->B * d->T;
+    L->T_pad = div_up_h(d->T, kTokPad) * kTokPad;
+    L->qkv = off;
+    L->o = off;  // o reuses the raw projection buffer (dead after QK-norm)
+    off = align_up(off + M * n_qkv * esz);
+    L->q = off;
+    off = align_up(off + (size_t)d->B * d->H * d->T * d->d_h * esz);
+    L->k = off;
+    off = align_up(off + (size_t)d->B * d->H_kv * L->T_pad * d->d_h * esz);
+    L->vt = off;
+    off = align_up(off + (size_t)d->B * d->H_kv * d->d_h * L->T_pad * esz);
+  } else {
+    const bool bf = d->dtype == GEMMA3_BF16;
+    const bool local = d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING;
+    L->ksplit_qkv = bf ? gemv_ksplit((int)n_qkv, d->D) : 1;
+    L->ksplit_out = bf ? gemv_ksplit(d->D, d->H * d->d_h) : 1;
+    L->chunk = decode_chunk(local, d->window, S, d->d_h);
+    const int range = local && d->window < S ? d->window : S;
+    L->n_chunks = div_up_h(range, L->chunk);
+    L->qkv = off;
+    off = align_up(off + (size_t)L->ksplit_qkv * d->B * n_qkv * 4);
+    L->q = off;
+    off = align_up(off + (size_t)d->B * d->H * d->d_h * 4);
+    L->part = off;
+    off = align_up(off + (size_t)d->B * d->H * L->n_chunks * (d->d_h + 2) * 4);
+    L->o = off;
+    off = align_up(off + (size_t)d->B * d->H * d->d_h * esz);
+    L->ypart = off;
+    off = align_up(off + (size_t)L->ksplit_out * d->B * d->D * 4);
+  }
+  L->total_bytes = off;
+  return GEMMA3_OK;
+}
+
+int check_weights(const gemma3_attn_weights *w) {
+  if (!w || !w->w_q || !w->w_kv || !w->w_o || !w->gamma_q || !w->gamma_k) return GEMMA3_ERR_NULL;
+  if (!aligned16(w->w_q) || !aligned16(w->w_kv) || !aligned16(w->w_o)) return GEMMA3_ERR_ALIGN;
+  return GEMMA3_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GEMMA3_OK : GEMMA3_ERR_HIP; }
+
+#define RUN(expr)                              \
+  do {                                         \
+    int _st = hip_status(expr);                \
+    if (_st != GEMMA3_OK) return _st;          \
+  } while (0)
+
+template <typename T>
+int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
+                 const int32_t *kv_len, const gemma3_attn_weights *w, void *y, void *ws,
+                 const gemma3_ws_layout &L, hipStream_t s, uint32_t stages) {
+  char *base = (char *)ws;
+  T *qkv = (T *)(base + L.qkv), *o = (T *)(base + L.o);
+  T *q = (T *)(base + L.q), *k = (T *)(base + L.k), *vt = (T *)(base + L.vt);
+  const int M = d->B * d->T, Nq = d->H * d->d_h, Nkv = 2 * d->H_kv * d->d_h;
+  const bool bf = d->dtype == GEMMA3_BF16;
+
+  if (stages & GEMMA3_STAGE_QKV_PROJ) {
+    if (bf)
+      RUN(launch_gemm_bf16_nt((const bf16 *)x, (const bf16 *)w->w_q, (const bf16 *)w->w_kv, Nq,
+                              (bf16 *)qkv, M, Nq + Nkv, d->D, s));
+    else
+      RUN(launch_gemm_f32_nt((const float *)x, (const float *)w->w_q, (const float *)w->w_kv, Nq,
+                             (float *)qkv, M, Nq + Nkv, d->D, s));
+  }
+  if (stages & GEMMA3_STAGE_QK_NORM) {
+    NormRopeArgs a{d->B, d->T, d->H, d->H_kv, d->d_h, L.T_pad,
+                   d->rope_theta, d->rope_scale, d->query_scale};
+    RUN(launch_qk_norm_rope<T>(qkv, pos, (const T *)w->gamma_q, (const T *)w->gamma_k, q, k, vt,
+                               a, s));
+  }
+  if (stages & GEMMA3_STAGE_ATTN) {
+    AttnArgs a{d->B, d->T, d->H, d->H_kv, d->d_h, L.T_pad,
+               d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window};
+    if (bf)
+      RUN(launch_flash_attn_bf16((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, kv_len,
+                                 (bf16 *)o, a, s));
+    else
+      RUN(launch_attn_f32((const float *)q, (const float *)k, (const float *)vt, kv_len,
+                          (float *)o, a, s));
+  }
+  if (stages & GEMMA3_STAGE_OUT_PROJ) {
+    if (bf)
+      RUN(launch_gemm_bf16_nt((const bf16 *)o, (const bf16 *)w->w_o, (const bf16 *)w->w_o, d->D,
+                              (bf16 *)y, M, d->D, Nq, s));
+    else
+      RUN(launch_gemm_f32_nt((const float *)o, (const float *)w->w_o, (const float *)w->w_o, d->D,
+                             (float *)y, M, d->D, Nq, s));
+  }
+  return GEMMA3_OK;
+}
+
+template <typename T>
+int decode_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
+                const gemma3_attn_weights *w, void *kc, void *vc, int32_t S, void *y, void *ws,
+                const gemma3_ws_layout &L, hipStream_t s, uint32_t stages) {
+  char *base = (char *)ws;
+  float *pqkv = (float *)(base + L.qkv), *qf = (float *)(base + L.q);
+  float *part = (float *)(base + L.part), *ypart = (float *)(base + L.ypart);
+  T *o = (T *)(base + L.o);
+  const int B = d->B, Nq = d->H * d->d_h, Nkv = 2 * d->H_kv * d->d_h;
+  const bool bf = d->dtype == GEMMA3_BF16;
+
+  if (stages & GEMMA3_DSTAGE_QKV_PROJ) {
+    if (bf)
+      RUN(launch_gemv16_bf16((const bf16 *)x, (const bf16 *)w->w_q, (const bf16 *)w->w_kv, Nq,
+                             pqkv, B, Nq + Nkv, d->D, L.ksplit_qkv, s));
+    else
+      RUN(launch_gemv_f32((const float *)x, (const float *)w->w_q, (const float *)w->w_kv, Nq,
+                          pqkv, B, Nq + Nkv, d->D, s));
+  }
+  if (stages & GEMMA3_DSTAGE_QK_NORM) {
+    NormRopeArgs a{B, 1, d->H, d->H_kv, d->d_h, 0, d->rope_theta, d->rope_scale, d->query_scale};
+    RUN(launch_qk_norm_rope_decode<T>(pqkv, L.ksplit_qkv, pos, (const T *)w->gamma_q,
+                                      (const T *)w->gamma_k, qf, (T *)kc, (T *)vc, S, a, s));
+  }
+  if (stages & GEMMA3_DSTAGE_ATTN) {
+    DecodeArgs a{B, d->H, d->H_kv, d->d_h, S,
+                 d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window, L.chunk,
+                 L.n_chunks};
+    RUN(launch_decode_attn<T>(qf, (const T *)kc, (const T *)vc, pos, part, o, a, s));
+  }
+  if (stages & GEMMA3_DSTAGE_OUT_PROJ) {
+    if (bf)
+      RUN(launch_gemv16_bf16((const bf16 *)o, (const bf16 *)w->w_o, (const bf16 *)w->w_o, d->D,
+                             ypart, B, d->D, Nq, L.ksplit_out, s));
+    else
+      RUN(launch_gemv_f32((const float *)o, (const float *)w->w_o, (const float *)w->w_o, d->D,
+                          ypart, B, d->D, Nq, s));
+    RUN(launch_splitk_reduce<T>(ypart, L.ksplit_out, (T *)y, (long)B * d->D, s));
+  }
+  return GEMMA3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemma3_attn_abi_version(void) { return GEMMA3_ATTN_ABI_VERSION; }
+
+const char *gemma3_attn_status_string(int status) {
+  switch (status) {
+    case GEMMA3_OK: return "ok";
+    case GEMMA3_ERR_NULL: return "a required pointer is NULL";
+    case GEMMA3_ERR_SHAPE: return "invalid shape (non-positive size, H % H_kv != 0, odd d_h, or T != 1 in decode)";
+    case GEMMA3_ERR_WINDOW: return "local layer needs window >= 1";
+    case GEMMA3_ERR_DTYPE: return "unknown dtype or attention type";
+    case GEMMA3_ERR_ROPE: return "rope_theta and rope_scale must be finite and > 0, query_scale finite";
+    case GEMMA3_ERR_WORKSPACE: return "workspace is NULL or smaller than gemma3_attn_workspace_bytes()";
+    case GEMMA3_ERR_UNSUPPORTED: return "shape has no kernel in this build";
+    case GEMMA3_ERR_HIP: return "a HIP kernel launch failed";
+    case GEMMA3_ERR_ALIGN: return "pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int gemma3_layer_attn_type(int32_t layer, int32_t num_layers) {
+  if (layer < 0 || layer >= num_layers) return -1;
+  // six-slot tile (L, L, L, L, L, G): slot 5 of every tile is global
+  return (layer % 6 == 5) ? GEMMA3_ATTN_GLOBAL : GEMMA3_ATTN_LOCAL_SLIDING;
+}
+
+int gemma3_attn_workspace_layout(const gemma3_attn_desc *desc, int32_t S, gemma3_ws_layout *out) {
+  if (!out) return GEMMA3_ERR_NULL;
+  return layout(desc, S, out);
+}
+
+size_t gemma3_attn_workspace_bytes(const gemma3_attn_desc *desc, int32_t S) {
+  gemma3_ws_layout L;
+  return layout(desc, S, &L) == GEMMA3_OK ? L.total_bytes : 0;
+}
+
+int gemma3_attn_prefill_stages(const gemma3_attn_desc *desc, const void *x,
+                               const int32_t *segment_pos, const int32_t *kv_valid_len,
+                               const gemma3_attn_weights *w, void *y, void *workspace,
+                               size_t workspace_bytes, void *hip_stream, uint32_t stages) {
+  gemma3_ws_layout L;
+  int st = layout(desc, 0, &L);
+  if (st != GEMMA3_OK) return st;
+  if (!x || !segment_pos || !y) return GEMMA3_ERR_NULL;
+  if ((st = check_weights(w)) != GEMMA3_OK) return st;
+  if (!aligned16(x) || !aligned16(y)) return GEMMA3_ERR_ALIGN;
+  if (!workspace || workspace_bytes < L.total_bytes) return GEMMA3_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (desc->dtype == GEMMA3_BF16)
+    return prefill_impl<bf16>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s, stages);
+  return prefill_impl<float>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s, stages);
+}
+
+int gemma3_attn_prefill(const gemma3_attn_desc *desc, const void *x, const int32_t *segment_pos,
+                        const int32_t *kv_valid_len, const gemma3_attn_weights *w, void *y,
+                        void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return gemma3_attn_prefill_stages(desc, x, segment_pos, kv_valid_len, w, y, workspace,
+                                    workspace_bytes, hip_stream, GEMMA3_STAGE_ALL);
+}
+
+int gemma3_attn_decode_stages(const gemma3_attn_desc *desc, const void *x,
+                              const int32_t *segment_pos, const gemma3_attn_weights *w,
+                              void *k_cache, void *v_cache, int32_t S, void *y, void *workspace,
+                              size_t workspace_bytes, void *hip_stream, uint32_t stages) {
+  if (S < 1) return desc ? GEMMA3_ERR_SHAPE : GEMMA3_ERR_NULL;
+  gemma3_ws_layout L;
+  int st = layout(desc, S, &L);
+  if (st != GEMMA3_OK) return st;
+  if (!x || !segment_pos || !y || !k_cache || !v_cache) return GEMMA3_ERR_NULL;
+  if ((st = check_weights(w)) != GEMMA3_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache))
+    return GEMMA3_ERR_ALIGN;
+  if ((long)desc->B * S * desc->H_kv * desc->d_h >= (1L << 62)) return GEMMA3_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < L.total_bytes) return GEMMA3_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (desc->dtype == GEMMA3_BF16)
+    return decode_impl<bf16>(desc, x, segment_pos, w, k_cache, v_cache, S, y, workspace, L, s,
+                             stages);
+  return decode_impl<float>(desc, x, segment_pos, w, k_cache, v_cache, S, y, workspace, L, s,
+                            stages);
+}
+
+int gemma3_attn_decode(const gemma3_attn_desc *desc, const void *x, const int32_t *segment_pos,
+                       const gemma3_attn_weights *w, void *k_cache, void *v_cache, int32_t S,
+                       void *y, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return gemma3_attn_decode_stages(desc, x, segment_pos, w, k_cache, v_cache, S, y, workspace,
+                                   workspace_bytes, hip_stream, GEMMA3_DSTAGE_ALL);
+}
+
+}  // extern "C"

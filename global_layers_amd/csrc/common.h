@@ -1,0 +1,65 @@
+// Shared device helpers for the gfx950 attention kernels: element types,
+// MFMA operand vectors, bf16 conversion and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define DEVI __device__ __forceinline__
+
+constexpr int kWave = 64;
+
+DEVI float to_f32(float v) { return v; }
+DEVI float to_f32(bf16 v) { return (float)v; }
+
+template <typename T> DEVI T from_f32(float v);
+template <> DEVI float from_f32<float>(float v) { return v; }
+template <> DEVI bf16 from_f32<bf16>(float v) { return (bf16)v; }  // round to nearest even
+
+// 16-byte vector load/store helpers (addresses must be 16-byte aligned).
+DEVI u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+DEVI void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+DEVI float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+DEVI float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sum over aligned groups of `n` lanes (n a power of two <= 64).
+template <int n> DEVI float group_sum(float v) {
+#pragma unroll
+  for (int o = n / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+DEVI int div_up(int a, int b) { return (a + b - 1) / b; }
+
+// Remap a linear block id so that runs of consecutive logical ids land on the
+// same XCD: the dispatcher deals workgroups round-robin over the 8 XCDs, so
+// physical id p runs on XCD p % 8. Ids past the largest multiple of 8 keep
+// their own value.
+DEVI int xcd_remap(int p, int n) {
+  const int full = n & ~7;
+  if (p >= full) return p;
+  const int per = full >> 3;
+  return (p & 7) * per + (p >> 3);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;

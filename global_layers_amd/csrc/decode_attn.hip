@@ -1,0 +1,309 @@
+// Decode attention against a left-aligned KV cache ("Gemma 3 Attention
+// Block", How it works: the step's K and V land in the cache at the query's
+// position; the query then attends to cached positions s <= pos, and on local
+// layers only to s > pos - W; softmax over those slots mixes V).
+//
+// HBM-bound split-KV evaluation of that softmax:
+//  * The allowed slot range [lo, pos] of row b is cut into chunks of C slots.
+//    One workgroup streams one (row, chunk, KV head): K and V rows of that
+//    head, d_h contiguous elements per slot, 16-byte loads, each byte read once
+//    for all the query heads of the GQA group.
+//  * Inside a wave, d_h/32 lanes share one slot (32 channels each); per-slot
+//    logits are a short xor-shuffle sum. Each slot group keeps an online
+//    softmax state (m, l, acc) per query head; groups and waves are merged by
+//    log-sum-exp, and the chunk's (acc, m, l) go to the workspace.
+//  * A second kernel merges the chunks of each (row, head) the same way and
+//    divides by the total weight. Logits are in log2 units (q pre-scaled by
+//    log2 e), so every exponential is an exp2.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecUnroll = 4;  // slots per slot group per iteration
+constexpr int kChansPerLane = 32;
+
+template <typename T> struct LoadVec;
+template <> struct LoadVec<bf16> {
+  static DEVI void load(const bf16 *p, float (&out)[kChansPerLane]) {
+#pragma unroll
+    for (int i = 0; i < kChansPerLane / 8; ++i) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, ld16(p + 8 * i));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[8 * i + j] = (float)v[j];
+    }
+  }
+};
+template <> struct LoadVec<float> {
+  static DEVI void load(const float *p, float (&out)[kChansPerLane]) {
+#pragma unroll
+    for (int i = 0; i < kChansPerLane / 4; ++i) {
+      const f32x4 v = __builtin_bit_cast(f32x4, ld16(p + 4 * i));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[4 * i + j] = v[j];
+    }
+  }
+};
+
+DEVI void row_range(const int32_t *pos, int b, int S, int local, int window, int &lo, int &hi) {
+  const int p = pos[b];
+  if (p < 0 || p >= S) {
+    lo = 0;
+    hi = -1;
+    return;
+  }
+  hi = p;
+  lo = local ? max(0, p - window + 1) : 0;
+}
+
+// grid: x = chunk, y = b, z = kh * n_hgrp + head group. GQ query heads per workgroup.
+template <typename T, int D, int GQ>
+__global__ void __launch_bounds__(kDecThreads)
+decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
+                    const T *__restrict__ v_cache, const int32_t *__restrict__ pos,
+                    float *__restrict__ part, DecodeArgs a, int n_hgrp) {
+  constexpr int LPS = D / kChansPerLane;         // lanes per slot
+  constexpr int kGroupsPerWave = kWave / LPS;
+  constexpr int NG = kGroupsPerWave * (kDecThreads / kWave);
+  __shared__ float red[kDecThreads / kWave][GQ][D + 2];
+
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const int kh = blockIdx.z / n_hgrp, hgrp = blockIdx.z % n_hgrp;
+  const int G = a.H / a.Hk;
+  const int h0 = kh * G + hgrp * GQ;
+  int lo, hi;
+  row_range(pos, b, a.S, a.local, a.window, lo, hi);
+  const int c_lo = lo + chunk * a.chunk;
+  if (c_lo > hi) return;  // chunk past this row's range (uniform per block)
+  const int c_hi = min(hi, c_lo + a.chunk - 1);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % LPS;             // which 32-channel slice
+  const int grp = wave * kGroupsPerWave + lane / LPS;
+  const int c0 = sub * kChansPerLane;
+
+  float qv[GQ][kChansPerLane];
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    const float *qp = q + ((size_t)b * a.H + h0 + g) * D + c0;
+#pragma unroll
+    for (int i = 0; i < kChansPerLane; ++i) qv[g][i] = qp[i] * kLog2e;
+  }
+  float m[GQ], l[GQ], acc[GQ][kChansPerLane];
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kChansPerLane; ++i) acc[g][i] = 0.f;
+  }
+
+  const size_t slot_stride = (size_t)a.Hk * D;
+  const T *kb = k_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D + c0;
+  const T *vb = v_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D + c0;
+
+  for (int s_base = c_lo + grp; s_base <= c_hi; s_base += NG * kDecUnroll) {
+    float x[kDecUnroll][GQ];
+    bool ok[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int s = s_base + u * NG;
+      ok[u] = s <= c_hi;
+      float kv[kChansPerLane];
+      if (ok[u]) {
+        LoadVec<T>::load(kb + (size_t)s * slot_stride, kv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kChansPerLane; ++i) kv[i] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < kChansPerLane; ++i) d = fmaf(qv[g][i], kv[i], d);
+        x[u][g] = d;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u)
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) {
+        const float d = group_sum<LPS>(x[u][g]);
+        x[u][g] = ok[u] ? d : -INFINITY;
+      }
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) mx = fmaxf(mx, x[u][g]);
+      // at least slot s_base is valid, so mx is finite
+      const float corr = exp2f(m[g] - mx);
+      m[g] = mx;
+      l[g] *= corr;
+#pragma unroll
+      for (int i = 0; i < kChansPerLane; ++i) acc[g][i] *= corr;
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) {
+        x[u][g] = exp2f(x[u][g] - mx);
+        l[g] += x[u][g];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      if (!ok[u]) continue;
+      float vv[kChansPerLane];
+      LoadVec<T>::load(vb + (size_t)(s_base + u * NG) * slot_stride, vv);
+#pragma unroll
+      for (int g = 0; g < GQ; ++g)
+#pragma unroll
+        for (int i = 0; i < kChansPerLane; ++i) acc[g][i] = fmaf(x[u][g], vv[i], acc[g][i]);
+    }
+  }
+
+  // merge the slot groups of this wave (lanes with equal `sub` hold equal channels)
+#pragma unroll
+  for (int off = LPS; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      const float mo = __shfl_xor(m[g], off, kWave);
+      const float lo_ = __shfl_xor(l[g], off, kWave);
+      const float mn = fmaxf(m[g], mo);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float ea = exp2f(m[g] - mu), eb = exp2f(mo - mu);
+      m[g] = mn;
+      l[g] = l[g] * ea + lo_ * eb;
+#pragma unroll
+      for (int i = 0; i < kChansPerLane; ++i) {
+        const float ao = __shfl_xor(acc[g][i], off, kWave);
+        acc[g][i] = acc[g][i] * ea + ao * eb;
+      }
+    }
+  }
+  if (lane < LPS) {
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+#pragma unroll
+      for (int i = 0; i < kChansPerLane; ++i) red[wave][g][c0 + i] = acc[g][i];
+      if (lane == 0) {
+        red[wave][g][D] = m[g];
+        red[wave][g][D + 1] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < GQ * D; e += kDecThreads) {
+    const int g = e / D, c = e % D;
+    float mn = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < kDecThreads / kWave; ++wv) mn = fmaxf(mn, red[wv][g][D]);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    float sa = 0.f, sl = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kDecThreads / kWave; ++wv) {
+      const float wgt = exp2f(red[wv][g][D] - mu);
+      sa += wgt * red[wv][g][c];
+      sl += wgt * red[wv][g][D + 1];
+    }
+    float *pp = part + (((size_t)b * a.H + h0 + g) * a.n_chunks + chunk) * (D + 2);
+    pp[c] = sa;
+    if (c == 0) {
+      pp[D] = mn;
+      pp[D + 1] = sl;
+    }
+  }
+}
+
+// grid: x = H, y = B; one thread per channel.
+template <typename T, int D>
+__global__ void __launch_bounds__(D)
+decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos,
+                    T *__restrict__ o, DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  int lo, hi;
+  row_range(pos, b, a.S, a.local, a.window, lo, hi);
+  const int n = hi >= lo ? div_up(hi - lo + 1, a.chunk) : 0;
+  const float *pp = part + ((size_t)b * a.H + h) * a.n_chunks * (D + 2);
+  float mn = -INFINITY;
+  for (int j = 0; j < n; ++j) mn = fmaxf(mn, pp[(size_t)j * (D + 2) + D]);
+  const float mu = mn == -INFINITY ? 0.f : mn;
+  float sa = 0.f, sl = 0.f;
+  for (int j = 0; j < n; ++j) {
+    const float *e = pp + (size_t)j * (D + 2);
+    const float wgt = exp2f(e[D] - mu);
+    sa += wgt * e[c];
+    sl += wgt * e[D + 1];
+  }
+  o[((size_t)b * a.H + h) * D + c] = from_f32<T>(sl > 0.f ? sa / sl : 0.f);
+}
+
+template <typename T, int D, int GQ>
+hipError_t launch_dec(const float *q, const T *kc, const T *vc, const int32_t *pos, float *part,
+                      T *o, const DecodeArgs &a, hipStream_t s) {
+  const int G = a.H / a.Hk;
+  const int n_hgrp = G / GQ;
+  dim3 grid(a.n_chunks, a.B, a.Hk * n_hgrp);
+  hipLaunchKernelGGL((decode_attn_partial<T, D, GQ>), grid, dim3(kDecThreads), 0, s, q, kc, vc,
+                     pos, part, a, n_hgrp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_attn_combine<T, D>), dim3(a.H, a.B), dim3(D), 0, s, part, pos, o, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dec_g(const float *q, const T *kc, const T *vc, const int32_t *pos,
+                        float *part, T *o, const DecodeArgs &a, hipStream_t s) {
+  const int G = a.H / a.Hk;
+  if (G % 4 == 0) return launch_dec<T, D, 4>(q, kc, vc, pos, part, o, a, s);
+  if (G % 2 == 0) return launch_dec<T, D, 2>(q, kc, vc, pos, part, o, a, s);
+  return launch_dec<T, D, 1>(q, kc, vc, pos, part, o, a, s);
+}
+
+template <typename T>
+__global__ void splitk_reduce(const float *__restrict__ part, int ksplit, T *__restrict__ y,
+                              long MN) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < MN;
+       i += (long)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int sp = 0; sp < ksplit; ++sp) s += part[(size_t)sp * MN + i];
+    y[i] = from_f32<T>(s);
+  }
+}
+
+}  // namespace
+
+int decode_chunk(int local, int window, int S, int d_h) {
+  (void)d_h;
+  if (local) return 64;
+  return S >= 32768 ? 512 : 128;
+}
+
+template <typename T>
+hipError_t launch_decode_attn(const float *q, const T *k_cache, const T *v_cache,
+                              const int32_t *pos, float *part, T *o, const DecodeArgs &a,
+                              hipStream_t s) {
+  switch (a.d_h) {
+    case 64: return launch_dec_g<T, 64>(q, k_cache, v_cache, pos, part, o, a, s);
+    case 128: return launch_dec_g<T, 128>(q, k_cache, v_cache, pos, part, o, a, s);
+    case 256: return launch_dec_g<T, 256>(q, k_cache, v_cache, pos, part, o, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_splitk_reduce(const float *part, int ksplit, T *y, long MN, hipStream_t s) {
+  const int nb = div_up_h(MN, 256);
+  const int blocks = nb < 2048 ? nb : 2048;
+  hipLaunchKernelGGL(splitk_reduce<T>, dim3(blocks), dim3(256), 0, s, part, ksplit, y, MN);
+  return hipGetLastError();
+}
+
+template hipError_t launch_decode_attn<bf16>(const float *, const bf16 *, const bf16 *,
+                                             const int32_t *, float *, bf16 *,
+                                             const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode_attn<float>(const float *, const float *, const float *,
+                                              const int32_t *, float *, float *,
+                                              const DecodeArgs &, hipStream_t);
+template hipError_t launch_splitk_reduce<bf16>(const float *, int, bf16 *, long, hipStream_t);
+template hipError_t launch_splitk_reduce<float>(const float *, int, float *, long, hipStream_t);

@@ -1,0 +1,73 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+
+static inline int div_up_h(long a, long b) { return (int)((a + b - 1) / b); }
+
+// The weight operand of every projection is given as two row blocks: rows
+// [0, N0) come from B0 and rows [N0, N) from B1 (W_q and W_kv are separate
+// caller buffers that together form the [Q|K|V] projection).
+// K1: C[M,N] (bf16) = A[M,K] * B[N,K]^T; K % 64 == 0, 16-byte aligned rows.
+hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C,
+                               int M, int N, int K, hipStream_t s);
+// K1d: P[ksplit][M][N] (fp32 partials) = A[M,K] * W[N,K]^T per K split; K % (32 ksplit) == 0.
+int gemv_ksplit(int N, int K);
+hipError_t launch_gemv16_bf16(const bf16 *A, const bf16 *W0, const bf16 *W1, int N0, float *P,
+                              int M, int N, int K, int ksplit, hipStream_t s);
+
+// Arguments shared by the norm/RoPE kernels.
+struct NormRopeArgs {
+  int B, T, H, Hk, d_h, T_pad;
+  float theta, scale, alpha;
+};
+
+// K2 (prefill): reads raw [B*T, (H+2Hk) d_h] projections; writes q [B,H,T,d_h]
+// (normalised, rotated, times alpha), k [B,Hk,T_pad,d_h], vt [B,Hk,d_h,T_pad].
+template <typename T>
+hipError_t launch_qk_norm_rope(const T *qkv, const int32_t *pos, const T *gamma_q,
+                               const T *gamma_k, T *q, T *k, T *vt, const NormRopeArgs &a,
+                               hipStream_t s);
+
+// K2d (decode): sums ksplit fp32 partials [ksplit][B][(H+2Hk) d_h]; q -> fp32 [B,H,d_h];
+// rotated k and v -> cache slot pos[b] of [B,S,Hk,d_h].
+template <typename T>
+hipError_t launch_qk_norm_rope_decode(const float *part, int ksplit, const int32_t *pos,
+                                      const T *gamma_q, const T *gamma_k, float *q, T *k_cache,
+                                      T *v_cache, int S, const NormRopeArgs &a, hipStream_t s);
+
+// K3 (prefill attention, bf16).
+struct AttnArgs {
+  int B, T, H, Hk, d_h, T_pad;
+  int local, window;
+};
+hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
+                                  const int32_t *kv_len, bf16 *o, const AttnArgs &a,
+                                  hipStream_t s);
+
+// K4 + K4c (decode attention): split-KV partials then combine into o [B, H*d_h].
+struct DecodeArgs {
+  int B, H, Hk, d_h, S;
+  int local, window;
+  int chunk, n_chunks;
+};
+int decode_chunk(int local, int window, int S, int d_h);
+template <typename T>
+hipError_t launch_decode_attn(const float *q, const T *k_cache, const T *v_cache,
+                              const int32_t *pos, float *part, T *o, const DecodeArgs &a,
+                              hipStream_t s);
+
+// Sum of fp32 split partials [ksplit][M][N] into y [M][N].
+template <typename T>
+hipError_t launch_splitk_reduce(const float *part, int ksplit, T *y, long MN, hipStream_t s);
+
+// K5: fp32 path (correctness grade).
+hipError_t launch_gemm_f32_nt(const float *A, const float *B0, const float *B1, int N0, float *C,
+                              int M, int N, int K, hipStream_t s);
+hipError_t launch_attn_f32(const float *q, const float *k, const float *vt,
+                           const int32_t *kv_len, float *o, const AttnArgs &a, hipStream_t s);
+hipError_t launch_gemv_f32(const float *A, const float *W0, const float *W1, int N0, float *P,
+                           int M, int N, int K, hipStream_t s);

@@ -1,0 +1,163 @@
+/*
+ * gemma3_attn.h -- C ABI of the MI355X (gfx950) Gemma 3 attention-block forward.
+ *
+ * What it computes (study-note pages on Gemma 3):
+ *   "Gemma 3 Attention Block", How it works: Q = q_einsum(x), K,V = kv_einsum(x);
+ *     RMSNorm on Q and on K, then RoPE with the layer's (theta, scale), then the
+ *     query scale alpha; grouped scores sum_c Q[t,h,c] K[s,h/G,c]; causal and
+ *     padding mask, times the sliding mask 1[s > t-W] 1[s < t+W] on local
+ *     layers, blocked entries filled with K_MASK = -2.3819763e38; softmax over
+ *     s; weights mix V; attn_vec_einsum maps heads back to D. A decode step
+ *     writes the new K and V into a left-aligned cache and attends to it.
+ *   "QK-Norm", How it works: RMSNorm(v) = v / sqrt(mean(v^2) + 1e-6) * (1 + gamma)
+ *     over the head dimension, separate gammas for Q and K, V not normalised,
+ *     applied before RoPE; alpha applied after RoPE.
+ *   "Global vs Local Layer Routing", How it works: layer l has type
+ *     P[l mod 6] with P = (L, L, L, L, L, G); local layers use theta = 1e4,
+ *     scale 1 and the window; global layers theta = 1e6 and scale 8 (or 1 on
+ *     the 1B/270M sizes). This ABI takes the resolved (type, W, theta, scale).
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *   - RoPE pairs channel i with channel i + d_h/2; channel pair i turns by
+ *     (pos / scale) * theta^(-2i/d_h) radians: (a, b) -> (a cos - b sin, b cos + a sin).
+ *   - gamma_q, gamma_k are [d_h] vectors shared by every head and position.
+ *   - Query head h reads KV head h / G, G = H / H_kv.
+ *   - Prefill masks use token indices (t, s); segment_pos only feeds RoPE.
+ *     Key s of batch row b is padding when s >= kv_valid_len[b].
+ *   - Decode: cache slot s holds position s (left-aligned); the query of row b
+ *     sits at pos_b = segment_pos[b] and its rotated key and its value are
+ *     written to slot pos_b before attending to slots s <= pos_b (and
+ *     s > pos_b - W on local layers).
+ *   - A row with no allowed key (unreachable with causal masks: key t itself,
+ *     or key 0, is always allowed unless kv_valid_len[b] == 0) outputs 0
+ *     instead of the fill-value result (uniform mean over all keys).
+ *
+ * Layouts (all row-major, element type per desc.dtype):
+ *   x            [B, T, D]
+ *   segment_pos  [B, T] int32                      (device)
+ *   kv_valid_len [B] int32 or NULL = all T valid   (device)
+ *   w_q          [H*d_h, D]       output-major: row h*d_h + c is head h, channel c
+ *   w_kv         [2*H_kv*d_h, D]  rows 0..H_kv*d_h-1 are K heads, then V heads
+ *   w_o          [D, H*d_h]       y[., j] = sum_n o[., n] * w_o[j, n]
+ *   gamma_q, gamma_k [d_h]
+ *   y            [B, T, D]
+ *   k_cache, v_cache [B, S, H_kv, d_h]  (decode only)
+ *
+ * Ownership and threading: every pointer is a DEVICE pointer unless noted;
+ * the caller owns every buffer, the library allocates nothing, keeps no
+ * pointer after it returns and holds no global state. Work is enqueued on
+ * `hip_stream` (a hipStream_t, NULL = the default stream) and the call
+ * returns without synchronising; buffers must stay alive until the stream
+ * passes the work. y must not alias an input; the workspace must not alias
+ * anything else. Calls on different streams need different workspaces.
+ *
+ * Errors: every call returns a gemma3_status. All host-side validation runs
+ * before the first enqueue, so on any status other than GEMMA3_OK and
+ * GEMMA3_ERR_HIP nothing was enqueued. GEMMA3_ERR_HIP means a launch failed
+ * (outputs undefined). The library never aborts, prints or synchronises.
+ * Preconditions on device data that the host cannot see without a sync:
+ * 0 <= kv_valid_len[b] <= T, 0 <= segment_pos[b] < S in decode; a decode
+ * position outside [0, S) makes that row skip its cache write and output 0.
+ */
+#ifndef GEMMA3_ATTN_H
+#define GEMMA3_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMMA3_ATTN_ABI_VERSION 1
+
+/* AttentionType ("Global vs Local Layer Routing", How it works). */
+typedef enum { GEMMA3_ATTN_GLOBAL = 0, GEMMA3_ATTN_LOCAL_SLIDING = 1 } gemma3_attn_type;
+
+/* Element type of x, weights, gammas, y and the cache. Accumulation is fp32. */
+typedef enum { GEMMA3_F32 = 0, GEMMA3_BF16 = 1 } gemma3_dtype;
+
+typedef enum {
+  GEMMA3_OK = 0,
+  GEMMA3_ERR_NULL = 1,        /* a required pointer is NULL */
+  GEMMA3_ERR_SHAPE = 2,       /* non-positive size, H % H_kv != 0, odd d_h, T != 1 in decode */
+  GEMMA3_ERR_WINDOW = 3,      /* local layer with window < 1 */
+  GEMMA3_ERR_DTYPE = 4,       /* unknown dtype or attention type */
+  GEMMA3_ERR_ROPE = 5,        /* theta <= 0, scale <= 0, or a non-finite theta/scale/alpha */
+  GEMMA3_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gemma3_attn_workspace_bytes */
+  GEMMA3_ERR_UNSUPPORTED = 7, /* valid shape this build has no kernel for (see below) */
+  GEMMA3_ERR_HIP = 8,         /* a kernel launch failed */
+  GEMMA3_ERR_ALIGN = 9        /* a pointer is not 16-byte aligned */
+} gemma3_status;
+
+/* One attention layer. All sizes are element counts. */
+typedef struct {
+  int32_t B, T, D, H, H_kv, d_h; /* T == 1 for decode; H % H_kv == 0; d_h even */
+  int32_t attn_type;             /* gemma3_attn_type */
+  int32_t window;                /* W >= 1 when LOCAL_SLIDING; ignored when GLOBAL */
+  float rope_theta;              /* theta > 0 */
+  float rope_scale;              /* > 0; RoPE positions are divided by it */
+  float query_scale;             /* alpha (e.g. d_h^-1/2, or (D/H)^-1/2 for 27B shapes), finite */
+  int32_t dtype;                 /* gemma3_dtype */
+} gemma3_attn_desc;
+
+/* Weights of one layer (device pointers, layouts above, element type dtype). */
+typedef struct {
+  const void *w_q;
+  const void *w_kv;
+  const void *w_o;
+  const void *gamma_q;
+  const void *gamma_k;
+} gemma3_attn_weights;
+
+/*
+ * Shapes with kernels in this build:
+ *   GEMMA3_BF16: d_h in {64, 128, 256}; D % 64 == 0; H*d_h % 64 == 0;
+ *                B*T < 2^31 / max(D, (H + 2 H_kv) d_h); H / H_kv <= 8.
+ *   GEMMA3_F32:  d_h even and <= 256; any D, H, H_kv, B, T within int32.
+ * Anything else valid returns GEMMA3_ERR_UNSUPPORTED.
+ */
+
+/* Bytes of device workspace prefill (S == 0) or decode (S = cache length)
+ * needs for this descriptor; 0 when the descriptor is invalid. */
+size_t gemma3_attn_workspace_bytes(const gemma3_attn_desc *desc, int32_t S);
+
+/*
+ * Prefill: y = Attention(x) for every token of every row, no cache
+ * ("Gemma 3 Attention Block", How it works, S = T). Masks: causal on token
+ * indices, keys s >= kv_valid_len[b] blocked, and on local layers keys
+ * s <= t - W blocked. segment_pos feeds RoPE only.
+ */
+int gemma3_attn_prefill(const gemma3_attn_desc *desc, const void *x,
+                        const int32_t *segment_pos, const int32_t *kv_valid_len,
+                        const gemma3_attn_weights *w, void *y, void *workspace,
+                        size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Decode: one token per row against a left-aligned cache of S slots
+ * ("Gemma 3 Attention Block", How it works, Cache). Writes the rotated key
+ * and the value of row b into k_cache/v_cache slot segment_pos[b], then
+ * attends to slots 0..segment_pos[b] (global) or the last W of them (local).
+ * Slots past segment_pos[b] are never read (they may hold anything, NaN included).
+ */
+int gemma3_attn_decode(const gemma3_attn_desc *desc, const void *x,
+                       const int32_t *segment_pos, const gemma3_attn_weights *w,
+                       void *k_cache, void *v_cache, int32_t S, void *y,
+                       void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Host-only routing helper ("Global vs Local Layer Routing", How it works):
+ * type of layer `layer` in a stack of `num_layers`: P[layer mod 6] with
+ * P = (L, L, L, L, L, G). Returns -1 when layer is outside [0, num_layers). */
+int gemma3_layer_attn_type(int32_t layer, int32_t num_layers);
+
+/* Static, never-NULL description of a status code. */
+const char *gemma3_attn_status_string(int status);
+
+/* GEMMA3_ATTN_ABI_VERSION of the built library. */
+int gemma3_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMA3_ATTN_H */

@@ -142,12 +142,13 @@ def attention_core(q, k, v, allowed):
     allowed: [Tq, S]. Blocked logits are filled with K_MASK, then a softmax over
     s weights the rows of V. Returns o [Tq, G, d_h].
     """
-    logits = np.einsum("tgc,sc->tgs", q, k)
+    Tq, G, d_h = q.shape
+    logits = (q.reshape(Tq * G, d_h) @ k.T).reshape(Tq, G, -1)   # sum over c
     logits = np.where(allowed[:, None, :], logits, K_MASK)
     m = np.max(logits, axis=-1, keepdims=True)
     e = np.exp(logits - m)
     p = e / np.sum(e, axis=-1, keepdims=True)
-    return np.einsum("tgs,sc->tgc", p, v)
+    return (p.reshape(Tq * G, -1) @ v).reshape(Tq, G, d_h)        # sum over s
 
 
 # --------------------------------------------------------------------------
@@ -157,13 +158,24 @@ def prefill(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, *,
             num_heads: int, num_kv_heads: int, head_dim: int,
             attn_type: str, window: int, rope_theta: float, rope_scale: float,
             query_scale: float, kv_valid_len=None, return_intermediates=False,
-            q_block: int = 512):
+            q_block: int = 512, query_rows=None):
     """y [B,T,D] of one attention layer; optionally the intermediates.
 
     Order: projections -> RMSNorm_Q / RMSNorm_K -> RoPE -> query scale ->
     grouped scores -> mask with K_MASK fill -> softmax -> PV -> output
     projection ("Gemma 3 Attention Block" and "QK-Norm", How it works).
+
+    query_rows: optional sorted token indices; then only those rows of y are
+    computed (y is [B, len(query_rows), D]) and keys are projected only over
+    the index range some selected row may see. Exact whenever every selected
+    row has at least one allowed key (a row with none would average V over
+    all T keys, which this mode does not reproduce).
     """
+    if query_rows is not None:
+        return _prefill_rows(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k,
+                             np.asarray(query_rows), num_heads, num_kv_heads, head_dim,
+                             attn_type, window, rope_theta, rope_scale, query_scale,
+                             kv_valid_len)
     x = np.asarray(x, dtype=np.float64)
     B, T, _ = x.shape
     H, Hk, d_h = num_heads, num_kv_heads, head_dim
@@ -198,6 +210,44 @@ def prefill(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, *,
         return y
     return y, dict(q=q, k=k, v=v, q_hat=q_hat, k_hat=k_hat, q_rope=q_rope,
                    k_rope=k_rope, q_tilde=q_tilde, o=o)
+
+
+def _prefill_rows(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, rows, H, Hk, d_h,
+                  attn_type, window, rope_theta, rope_scale, query_scale, kv_valid_len):
+    """Selected query rows of prefill (same steps as the full computation)."""
+    B, T, _ = x.shape
+    G = H // Hk
+    rows = np.unique(rows)
+    if rows[0] < 0 or rows[-1] >= T:
+        raise ValueError("query row out of range")
+    lens = (np.full(B, T, dtype=np.int64) if kv_valid_len is None
+            else np.asarray(kv_valid_len, dtype=np.int64).reshape(B))
+    k_hi = int(rows[-1])
+    k_lo = max(0, int(rows[0]) - window + 1) if attn_type == LOCAL_SLIDING else 0
+    s_idx = np.arange(k_lo, k_hi + 1)
+    pos = np.asarray(segment_pos, dtype=np.int64).reshape(B, T)
+    w_q = np.asarray(w_q, dtype=np.float64)
+    w_kv = np.asarray(w_kv, dtype=np.float64)
+    n_k = Hk * d_h
+    y = np.empty((B, len(rows), np.asarray(w_o).shape[0]), dtype=np.float64)
+    for b in range(B):
+        xq = np.asarray(x[b, rows], dtype=np.float64)
+        xk = np.asarray(x[b, k_lo:k_hi + 1], dtype=np.float64)
+        q = (xq @ w_q.T).reshape(len(rows), H, d_h)
+        kv = xk @ w_kv.T
+        k = kv[:, :n_k].reshape(-1, Hk, d_h)
+        v = kv[:, n_k:].reshape(-1, Hk, d_h)
+        q_t = query_scale * rope(rms_norm(q, gamma_q), pos[b, rows][:, None], rope_theta,
+                                 rope_scale)
+        k_r = rope(rms_norm(k, gamma_k), pos[b, k_lo:k_hi + 1][:, None], rope_theta,
+                   rope_scale)
+        ok = allowed_mask(rows, s_idx, attn_type, window, lens[b])
+        o = np.empty((len(rows), H, d_h), dtype=np.float64)
+        for kh in range(Hk):
+            o[:, kh * G:(kh + 1) * G] = attention_core(q_t[:, kh * G:(kh + 1) * G],
+                                                       k_r[:, kh], v[:, kh], ok)
+        y[b] = o.reshape(len(rows), H * d_h) @ np.asarray(w_o, dtype=np.float64).T
+    return y
 
 
 # --------------------------------------------------------------------------

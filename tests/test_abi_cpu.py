@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the public headers declare, and host validation returns each status before
+anything is enqueued (fake device addresses are never dereferenced on these
+paths)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from global_layers_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in ("gemma3_attn.h", "gemma3_attn_stages.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(gemma3_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"gemma3_attn_prefill", "gemma3_attn_decode", "gemma3_attn_workspace_bytes",
+            "gemma3_layer_attn_type", "gemma3_attn_status_string"} <= names
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(so, n), f"{n} declared but not exported"
+    assert set(lib.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings():
+    assert lib.abi_version() == 1
+    for st in range(10):
+        assert lib._lib.gemma3_attn_status_string(st)
+    assert lib._lib.gemma3_attn_status_string(99) == b"unknown status"
+
+
+def test_layer_routing_helper():
+    for n in (1, 5, 6, 7, 26, 34, 48, 62):
+        types = [lib.layer_attn_type(l, n) for l in range(n)]
+        assert types[0] == lib.LOCAL_SLIDING
+        assert all((t == lib.GLOBAL) == (l % 6 == 5) for l, t in enumerate(types))
+        assert types.count(lib.GLOBAL) == n // 6
+    assert lib.layer_attn_type(-1, 6) == -1 and lib.layer_attn_type(6, 6) == -1
+
+
+def _desc(**kw):
+    d = dict(B=1, T=128, D=256, H=4, H_kv=1, d_h=64, attn_type="LOCAL_SLIDING", window=32,
+             rope_theta=1e4, rope_scale=1.0, query_scale=0.125, dtype=lib.BF16)
+    d.update(kw)
+    return lib.make_desc(**d)
+
+
+FAKE = 1 << 40  # 16-byte aligned address never touched by the validation paths
+
+
+def _call_prefill(desc, ws_bytes=None, x=FAKE, pos=FAKE, y=FAKE, ws=FAKE, weights=None):
+    w = weights or lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    n = lib.workspace_bytes(desc) if ws_bytes is None else ws_bytes
+    return lib._lib.gemma3_attn_prefill(ctypes.byref(desc), x, pos, None, ctypes.byref(w), y, ws,
+                                        n, None)
+
+
+def _call_decode(desc, S=1024, ws_bytes=None, kc=FAKE, vc=FAKE):
+    w = lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    n = lib.workspace_bytes(desc, S) if ws_bytes is None else ws_bytes
+    return lib._lib.gemma3_attn_decode(ctypes.byref(desc), FAKE, FAKE, ctypes.byref(w), kc, vc,
+                                       S, FAKE, FAKE, n, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(T=-1), 2), (dict(D=0), 2), (dict(H=0), 2), (dict(H_kv=0), 2),
+    (dict(H=6, H_kv=4), 2), (dict(d_h=63), 2),
+    (dict(attn_type=7), 4), (dict(dtype=5), 4),
+    (dict(window=0), 3), (dict(window=-3), 3),
+    (dict(rope_theta=0.0), 5), (dict(rope_scale=-1.0), 5), (dict(rope_theta=float("inf")), 5),
+    (dict(query_scale=float("nan")), 5),
+    (dict(d_h=96), 7), (dict(D=100), 7), (dict(d_h=512), 7),
+    (dict(d_h=300, dtype=lib.F32), 7),
+])
+def test_prefill_validation_status(kw, status):
+    assert _call_prefill(_desc(**kw), ws_bytes=1 << 40) == status
+    if status != 7:
+        assert lib.workspace_bytes(_desc(**kw)) == 0
+
+
+def test_prefill_pointer_workspace_alignment_errors():
+    d = _desc()
+    assert lib._lib.gemma3_attn_prefill(None, FAKE, FAKE, None, None, FAKE, FAKE, 1, None) == 1
+    assert _call_prefill(d, x=None) == 1
+    assert _call_prefill(d, pos=None) == 1
+    assert _call_prefill(d, y=None) == 1
+    assert _call_prefill(d, weights=lib.Weights(FAKE, None, FAKE, FAKE, FAKE)) == 1
+    assert _call_prefill(d, ws=None) == 6
+    assert _call_prefill(d, ws_bytes=lib.workspace_bytes(d) - 1) == 6
+    assert _call_prefill(d, x=FAKE + 2) == 9
+    assert _call_prefill(d, ws=FAKE + 8) == 9
+    assert _call_prefill(d, weights=lib.Weights(FAKE, FAKE + 4, FAKE, FAKE, FAKE)) == 9
+
+
+def test_global_layer_ignores_window():
+    d = _desc(attn_type="GLOBAL", window=0)
+    assert lib.workspace_bytes(d) > 0
+
+
+def test_decode_validation_status():
+    d = _desc(T=1, d_h=128, H=4, H_kv=2, D=256)
+    assert _call_decode(d, S=0) == 2
+    assert _call_decode(_desc(T=2, d_h=128), S=16) == 2
+    assert _call_decode(d, ws_bytes=16) == 6
+    assert _call_decode(d, kc=None) == 1
+    assert _call_decode(d, vc=FAKE + 2) == 9
+    assert _call_decode(_desc(T=1, d_h=32, dtype=lib.F32, D=64), S=8, ws_bytes=1 << 30) == 7
+
+
+def test_workspace_layout_prefill_and_decode():
+    d = _desc(B=2, T=100, D=128, H=4, H_kv=2, d_h=64)
+    L = lib.workspace_layout(d, 0)
+    assert L.T_pad == 128
+    esz, n_qkv = 2, (4 + 4) * 64
+    assert L.q >= 2 * 100 * n_qkv * esz and L.q % 256 == 0
+    assert L.k >= L.q + 2 * 4 * 100 * 64 * esz
+    assert L.vt >= L.k + 2 * 2 * 128 * 64 * esz
+    assert L.total_bytes >= L.vt + 2 * 2 * 64 * 128 * esz
+    dd = _desc(B=16, T=1, D=3840, H=16, H_kv=8, d_h=256, attn_type="GLOBAL", window=0)
+    Ld = lib.workspace_layout(dd, 131072)
+    assert Ld.n_chunks * Ld.chunk >= 131072
+    assert (3840 // 32) % Ld.ksplit_qkv == 0 and (4096 // 32) % Ld.ksplit_out == 0
+    dl = _desc(B=16, T=1, D=3840, H=16, H_kv=8, d_h=256, window=1024)
+    Ll = lib.workspace_layout(dl, 131072)
+    assert Ll.n_chunks * Ll.chunk >= 1024 and Ll.total_bytes < Ld.total_bytes

@@ -1,0 +1,210 @@
+"""GPU parity of prefill: HIP path (through the C ABI) vs the fp64 oracle on the
+same seeded inputs. Small cases cover every kernel variant with ragged tails;
+the workload cases run at full size (all rows for the 1B-shaped pair, sampled
+rows for the 4B-like tile and the 27B-shaped pair)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from workloads import inputs as I
+from parity_util import (assert_bf16_close, assert_f32_close, f64, gpu_prefill, layer_kw, log,
+                         oracle_prefill, small_prefill_inputs, to_dev, weights_of)
+
+pytestmark = pytest.mark.gpu
+
+L, G = "LOCAL_SLIDING", "GLOBAL"
+
+SMALL_BF16 = [
+    # B, T, D, H, Hk, d_h, type, W, lens. D = H * d_h as in the workloads (the
+    # output scale, and with it the bf16 storage error of y, grows with
+    # sqrt(H * d_h / D)).
+    (1, 200, 256, 4, 1, 64, L, 33, None),
+    (2, 333, 512, 4, 2, 128, G, 0, None),
+    (2, 257, 512, 2, 2, 256, L, 64, (257, 200)),
+    (1, 300, 1024, 8, 1, 128, G, 0, None),
+    (1, 130, 192, 3, 1, 64, L, 1, None),
+    (3, 64, 1024, 4, 4, 256, G, 0, (64, 1, 33)),
+    (1, 1, 256, 2, 1, 128, G, 0, None),
+    (2, 129, 1024, 4, 2, 256, L, 500, None),
+    (1, 520, 1024, 4, 1, 256, L, 128, None),
+    (1, 700, 1024, 8, 4, 128, G, 0, (650,)),
+]
+
+
+def _kw(H, Hk, d_h, t, Wn, theta=1e4, scale=1.0, alpha=None):
+    return dict(H=H, H_kv=Hk, d_h=d_h, attn_type=t, window=Wn, rope_theta=theta,
+                rope_scale=scale, query_scale=d_h ** -0.5 if alpha is None else alpha)
+
+
+@pytest.mark.parametrize("case", SMALL_BF16, ids=[str(c[:8]) for c in SMALL_BF16])
+def test_prefill_bf16_small(gpu_lib, case):
+    B, T, D, H, Hk, d_h, t, Wn, lens = case
+    log(f"case {case}")
+    inp = small_prefill_inputs(1, B, T, D, H, Hk, d_h, "bf16", lens)
+    kw = _kw(H, Hk, d_h, t, Wn, theta=1e6 if t == G else 1e4, scale=8.0 if t == G else 1.0)
+    y = gpu_prefill(gpu_lib, inp, kw)
+    assert_bf16_close(f64(y), oracle_prefill(inp, kw), "y")
+
+
+@pytest.mark.parametrize("case", [(1, 77, 100, 3, 1, 32, L, 9, None),
+                                  (2, 150, 256, 4, 2, 64, G, 0, (150, 90)),
+                                  (1, 65, 96, 2, 2, 256, L, 20, None)])
+def test_prefill_fp32_small(gpu_lib, case):
+    B, T, D, H, Hk, d_h, t, Wn, lens = case
+    log(f"case {case}")
+    inp = small_prefill_inputs(2, B, T, D, H, Hk, d_h, "f32", lens)
+    kw = _kw(H, Hk, d_h, t, Wn)
+    y = gpu_prefill(gpu_lib, inp, kw)
+    assert_f32_close(f64(y), oracle_prefill(inp, kw), "y")
+
+
+def test_cfg1_fp32_local_layer(gpu_lib):
+    w = W.WORKLOADS[1]
+    inp = I.prefill_inputs(w, 0)
+    kw = layer_kw(w, w.layers[0])
+    y = gpu_prefill(gpu_lib, inp, kw)
+    assert_f32_close(f64(y), oracle_prefill(inp, kw), "cfg1 y")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_intermediates(gpu_lib, dtype):
+    """Q (normalised, rotated, times alpha), K (normalised, rotated) and V^T in
+    the workspace against the oracle's intermediates; padding rows are zero."""
+    B, T, D, H, Hk, d_h = 2, 100, 128, 4, 2, 128
+    inp = small_prefill_inputs(3, B, T, D, H, Hk, d_h, dtype)
+    inp["segment_pos"] = inp["segment_pos"] + torch.tensor([[0], [131071 - T]], dtype=torch.int32)
+    kw = _kw(H, Hk, d_h, G, 0, theta=1e6, scale=8.0, alpha=0.3)
+    d = to_dev(inp)
+    desc = gpu_lib.make_desc(B=B, T=T, D=D, dtype=d["x"].dtype, **kw)
+    ws = gpu_lib.new_workspace(desc)
+    gpu_lib.prefill(d["x"], d["segment_pos"], weights_of(d), workspace=ws,
+                    stages=gpu_lib.STAGE_QKV_PROJ | gpu_lib.STAGE_QK_NORM, **kw)
+    torch.cuda.synchronize()
+    it_gpu = gpu_lib.prefill_intermediates(ws, desc)
+    _, it = oracle_prefill(inp, kw, return_intermediates=True)
+    Tp = it_gpu["T_pad"]
+    q = f64(it_gpu["q"]).transpose(0, 2, 1, 3)           # -> [B,T,H,d]
+    k = f64(it_gpu["k"])[:, :, :T].transpose(0, 2, 1, 3)
+    v = f64(it_gpu["vt"])[:, :, :, :T].transpose(0, 3, 1, 2)
+    check = assert_bf16_close if dtype == "bf16" else (
+        lambda g, r, n: assert_f32_close(g, r, n, atol=2e-5))
+    check(q, it["q_tilde"], "q")
+    check(k, it["k_rope"], "k")
+    check(v, it["v"], "v")
+    assert np.all(f64(it_gpu["k"])[:, :, T:Tp] == 0) and np.all(f64(it_gpu["vt"])[..., T:Tp] == 0)
+
+
+def test_cfg2_full_both_layers(gpu_lib):
+    w = W.WORKLOADS[2]
+    for li, layer in enumerate(w.layers):
+        log(f"cfg2 layer {li} {layer}")
+        inp = I.prefill_inputs(w, li)
+        kw = layer_kw(w, layer)
+        y = gpu_prefill(gpu_lib, inp, kw)
+        assert_bf16_close(f64(y), oracle_prefill(inp, kw), f"cfg2 layer {li} y")
+
+
+def _sampled(gpu_lib, w, layer_ids, rows):
+    x_cache = None
+    for li in layer_ids:
+        layer = w.layers[li]
+        log(f"cfg{w.cfg_id} layer {li} {layer.attn_type}")
+        inp = I.prefill_inputs(w, li)
+        if x_cache is None:
+            x_cache = inp["x"]
+        inp["x"] = x_cache
+        kw = layer_kw(w, layer)
+        y = f64(gpu_prefill(gpu_lib, inp, kw))
+        if layer.attn_type == L:  # one window per row keeps the oracle cheap
+            r = np.concatenate([oracle_prefill(inp, kw, rows=[t]) for t in rows], axis=1)
+        else:
+            r = oracle_prefill(inp, kw, rows=rows)
+        assert_bf16_close(y[:, rows], r, f"cfg{w.cfg_id} layer {li} sampled y")
+        del y
+
+
+@pytest.mark.slow
+def test_cfg3_sampled_rows_all_layers(gpu_lib):
+    rows = [0, 5, 511, 1023, 1024, 2047, 4096, 7000, 7782, 7783, 7800, 8191]
+    _sampled(gpu_lib, W.WORKLOADS[3], range(6), rows)
+
+
+@pytest.mark.slow
+def test_cfg4_sampled_rows(gpu_lib):
+    rows = [0, 1, 127, 1023, 1024, 9999, 16383, 32640, 32767]
+    _sampled(gpu_lib, W.WORKLOADS[4], range(2), rows)
+
+
+# ---------------------------------------------------------------- structure
+def test_window_at_least_T_is_bitwise_global(gpu_lib):
+    B, T, D, H, Hk, d_h = 1, 600, 128, 4, 1, 256
+    inp = small_prefill_inputs(4, B, T, D, H, Hk, d_h, "bf16")
+    yg = gpu_prefill(gpu_lib, inp, _kw(H, Hk, d_h, G, 0))
+    for Wn in (T, T + 1, 1 << 20):
+        yl = gpu_prefill(gpu_lib, inp, _kw(H, Hk, d_h, L, Wn))
+        assert torch.equal(yl, yg)
+    assert not torch.equal(gpu_prefill(gpu_lib, inp, _kw(H, Hk, d_h, L, T - 1)), yg)
+
+
+def _attn_core_only(gpu_lib, inp, kw):
+    d = to_dev(inp)
+    B, T, D = d["x"].shape
+    desc = gpu_lib.make_desc(B=B, T=T, D=D, dtype=d["x"].dtype, **kw)
+    ws = gpu_lib.new_workspace(desc)
+    gpu_lib.prefill(d["x"], d["segment_pos"], weights_of(d), kv_valid_len=d["kv_valid_len"],
+                    workspace=ws, stages=gpu_lib.STAGE_ALL & ~gpu_lib.STAGE_OUT_PROJ, **kw)
+    torch.cuda.synchronize()
+    return gpu_lib.prefill_intermediates(ws, desc)
+
+
+@pytest.mark.parametrize("d_h,Hk", [(64, 1), (128, 2), (256, 1)])
+def test_window_one_returns_v(gpu_lib, d_h, Hk):
+    B, T, D, H = 2, 190, 128, 4
+    inp = small_prefill_inputs(5, B, T, D, H, Hk, d_h, "bf16")
+    it = _attn_core_only(gpu_lib, inp, _kw(H, Hk, d_h, L, 1))
+    o = it["o"].float()                                        # [B,T,H,d]
+    v = it["vt"][..., :T].float().permute(0, 3, 1, 2)          # [B,T,Hk,d]
+    assert torch.equal(o, v.repeat_interleave(H // Hk, dim=2))
+
+
+@pytest.mark.parametrize("t,Wn,lens", [(L, 37, None), (G, 0, (300, 123)), (L, 200, (300, 250))])
+def test_zero_query_scale_gives_window_mean(gpu_lib, t, Wn, lens):
+    """alpha = 0: o_t is the mean of V over the allowed keys (exact window count)."""
+    B, T, D, H, Hk, d_h = 2, 300, 128, 4, 2, 128
+    inp = small_prefill_inputs(6, B, T, D, H, Hk, d_h, "bf16", lens)
+    it = _attn_core_only(gpu_lib, inp, _kw(H, Hk, d_h, t, Wn, alpha=0.0))
+    o = f64(it["o"])
+    v = f64(it["vt"])[..., :T].transpose(0, 3, 1, 2)
+    cs = np.concatenate([np.zeros((B, 1, Hk, d_h)), np.cumsum(v, axis=1)], axis=1)
+    exp = np.empty_like(o)
+    for b in range(B):
+        Lb = T if lens is None else lens[b]
+        for tt in range(T):
+            lo = max(0, tt - Wn + 1) if t == L else 0
+            hi = min(tt, Lb - 1)
+            m = (cs[b, hi + 1] - cs[b, lo]) / (hi - lo + 1)
+            exp[b, tt] = np.repeat(m, H // Hk, axis=0)
+    err = np.abs(o - exp).max()
+    log(f"  max err {err:.3g}")
+    assert err <= 1e-2 * np.abs(exp).max() + 4e-3
+
+
+def test_position_shift_matches_oracle(gpu_lib):
+    """Positions near 131071 (RoPE large-angle precision)."""
+    B, T, D, H, Hk, d_h = 1, 256, 256, 4, 2, 256
+    inp = small_prefill_inputs(7, B, T, D, H, Hk, d_h, "bf16")
+    inp["segment_pos"] = inp["segment_pos"] + (131071 - T + 1)
+    kw = _kw(H, Hk, d_h, G, 0, theta=1e4, scale=1.0)
+    y = gpu_prefill(gpu_lib, inp, kw)
+    assert_bf16_close(f64(y), oracle_prefill(inp, kw), "shifted y")
+
+
+def test_bitwise_deterministic(gpu_lib):
+    w = W.WORKLOADS[2]
+    inp = I.prefill_inputs(w, 1)
+    kw = layer_kw(w, w.layers[1])
+    ys = [gpu_prefill(gpu_lib, inp, kw) for _ in range(3)]
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])

@@ -470,3 +470,18 @@ def test_local_decode_short_history_equals_global():
     np.testing.assert_array_equal(y_l, y_g)
     y_w = _decode_from_prefill(O.LOCAL_SLIDING, 11, 1e4, 1.0)[0]
     assert np.max(np.abs(y_w - y_g)) > 1e-6
+
+
+# ---------------------------------------------------------------- sampled rows
+@pytest.mark.parametrize("attn_type,W,lens", [(O.LOCAL_SLIDING, 4, (17, 14)),
+                                              (O.GLOBAL, 0, (17, 9))])
+def test_sampled_rows_equal_full(attn_type, W, lens):
+    B, T, D, H, Hk, d_h = 2, 17, 16, 4, 2, 8
+    x = _rand(35, B, T, D)
+    w = _layer(36, D, H, Hk, d_h)
+    kw = dict(num_heads=H, num_kv_heads=Hk, head_dim=d_h, attn_type=attn_type, window=W,
+              rope_theta=1e4, rope_scale=1.0, query_scale=0.4, kv_valid_len=lens)
+    full = _prefill(x, w, **kw)
+    for rows in ([0], [16], [3, 9, 16], [5, 6, 7, 8]):
+        part = _prefill(x, w, query_rows=rows, **kw)
+        np.testing.assert_allclose(part, full[:, rows], rtol=1e-12, atol=1e-14)
