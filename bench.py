@@ -1,0 +1,334 @@
+"""Benchmark of the Gemma 3 attention-block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+
+A step is one prefill pass of the Gemma-3-1B-shaped pair of layers (one local,
+one global; B=1, T=4096, D=1152, H=4, H_kv=1, d_h=256, W=512, bf16) through
+the C ABI, inputs resident in HBM. `value` is the whole-call algorithmic
+TFLOP/s of that step: 2*M*N*K for the three projections plus 4*d_h*H per
+allowed (query, key) pair, never the masked or skipped pairs.
+
+The same run also times the decode step of the 12B-like shape (B=16,
+D=3840, H=16, H_kv=8, d_h=256, bf16 cache of 131072 slots, seeded lengths),
+as a global and as a local (W=1024) layer, reporting algorithmic GB/s
+(allowed KV slots, weights, x, y, cache write) with the 256 MB Infinity Cache
+flushed between repetitions; per-stage kernel times from HIP events on the
+launch stream; the roofline entry of the dominant kernel; and the fp64 oracle
+timed on the host cores as a reported CPU baseline.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--decode-reps", type=int, default=20)
+    p.add_argument("--stage-reps", type=int, default=20)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ work counts
+def allowed_pairs(T, attn_type, window, kv_len):
+    import numpy as np
+    t = np.arange(T)
+    hi = np.minimum(t, kv_len - 1)
+    lo = np.maximum(0, t - window + 1) if attn_type == "LOCAL_SLIDING" else np.zeros_like(t)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def prefill_flops(w, layer):
+    M = w.B * w.T
+    n_qkv = (w.H + 2 * w.H_kv) * w.d_h
+    proj = 2 * M * w.D * n_qkv + 2 * M * (w.H * w.d_h) * w.D
+    lens = w.kv_valid_len() or (w.T,) * w.B
+    pairs = sum(allowed_pairs(w.T, layer.attn_type, w.window, L) for L in lens)
+    attn = 4 * w.d_h * w.H * pairs
+    return proj, attn
+
+
+def decode_bytes(w, layer, lengths):
+    n = [min(int(L), w.window) if layer.attn_type == "LOCAL_SLIDING" else int(L)
+         for L in lengths]
+    kv = sum(n) * w.H_kv * w.d_h * 2 * 2
+    n_qkv = (w.H + 2 * w.H_kv) * w.d_h
+    weights = (n_qkv * w.D + w.D * w.H * w.d_h + 2 * w.d_h) * 2
+    io = 2 * w.B * w.D * 2 + w.B * w.H_kv * w.d_h * 2 * 2
+    return kv, weights + io
+
+
+# ------------------------------------------------------------------ helpers
+def stream_events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the "
+              "multi-GPU sharding is a design note, not an implemented path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads import inputs as I
+    from global_layers_amd import lib
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} CUs {props.multi_processor_count}")
+
+    # ---------------------------------------------------------------- prefill
+    w = W.WORKLOADS[2]
+    layers = []
+    x = I.prefill_x(w).to(dev)
+    pos = I.prefill_positions(w).to(dev)
+    for li, layer in enumerate(w.layers):
+        wts = {k: v.to(dev) for k, v in I.layer_weights(w, li).items()}
+        kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
+                  rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
+                  query_scale=w.query_scale)
+        desc = lib.make_desc(B=w.B, T=w.T, D=w.D, dtype=torch.bfloat16, **kw)
+        ws = lib.new_workspace(desc, 0, dev)
+        y = torch.empty((w.B, w.T, w.D), dtype=torch.bfloat16, device=dev)
+        proj, attn = prefill_flops(w, layer)
+        layers.append(dict(layer=layer, wts=wts, kw=kw, ws=ws, y=y, proj=proj, attn=attn))
+    step_flops = sum(L["proj"] + L["attn"] for L in layers)
+
+    def step():
+        for L in layers:
+            lib.prefill(x, pos, L["wts"], workspace=L["ws"], y=L["y"], **L["kw"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = stream_events(torch)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"prefill step {ms_per_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall) "
+        f"-> {value:.1f} TFLOP/s ({value / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
+
+    # per-stage kernel times (events on the launch stream, each stage repeated alone)
+    stage_names = {lib.STAGE_QKV_PROJ: "qkv_proj", lib.STAGE_QK_NORM: "qk_norm_rope",
+                   lib.STAGE_ATTN: "attention", lib.STAGE_OUT_PROJ: "out_proj"}
+    stage_ms = {n: 0.0 for n in stage_names.values()}
+    per_layer = []
+    for L in layers:
+        row = {}
+        for bit, name in stage_names.items():
+            a, b = stream_events(torch)
+            a.record()
+            for _ in range(args.stage_reps):
+                lib.prefill(x, pos, L["wts"], workspace=L["ws"], y=L["y"], stages=bit,
+                            **L["kw"])
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.stage_reps
+            row[name] = ms
+            stage_ms[name] += ms
+        per_layer.append(row)
+        log(f"  {L['layer'].attn_type:13s} " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in row.items()))
+    step()  # leave the workspaces consistent
+    torch.cuda.synchronize()
+
+    proj_flops = {"qkv_proj": sum(2 * w.B * w.T * w.D * (w.H + 2 * w.H_kv) * w.d_h
+                                  for _ in layers),
+                  "out_proj": sum(2 * w.B * w.T * w.H * w.d_h * w.D for _ in layers),
+                  "attention": sum(L["attn"] for L in layers)}
+    dominant = max(stage_ms, key=stage_ms.get)
+    if dominant in proj_flops:
+        ach = proj_flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:  # the norm/RoPE pass is HBM-bound
+        nbytes = sum(w.B * w.T * (w.H + 2 * w.H_kv) * w.d_h * 2 * 2 for _ in layers)
+        ach = nbytes / (stage_ms[dominant] * 1e-3) / 1e9
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(ach, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                    "traffic": None}
+    attn_tflops = proj_flops["attention"] / (stage_ms["attention"] * 1e-3) / 1e12
+    log(f"  dominant kernel {dominant}: {roofline['achieved']} {roofline['unit']}; "
+        f"attention core {attn_tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": "prefill attn TFLOP/s (% MFMA bf16 peak); decode KV GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "H": w.H, "H_kv": w.H_kv,
+                   "d_h": w.d_h, "window": w.window,
+                   "layers": [f"{L['layer'].attn_type}(theta={L['layer'].rope_theta:g},"
+                              f"scale={L['layer'].rope_scale:g})" for L in layers],
+                   "step_flops": step_flops, "parallelism": "none (1 GPU)"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "attention_core_tflops": round(attn_tflops, 2),
+        "roofline": roofline,
+    }
+
+    # ---------------------------------------------------------------- decode
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, torch, np, W, I, lib, dev)
+        for L in layers:
+            L["ws"] = None
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU baseline
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, step_flops)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, torch, np, W, I, lib, dev):
+    w = W.WORKLOADS[5]
+    lengths = I.decode_lengths(w)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    out = {"workload": w.name, "B": w.B, "D": w.D, "H": w.H, "H_kv": w.H_kv, "d_h": w.d_h,
+           "cache_slots": w.cache_len, "lengths_sum": int(lengths.sum())}
+    for li, layer in enumerate(w.layers):
+        name = "global" if layer.attn_type == "GLOBAL" else "local"
+        inp = I.decode_inputs(w, li, lengths)
+        kc, vc = I.decode_cache(w, li, lengths, device=dev, poison=True)
+        xd = inp["x"].to(dev)
+        pd = inp["segment_pos"].to(dev)
+        wts = {k: inp[k].to(dev) for k in ("w_q", "w_kv", "w_o", "gamma_q", "gamma_k")}
+        kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
+                  rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
+                  query_scale=w.query_scale)
+        desc = lib.make_desc(B=w.B, T=1, D=w.D, dtype=torch.bfloat16, **kw)
+        ws = lib.new_workspace(desc, w.cache_len, dev)
+        y = torch.empty((w.B, 1, w.D), dtype=torch.bfloat16, device=dev)
+        kv_bytes, other_bytes = decode_bytes(w, layer, lengths)
+
+        def call(stages=lib.DSTAGE_ALL):
+            lib.decode(xd, pd, wts, kc, vc, workspace=ws, y=y, stages=stages, **kw)
+
+        for _ in range(3):
+            call()
+        times = []
+        stage_t = {"qkv_proj": [], "qk_norm_cache_write": [], "attention": [], "out_proj": []}
+        bits = [lib.DSTAGE_QKV_PROJ, lib.DSTAGE_QK_NORM, lib.DSTAGE_ATTN, lib.DSTAGE_OUT_PROJ]
+        for _ in range(args.decode_reps):
+            flush.zero_()
+            a, b = stream_events(torch)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+            # stages one at a time, cache flushed before each
+            for bit, key in zip(bits, stage_t):
+                flush.zero_()
+                a, b = stream_events(torch)
+                a.record()
+                call(bit)
+                b.record()
+                torch.cuda.synchronize()
+                stage_t[key].append(a.elapsed_time(b))
+        med = float(np.median(times))
+        gbs = (kv_bytes + other_bytes) / (med * 1e-3) / 1e9
+        st = {k: float(np.median(v)) for k, v in stage_t.items()}
+        core_gbs = kv_bytes / (st["attention"] * 1e-3) / 1e9
+        out[name] = {
+            "ms_median": round(med, 4), "ms_min": round(float(np.min(times)), 4),
+            "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "kv_bytes": kv_bytes, "other_bytes": other_bytes,
+            "stage_us": {k: round(v * 1e3, 2) for k, v in st.items()},
+            "roofline": {"kernel": "decode attention (split-KV partial + combine)",
+                         "bound": "hbm", "achieved": round(core_gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(core_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": None},
+        }
+        log(f"decode {name}: {med * 1e3:.1f} us -> {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%}); "
+            f"attention core {core_gbs:.0f} GB/s; stages {out[name]['stage_us']}")
+        del kc, vc, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, step_flops):
+    """The fp64 oracle on this host's cores, on the same step (both layers)."""
+    import numpy as np
+
+    import oracle as O
+    from workloads import inputs as I
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    x = I.prefill_x(w).float().numpy().astype(np.float64)
+    pos = I.prefill_positions(w).numpy()
+    total = 0.0
+    for li, layer in enumerate(w.layers):
+        wt = {k: v.float().numpy().astype(np.float64) for k, v in I.layer_weights(w, li).items()}
+        t0 = time.perf_counter()
+        O.prefill(x, pos, wt["w_q"], wt["w_kv"], wt["w_o"], wt["gamma_q"], wt["gamma_k"],
+                  num_heads=w.H, num_kv_heads=w.H_kv, head_dim=w.d_h,
+                  attn_type=layer.attn_type, window=w.window, rope_theta=layer.rope_theta,
+                  rope_scale=layer.rope_scale, query_scale=w.query_scale)
+        total += time.perf_counter() - t0
+    value = step_flops / total / 1e12
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    log(f"cpu baseline (fp64 oracle): {total:.2f} s for one step -> {value * 1e3:.2f} GFLOP/s "
+        f"on {threads} BLAS threads")
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step ({w.name}, both layers), fp64 numpy; BLAS threads "
+                      f"{threads}, affinity {len(os.sched_getaffinity(0))} cores, "
+                      f"numpy elementwise ops single-threaded; {cpu_model}",
+            "seconds": round(total, 3)}
+
+
+if __name__ == "__main__":
+    main()

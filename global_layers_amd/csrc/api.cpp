@@ -48,10 +48,16 @@ int check_desc(const gemma3_attn_desc *d, int32_t S) {
     if (d->d_h != 64 && d->d_h != 128 && d->d_h != 256) return GEMMA3_ERR_UNSUPPORTED;
     if (d->D % 64 != 0 || (d->H * d->d_h) % 64 != 0) return GEMMA3_ERR_UNSUPPORTED;
   } else {
-    if (d->d_h > 256) return GEMMA3_ERR_UNSUPPORTED;
+    // the norm/RoPE kernel spreads a head over d_h/16 lanes (a power of two)
+    if (d->d_h < 16 || d->d_h > 256 || (d->d_h & (d->d_h - 1)) != 0) return GEMMA3_ERR_UNSUPPORTED;
   }
   if (S > 0 && d->d_h % 64 != 0) return GEMMA3_ERR_UNSUPPORTED;  // decode: 32 channels per lane
   return GEMMA3_OK;
+}
+
+AttnArgs attn_args(const gemma3_attn_desc *d, int T_pad) {
+  return AttnArgs{d->B, d->T, d->H, d->H_kv, d->d_h, T_pad,
+                  d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window};
 }
 
 int layout(const gemma3_attn_desc *d, int32_t S, gemma3_ws_layout *L) {
@@ -73,6 +79,13 @@ int layout(const gemma3_attn_desc *d, int32_t S, gemma3_ws_layout *L) {
     off = align_up(off + (size_t)d->B * d->H_kv * L->T_pad * d->d_h * esz);
     L->vt = off;
     off = align_up(off + (size_t)d->B * d->H_kv * d->d_h * L->T_pad * esz);
+    if (d->dtype == GEMMA3_BF16) {
+      const size_t part = flash_attn_partial_bytes(attn_args(d, L->T_pad));
+      if (part) {
+        L->attn_part = off;
+        off = align_up(off + part);
+      }
+    }
   } else {
     const bool bf = d->dtype == GEMMA3_BF16;
     const bool local = d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING;
@@ -135,11 +148,11 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
                                a, s));
   }
   if (stages & GEMMA3_STAGE_ATTN) {
-    AttnArgs a{d->B, d->T, d->H, d->H_kv, d->d_h, L.T_pad,
-               d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window};
+    const AttnArgs a = attn_args(d, L.T_pad);
     if (bf)
       RUN(launch_flash_attn_bf16((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, kv_len,
-                                 (bf16 *)o, a, s));
+                                 (const bf16 *)w->gamma_k, (bf16 *)o,
+                                 L.attn_part ? base + L.attn_part : nullptr, a, s));
     else
       RUN(launch_attn_f32((const float *)q, (const float *)k, (const float *)vt, kv_len,
                           (float *)o, a, s));

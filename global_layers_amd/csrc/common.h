@@ -63,3 +63,7 @@ DEVI int xcd_remap(int p, int n) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 and leaves the
+// expcnt and lgkmcnt counters unconstrained.
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);

@@ -22,27 +22,35 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;  // slots per slot group per iteration
-constexpr int kChansPerLane = 32;
+constexpr int kChansPerLane = 16;
 
-template <typename T> struct LoadVec;
-template <> struct LoadVec<bf16> {
-  static DEVI void load(const bf16 *p, float (&out)[kChansPerLane]) {
-#pragma unroll
-    for (int i = 0; i < kChansPerLane / 8; ++i) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, ld16(p + 8 * i));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) out[8 * i + j] = (float)v[j];
-    }
+// Raw 16-channel slice of one cache row held in registers until it is used.
+template <typename T> struct Slice;
+template <> struct Slice<bf16> {
+  u32x4 v[2];
+  DEVI void load(const bf16 *p) {
+    v[0] = ld16(p);
+    v[1] = ld16(p + 8);
+  }
+  DEVI void zero() { v[0] = v[1] = u32x4{0, 0, 0, 0}; }
+  DEVI float get(int i) const {
+    const bf16x8 h = __builtin_bit_cast(bf16x8, v[i >> 3]);
+    return (float)h[i & 7];
   }
 };
-template <> struct LoadVec<float> {
-  static DEVI void load(const float *p, float (&out)[kChansPerLane]) {
+template <> struct Slice<float> {
+  u32x4 v[4];
+  DEVI void load(const float *p) {
 #pragma unroll
-    for (int i = 0; i < kChansPerLane / 4; ++i) {
-      const f32x4 v = __builtin_bit_cast(f32x4, ld16(p + 4 * i));
+    for (int i = 0; i < 4; ++i) v[i] = ld16(p + 4 * i);
+  }
+  DEVI void zero() {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[4 * i + j] = v[j];
-    }
+    for (int i = 0; i < 4; ++i) v[i] = u32x4{0, 0, 0, 0};
+  }
+  DEVI float get(int i) const {
+    const uint32_t w = v[i >> 2][i & 3];  // scalar copy: bit_cast of a vector element misreads
+    return __builtin_bit_cast(float, w);
   }
 };
 
@@ -79,7 +87,7 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   const int c_hi = min(hi, c_lo + a.chunk - 1);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane % LPS;             // which 32-channel slice
+  const int sub = lane % LPS;             // which 16-channel slice
   const int grp = wave * kGroupsPerWave + lane / LPS;
   const int c0 = sub * kChansPerLane;
 
@@ -104,32 +112,30 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   const T *vb = v_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D + c0;
 
   for (int s_base = c_lo + grp; s_base <= c_hi; s_base += NG * kDecUnroll) {
-    float x[kDecUnroll][GQ];
+    Slice<T> ks[kDecUnroll], vs[kDecUnroll];
     bool ok[kDecUnroll];
+    // all K and V loads of the iteration are in flight before any math
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int s = s_base + u * NG;
       ok[u] = s <= c_hi;
-      float kv[kChansPerLane];
       if (ok[u]) {
-        LoadVec<T>::load(kb + (size_t)s * slot_stride, kv);
+        ks[u].load(kb + (size_t)s * slot_stride);
+        vs[u].load(vb + (size_t)s * slot_stride);
       } else {
-#pragma unroll
-        for (int i = 0; i < kChansPerLane; ++i) kv[i] = 0.f;
-      }
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) {
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < kChansPerLane; ++i) d = fmaf(qv[g][i], kv[i], d);
-        x[u][g] = d;
+        ks[u].zero();
+        vs[u].zero();
       }
     }
+    float x[kDecUnroll][GQ];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u)
 #pragma unroll
       for (int g = 0; g < GQ; ++g) {
-        const float d = group_sum<LPS>(x[u][g]);
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < kChansPerLane; ++i) d = fmaf(qv[g][i], ks[u].get(i), d);
+        d = group_sum<LPS>(d);
         x[u][g] = ok[u] ? d : -INFINITY;
       }
 #pragma unroll
@@ -137,7 +143,7 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
       float mx = m[g];
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) mx = fmaxf(mx, x[u][g]);
-      // at least slot s_base is valid, so mx is finite
+      // slot s_base is valid, so mx is finite
       const float corr = exp2f(m[g] - mx);
       m[g] = mx;
       l[g] *= corr;
@@ -150,15 +156,12 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
       }
     }
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      if (!ok[u]) continue;
-      float vv[kChansPerLane];
-      LoadVec<T>::load(vb + (size_t)(s_base + u * NG) * slot_stride, vv);
+    for (int u = 0; u < kDecUnroll; ++u)
 #pragma unroll
       for (int g = 0; g < GQ; ++g)
 #pragma unroll
-        for (int i = 0; i < kChansPerLane; ++i) acc[g][i] = fmaf(x[u][g], vv[i], acc[g][i]);
-    }
+        for (int i = 0; i < kChansPerLane; ++i)
+          acc[g][i] = fmaf(x[u][g], vs[u].get(i), acc[g][i]);
   }
 
   // merge the slot groups of this wave (lanes with equal `sub` hold equal channels)
@@ -214,27 +217,57 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   }
 }
 
-// grid: x = H, y = B; one thread per channel.
+// grid: x = H, y = B; D threads. Chunk weights exp2(m_j - M) are formed once
+// per block in LDS; each thread then sums its channel over the chunks.
+constexpr int kMaxChunks = 64;  // decode_chunk keeps every row at <= 64 chunks
+
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
 decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos,
                     T *__restrict__ o, DecodeArgs a) {
+  __shared__ float wgt[kMaxChunks];
+  __shared__ float red[D / 64];
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int lane = c & 63, wave = c >> 6;
   int lo, hi;
   row_range(pos, b, a.S, a.local, a.window, lo, hi);
   const int n = hi >= lo ? div_up(hi - lo + 1, a.chunk) : 0;
   const float *pp = part + ((size_t)b * a.H + h) * a.n_chunks * (D + 2);
-  float mn = -INFINITY;
-  for (int j = 0; j < n; ++j) mn = fmaxf(mn, pp[(size_t)j * (D + 2) + D]);
-  const float mu = mn == -INFINITY ? 0.f : mn;
-  float sa = 0.f, sl = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float *e = pp + (size_t)j * (D + 2);
-    const float wgt = exp2f(e[D] - mu);
-    sa += wgt * e[c];
-    sl += wgt * e[D + 1];
+
+  float mx = -INFINITY;
+  for (int j = c; j < n; j += D) mx = fmaxf(mx, pp[(size_t)j * (D + 2) + D]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) M = fmaxf(M, red[i]);
+  const float mu = M == -INFINITY ? 0.f : M;
+  __syncthreads();
+  float sl = 0.f;
+  for (int j = c; j < n; j += D) {
+    const float wj = exp2f(pp[(size_t)j * (D + 2) + D] - mu);
+    wgt[j] = wj;
+    sl += wj * pp[(size_t)j * (D + 2) + D + 1];
   }
-  o[((size_t)b * a.H + h) * D + c] = from_f32<T>(sl > 0.f ? sa / sl : 0.f);
+  sl = wave_sum(sl);
+  if (lane == 0) red[wave] = sl;
+  __syncthreads();
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) L += red[i];
+
+  float sa = 0.f;
+  int j = 0;
+  for (; j + 8 <= n; j += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pp[(size_t)(j + u) * (D + 2) + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sa = fmaf(wgt[j + u], v[u], sa);
+  }
+  for (; j < n; ++j) sa = fmaf(wgt[j], pp[(size_t)j * (D + 2) + c], sa);
+  o[((size_t)b * a.H + h) * D + c] = from_f32<T>(L > 0.f ? sa / L : 0.f);
 }
 
 template <typename T, int D, int GQ>
@@ -275,8 +308,12 @@ __global__ void splitk_reduce(const float *__restrict__ part, int ksplit, T *__r
 
 int decode_chunk(int local, int window, int S, int d_h) {
   (void)d_h;
-  if (local) return 64;
-  return S >= 32768 ? 512 : 128;
+  // local: short chunks so the W slots still spread over many workgroups;
+  // global: at most 64 chunks per row (long streams per workgroup, cheap combine)
+  const int range = local && window < S ? window : S;
+  int c = local ? 64 : 256;
+  while (div_up_h(range, c) > 64) c *= 2;
+  return c;
 }
 
 template <typename T>

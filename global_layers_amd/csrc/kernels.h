@@ -44,9 +44,13 @@ struct AttnArgs {
   int B, T, H, Hk, d_h, T_pad;
   int local, window;
 };
+// `partial` (flash_attn_partial_bytes(a) bytes, may be NULL when that is 0)
+// holds the split-KV partial outputs.
+size_t flash_attn_partial_bytes(const AttnArgs &a);
+// gamma_k [d_h] bounds the key norms (fixed softmax reference).
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
-                                  const int32_t *kv_len, bf16 *o, const AttnArgs &a,
-                                  hipStream_t s);
+                                  const int32_t *kv_len, const bf16 *gamma_k, bf16 *o,
+                                  void *partial, const AttnArgs &a, hipStream_t s);
 
 // K4 + K4c (decode attention): split-KV partials then combine into o [B, H*d_h].
 struct DecodeArgs {

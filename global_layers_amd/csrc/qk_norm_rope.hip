@@ -26,98 +26,166 @@ DEVI void rope_sincos(int p, double inv_scale, double inv_freq, float &c, float 
   sincosf((float)a, &s, &c);
 }
 
-// grid: x = B * (T_pad / 64) token blocks, y = H + 2 Hk head vectors; 256 threads.
+// 16-element slices of a head vector: 8 channels of the first half and the
+// 8 channels they pair with in the second half (two 16-byte vectors for bf16).
+template <typename T> struct Pair8;
+template <> struct Pair8<bf16> {
+  static DEVI void load(const bf16 *p, int half, float (&a)[8], float (&b)[8]) {
+    const bf16x8 u = __builtin_bit_cast(bf16x8, ld16(p));
+    const bf16x8 v = __builtin_bit_cast(bf16x8, ld16(p + half));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (float)u[i];
+      b[i] = (float)v[i];
+    }
+  }
+  static DEVI void store(bf16 *p, int half, const float (&a)[8], const float (&b)[8]) {
+    bf16x8 u, v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u[i] = (bf16)a[i];
+      v[i] = (bf16)b[i];
+    }
+    st16(p, __builtin_bit_cast(u32x4, u));
+    st16(p + half, __builtin_bit_cast(u32x4, v));
+  }
+};
+template <> struct Pair8<float> {
+  static DEVI void load(const float *p, int half, float (&a)[8], float (&b)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = p[i];
+      b[i] = p[half + i];
+    }
+  }
+  static DEVI void store(float *p, int half, const float (&a)[8], const float (&b)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = a[i];
+      p[half + i] = b[i];
+    }
+  }
+};
+
+constexpr int kQkUnroll = 4;  // head-vector iterations whose loads are issued together
+
+// Q and K heads. One wave per token (B * T_pad tokens, 4 per block): the RoPE
+// (cos, sin) of the token's position are formed once per lane and reused by
+// every Q and K head of the token. A head vector is spread over d_h/16 lanes
+// (8 pairs per lane); a wave covers 64/(d_h/16) head vectors per iteration.
+// Key rows t in [T, T_pad) are written as zeros.
 template <typename T>
 __global__ void __launch_bounds__(256)
 qk_norm_rope_prefill(const T *__restrict__ qkv, const int32_t *__restrict__ pos,
                      const T *__restrict__ gamma_q, const T *__restrict__ gamma_k,
-                     T *__restrict__ q, T *__restrict__ k, T *__restrict__ vt, NormRopeArgs a) {
+                     T *__restrict__ q, T *__restrict__ k, NormRopeArgs a) {
   __shared__ double inv_freq[kMaxHalf];
-  __shared__ T tile[kTokBlock][kTileC + 1];  // V transpose tile (odd row pitch)
-
-  const int blocks_per_row = a.T_pad / kTokBlock;
-  const int b = blockIdx.x / blocks_per_row;
-  const int t0 = (blockIdx.x % blocks_per_row) * kTokBlock;
-  const int j = blockIdx.y;
   const int d_h = a.d_h, half = d_h / 2;
-  const int n_qkv = (a.H + 2 * a.Hk) * d_h;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
-  if (j >= a.H + a.Hk) {
-    // V head: transpose [64 tokens][d_h] -> vt[b][kh][c][t0 .. t0+63], 128 channels at a time
-    const int kh = j - a.H - a.Hk;
-    T *dst = vt + ((size_t)b * a.Hk + kh) * d_h * a.T_pad + t0;
-    for (int c0 = 0; c0 < d_h; c0 += kTileC) {
-      const int nc = min(kTileC, d_h - c0);
-      for (int e = threadIdx.x; e < kTokBlock * nc; e += blockDim.x) {
-        const int tt = e / nc, c = e % nc, t = t0 + tt;
-        tile[tt][c] =
-            t < a.T ? qkv[((size_t)b * a.T + t) * n_qkv + j * d_h + c0 + c] : from_f32<T>(0.f);
-      }
-      __syncthreads();
-      for (int e = threadIdx.x; e < kTokBlock * nc; e += blockDim.x) {
-        const int c = e / kTokBlock, tt = e % kTokBlock;
-        dst[(size_t)(c0 + c) * a.T_pad + tt] = tile[tt][c];
-      }
-      __syncthreads();
-    }
-    return;
-  }
-
-  const bool is_q = j < a.H;
   for (int i = threadIdx.x; i < half; i += blockDim.x)
     inv_freq[i] = pow((double)a.theta, -2.0 * (double)i / (double)d_h);
   __syncthreads();
 
-  const T *gamma = is_q ? gamma_q : gamma_k;
-  const float mul = is_q ? a.alpha : 1.0f;
-  const double inv_scale = 1.0 / (double)a.scale;
-  // each lane owns pairs i = lane + 64 u, u < ceil(half / 64)
-  constexpr int kMaxPairs = kMaxHalf / 64;
-  float g1[kMaxPairs], g2[kMaxPairs];
-#pragma unroll
-  for (int u = 0; u < kMaxPairs; ++u) {
-    const int i = lane + 64 * u;
-    g1[u] = i < half ? (1.f + to_f32(gamma[i])) * mul : 0.f;
-    g2[u] = i < half ? (1.f + to_f32(gamma[i + half])) * mul : 0.f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long tok = (long)blockIdx.x * 4 + wave;  // over B * T_pad
+  if (tok >= (long)a.B * a.T_pad) return;
+  const int b = (int)(tok / a.T_pad), t = (int)(tok % a.T_pad);
+  const int lpv = d_h / 16;           // lanes per head vector
+  const int vpw = kWave / lpv;        // head vectors per wave iteration
+  const int sub = lane % lpv, vec = lane / lpv;
+  const int i0 = sub * 8;             // first pair index of this lane
+  const int n_heads = a.H + a.Hk;
+  const int n_qkv = (a.H + 2 * a.Hk) * d_h;
+
+  if (t >= a.T) {  // padding row: zero keys
+    for (int j = vec; j < a.Hk; j += vpw) {
+      const float z[8] = {};
+      Pair8<T>::store(k + (((size_t)b * a.Hk + j) * a.T_pad + t) * d_h + i0, half, z, z);
+    }
+    return;
   }
 
-  for (int tt = wave; tt < kTokBlock; tt += blockDim.x / 64) {
-    const int t = t0 + tt;
-    T *dst;
-    if (is_q) {
-      if (t >= a.T) break;
-      dst = q + (((size_t)b * a.H + j) * a.T + t) * d_h;
-    } else {
-      dst = k + (((size_t)b * a.Hk + (j - a.H)) * a.T_pad + t) * d_h;
-      if (t >= a.T) {  // zero padding rows of K
-        for (int c = lane; c < d_h; c += 64) dst[c] = from_f32<T>(0.f);
-        continue;
+  float cs[8], sn[8];
+  {
+    const int p = pos[(size_t)b * a.T + t];
+    const double inv_scale = 1.0 / (double)a.scale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rope_sincos(p, inv_scale, inv_freq[i0 + i], cs[i], sn[i]);
+  }
+  float gq1[8], gq2[8], gk1[8], gk2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gq1[i] = (1.f + to_f32(gamma_q[i0 + i])) * a.alpha;
+    gq2[i] = (1.f + to_f32(gamma_q[half + i0 + i])) * a.alpha;
+    gk1[i] = 1.f + to_f32(gamma_k[i0 + i]);
+    gk2[i] = 1.f + to_f32(gamma_k[half + i0 + i]);
+  }
+
+  const T *src = qkv + ((size_t)b * a.T + t) * n_qkv + i0;
+  const int n_iter = div_up(n_heads, vpw);
+  for (int it0 = 0; it0 < n_iter; it0 += kQkUnroll) {
+    float x1[kQkUnroll][8], x2[kQkUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kQkUnroll; ++u) {
+      const int j = (it0 + u) * vpw + vec;
+      if (j < n_heads) {
+        Pair8<T>::load(src + (size_t)j * d_h, half, x1[u], x2[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x1[u][i] = x2[u][i] = 0.f;
       }
     }
-    const T *src = qkv + ((size_t)b * a.T + t) * n_qkv + j * d_h;
-    float x1[kMaxPairs], x2[kMaxPairs];
-    float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < kMaxPairs; ++u) {
-      const int i = lane + 64 * u;
-      x1[u] = i < half ? to_f32(src[i]) : 0.f;
-      x2[u] = i < half ? to_f32(src[i + half]) : 0.f;
-      ss += x1[u] * x1[u] + x2[u] * x2[u];
-    }
-    ss = wave_sum(ss);
-    const float r = rsqrtf(ss / (float)d_h + 1e-6f);
-    const int p = pos[(size_t)b * a.T + t];
+    for (int u = 0; u < kQkUnroll; ++u) {
+      const int j = (it0 + u) * vpw + vec;
+      float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < kMaxPairs; ++u) {
-      const int i = lane + 64 * u;
-      if (i >= half) continue;
-      float c, s;
-      rope_sincos(p, inv_scale, inv_freq[i], c, s);
-      const float y1 = x1[u] * r * g1[u], y2 = x2[u] * r * g2[u];
-      dst[i] = from_f32<T>(y1 * c - y2 * s);
-      dst[i + half] = from_f32<T>(y2 * c + y1 * s);
+      for (int i = 0; i < 8; ++i) ss += x1[u][i] * x1[u][i] + x2[u][i] * x2[u][i];
+      // sum over the lpv lanes of this head vector (aligned lane groups)
+      for (int o = lpv / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+      if (j >= n_heads) continue;
+      const float r = rsqrtf(ss / (float)d_h + 1e-6f);
+      const bool is_q = j < a.H;
+      float o1[8], o2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float y1 = x1[u][i] * r * (is_q ? gq1[i] : gk1[i]);
+        const float y2 = x2[u][i] * r * (is_q ? gq2[i] : gk2[i]);
+        o1[i] = y1 * cs[i] - y2 * sn[i];
+        o2[i] = y2 * cs[i] + y1 * sn[i];
+      }
+      T *dst = is_q ? q + (((size_t)b * a.H + j) * a.T + t) * d_h + i0
+                    : k + (((size_t)b * a.Hk + (j - a.H)) * a.T_pad + t) * d_h + i0;
+      Pair8<T>::store(dst, half, o1, o2);
     }
+  }
+}
+
+// V heads: [64 tokens][d_h] tile -> vt[b][kh][c][t0 .. t0+63] through LDS.
+// grid: x = B * (T_pad / 64), y = H_kv.
+template <typename T>
+__global__ void __launch_bounds__(256)
+v_transpose(const T *__restrict__ qkv, T *__restrict__ vt, NormRopeArgs a) {
+  __shared__ T tile[kTokBlock][kTileC + 2];
+  const int blocks_per_row = a.T_pad / kTokBlock;
+  const int b = blockIdx.x / blocks_per_row;
+  const int t0 = (blockIdx.x % blocks_per_row) * kTokBlock;
+  const int kh = blockIdx.y, d_h = a.d_h;
+  const int n_qkv = (a.H + 2 * a.Hk) * d_h;
+  const int j = a.H + a.Hk + kh;
+  T *dst = vt + ((size_t)b * a.Hk + kh) * d_h * a.T_pad + t0;
+  for (int c0 = 0; c0 < d_h; c0 += kTileC) {
+    const int nc = min(kTileC, d_h - c0);
+    for (int e = threadIdx.x; e < kTokBlock * nc; e += blockDim.x) {
+      const int tt = e / nc, c = e % nc, t = t0 + tt;
+      tile[tt][c] =
+          t < a.T ? qkv[((size_t)b * a.T + t) * n_qkv + j * d_h + c0 + c] : from_f32<T>(0.f);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTokBlock * nc; e += blockDim.x) {
+      const int c = e / kTokBlock, tt = e % kTokBlock;
+      dst[(size_t)(c0 + c) * a.T_pad + tt] = tile[tt][c];
+    }
+    __syncthreads();
   }
 }
 
@@ -201,9 +269,13 @@ template <typename T>
 hipError_t launch_qk_norm_rope(const T *qkv, const int32_t *pos, const T *gamma_q,
                                const T *gamma_k, T *q, T *k, T *vt, const NormRopeArgs &a,
                                hipStream_t s) {
-  dim3 grid(a.B * (a.T_pad / kTokBlock), a.H + 2 * a.Hk);
-  hipLaunchKernelGGL(qk_norm_rope_prefill<T>, grid, dim3(256), 0, s, qkv, pos, gamma_q, gamma_k,
-                     q, k, vt, a);
+  const long toks = (long)a.B * a.T_pad;
+  hipLaunchKernelGGL(qk_norm_rope_prefill<T>, dim3((unsigned)div_up_h(toks, 4)), dim3(256), 0, s,
+                     qkv, pos, gamma_q, gamma_k, q, k, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(v_transpose<T>, dim3(a.B * (a.T_pad / kTokBlock), a.Hk), dim3(256), 0, s,
+                     qkv, vt, a);
   return hipGetLastError();
 }
 

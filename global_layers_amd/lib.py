@@ -58,7 +58,7 @@ class WsLayout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("qkv", ctypes.c_size_t),
                 ("q", ctypes.c_size_t), ("k", ctypes.c_size_t), ("vt", ctypes.c_size_t),
                 ("o", ctypes.c_size_t), ("part", ctypes.c_size_t), ("ypart", ctypes.c_size_t),
-                ("T_pad", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("attn_part", ctypes.c_size_t), ("T_pad", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("n_chunks", ctypes.c_int32), ("ksplit_qkv", ctypes.c_int32),
                 ("ksplit_out", ctypes.c_int32)]
 

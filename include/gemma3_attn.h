@@ -113,8 +113,9 @@ typedef struct {
 /*
  * Shapes with kernels in this build:
  *   GEMMA3_BF16: d_h in {64, 128, 256}; D % 64 == 0; H*d_h % 64 == 0;
- *                B*T < 2^31 / max(D, (H + 2 H_kv) d_h); H / H_kv <= 8.
- *   GEMMA3_F32:  d_h even and <= 256; any D, H, H_kv, B, T within int32.
+ *                B*T < 2^31 / max(D, (H + 2 H_kv) d_h).
+ *   GEMMA3_F32:  d_h in {16, 32, 64, 128, 256}; any D, H, H_kv, B, T within int32.
+ *   Decode (both dtypes): d_h a multiple of 64.
  * Anything else valid returns GEMMA3_ERR_UNSUPPORTED.
  */
 

@@ -40,6 +40,8 @@ extern "C" {
  *   q    [B, H, T, d_h]           normalised, rotated, times alpha
  *   k    [B, H_kv, T_pad, d_h]    normalised, rotated (rows T..T_pad-1 zero)
  *   vt   [B, H_kv, d_h, T_pad]    V transposed (columns T..T_pad-1 zero)
+ *   attn_part                     split-KV partial outputs of the attention stage
+ *                                 (only when the grid is too small to fill the GPU)
  *   T_pad = T rounded up to a multiple of 64.
  * Decode (S > 0):
  *   qkv  fp32 [ksplit_qkv, B, (H + 2 H_kv) d_h]  split-K partial projections
@@ -51,6 +53,7 @@ extern "C" {
 typedef struct {
   size_t total_bytes;
   size_t qkv, q, k, vt, o, part, ypart; /* offsets; unused ones are 0 */
+  size_t attn_part;
   int32_t T_pad;                        /* prefill */
   int32_t chunk, n_chunks;              /* decode: cache slots per chunk, chunks per (b, h) */
   int32_t ksplit_qkv, ksplit_out;       /* decode */

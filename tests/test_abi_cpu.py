@@ -81,7 +81,8 @@ def _call_decode(desc, S=1024, ws_bytes=None, kc=FAKE, vc=FAKE):
     (dict(rope_theta=0.0), 5), (dict(rope_scale=-1.0), 5), (dict(rope_theta=float("inf")), 5),
     (dict(query_scale=float("nan")), 5),
     (dict(d_h=96), 7), (dict(D=100), 7), (dict(d_h=512), 7),
-    (dict(d_h=300, dtype=lib.F32), 7),
+    (dict(d_h=300, dtype=lib.F32), 7), (dict(d_h=48, dtype=lib.F32), 7),
+    (dict(d_h=8, dtype=lib.F32), 7),
 ])
 def test_prefill_validation_status(kw, status):
     assert _call_prefill(_desc(**kw), ws_bytes=1 << 40) == status

@@ -31,6 +31,9 @@ SMALL_BF16 = [
     (2, 129, 1024, 4, 2, 256, L, 500, None),
     (1, 520, 1024, 4, 1, 256, L, 128, None),
     (1, 700, 1024, 8, 4, 128, G, 0, (650,)),
+    # few workgroups: key ranges split over several workgroups, then merged
+    (1, 1000, 512, 4, 1, 128, L, 600, (900,)),
+    (1, 1500, 256, 2, 1, 64, G, 0, None),
 ]
 
 
