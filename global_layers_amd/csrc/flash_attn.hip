@@ -406,27 +406,33 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
   const Geo geo = geometry(a, kv_len, base_id, gp, n_qtiles, n_hgrp, chunk_keys);
   if (geo.n_active <= 1) return;
 
-  float mj[8], M = -INFINITY;  // n_active <= n_split <= 8
+  // every load of the row is issued before any arithmetic (n_active <= 8)
+  float mj[8], lj[8], oj[8][kPer];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     mj[j] = -INFINITY;
+    lj[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) oj[j][i] = 0.f;
     if (j < geo.n_active) {
       const size_t row = (((size_t)j * a.B + b) * a.H + h) * a.T + t;
       mj[j] = part_ml[2 * row];
-      M = fmaxf(M, mj[j]);
+      lj[j] = part_ml[2 * row + 1];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) oj[j][i] = (float)part_o[row * D + lane * kPer + i];
     }
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) M = fmaxf(M, mj[j]);
   const float mu = M == -INFINITY ? 0.f : M;
   float num[kPer] = {}, den = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (j >= geo.n_active) break;
-    const size_t row = (((size_t)j * a.B + b) * a.H + h) * a.T + t;
-    const float wl = exp2f(mj[j] - mu) * part_ml[2 * row + 1];
+    const float wl = j < geo.n_active ? exp2f(mj[j] - mu) * lj[j] : 0.f;
     den += wl;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      num[i] = fmaf(wl, (float)part_o[row * D + lane * kPer + i], num[i]);
+    for (int i = 0; i < kPer; ++i) num[i] = fmaf(wl, oj[j][i], num[i]);
   }
   bf16 *op = o + ((size_t)b * a.T + t) * ((size_t)a.H * D) + (size_t)h * D + lane * kPer;
 #pragma unroll
@@ -446,15 +452,24 @@ Plan plan(const AttnArgs &a) {
   p.n_qtiles = div_up_h(a.T, TQ);
   p.n_hgrp = G / p.gp;
   p.n_base = (long)a.B * a.Hk * p.n_hgrp * p.n_qtiles;
-  // longest key range of a query tile, in 64-key tiles (+1 for alignment)
-  const int max_keys = a.local ? min(a.T, TQ + a.window - 1) : a.T;
+  // Split only when one query tile's key range is much longer than the
+  // average per-CU load (one 131 KB-LDS workgroup per CU): the critical path
+  // then sits in a few long workgroups. Chunks cost a per-workgroup prologue
+  // and a merge, so aim at about twice the average load per chunk
+  // (measured on the 1B shape: local layer best unsplit, global best 2-way).
+  const int TQ2 = kRowsPerWave * (4 / p.gp);
+  const int max_keys = a.local ? min(a.T, TQ2 + a.window - 1) : a.T;
   const int max_tiles = div_up_h(max_keys, kBN) + 1;
+  // key tiles over all query tiles of one (b, kh, head group), closed form
+  const double total_tiles =
+      a.local ? p.n_qtiles * (max_keys / (double)kBN + 1.0)
+              : p.n_qtiles * ((a.T + TQ2) / 2.0 / kBN + 1.0);
+  const double avg = total_tiles * (double)(p.n_base / p.n_qtiles) / 256.0;
   p.n_split = 1;
-  if (p.n_base < 1024 && max_tiles >= 8) {
-    p.n_split = div_up_h(1024, p.n_base);
-    const int cap = div_up_h(max_tiles, 4);  // at least 4 tiles per chunk
-    if (p.n_split > cap) p.n_split = cap;
-    if (p.n_split > 8) p.n_split = 8;        // flash_combine merges at most 8 chunks
+  if (max_tiles > 3.0 * avg && avg > 0) {
+    p.n_split = (int)((max_tiles + 2 * avg - 1) / (2 * avg));
+    if (p.n_split > 8) p.n_split = 8;  // flash_combine merges at most 8 chunks
+    if (p.n_split < 1) p.n_split = 1;
   }
   // one chunk covers every key range when there is no split
   p.chunk_keys = p.n_split == 1 ? a.T + kBN : div_up_h(max_tiles, p.n_split) * kBN;

@@ -3,11 +3,13 @@
 // back to D). Both are C[M,N] = A[M,K] * B[N,K]^T with A the activations and
 // B an output-major weight, accumulated in fp32.
 //
-//  * gemm_bf16_nt: prefill. Block tile BM x BN x 64, waves arranged WM x WN,
-//    32x32x16 bf16 MFMAs, LDS double buffer fed through registers so the next
-//    K slice's global loads overlap the current slice's MFMAs. The MFMA is
-//    issued with the weight fragment as its first operand so that each lane
-//    ends up holding 4 consecutive output columns (one 8-byte store).
+//  * gemm_bf16_nt: prefill. Block tile BM x BN, K in slices of BK, waves
+//    arranged WM x WN, 32x32x16 bf16 MFMAs. Slices move global -> LDS with
+//    direct loads (no staging registers) into NST stages, several slices ahead
+//    of the MFMAs; each slice waits only for its own loads (explicit vmcnt)
+//    before the barrier. The MFMA is issued with the weight fragment as its
+//    first operand so that each lane ends up holding 4 consecutive output
+//    columns (one 8-byte store).
 //  * gemv16_bf16_splitk: decode (M = batch <= 16 per M block). Weight-streaming
 //    16x16x32 MFMAs, each wave one 16-column block over one K split, fp32
 //    partials per split; the consumer adds the splits.
@@ -16,69 +18,91 @@
 
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kPad = 8;                // bf16 elements of row padding in LDS
-constexpr int kLdsRow = kBK + kPad;    // 72 elements = 144 bytes
-
-template <int BM, int BN, int WM, int WN>
-struct GemmCfg {
-  static constexpr int kThreads = WM * WN * kWave;
-  static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
-  static constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
-  static constexpr int kChunksA = BM * kBK / 8 / kThreads;  // 16-byte chunks per thread
-  static constexpr int kChunksB = BN * kBK / 8 / kThreads;
-  static constexpr int kLdsElems = 2 * (BM + BN) * kLdsRow;
-  static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be 32-aligned");
-  static_assert(BM * kBK / 8 % kThreads == 0 && BN * kBK / 8 % kThreads == 0, "chunking");
+// vmcnt immediates (gfx9 s_waitcnt encoding, expcnt/lgkmcnt unconstrained)
+template <int N> struct VmWait {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  static constexpr int kImm = (N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 };
 
-template <int BM, int BN, int WM, int WN>
+// One direct global -> LDS load: lane l moves 16 bytes to lds + 16 l.
+DEVI void load_lds16(const void *g, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave_base,
+                                   16, 0, 0);
+}
+
+// Tile of BM x BN outputs, K sliced by BK, NST LDS stages. Waves WM x WN.
+// Each stage holds A [BM][BK] and B [BN][BK] bf16, rows of BK*2 bytes, 16-byte
+// chunks XOR-swizzled by row so fragment reads by 8 consecutive rows hit all banks.
+template <int BM, int BN, int WM, int WN, int BK, int NST>
+struct GemmCfg {
+  static constexpr int kThreads = WM * WN * kWave;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
+  static constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
+  static constexpr int kRowBytes = BK * 2;
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kABytes = BM * kRowBytes, kBBytes = BN * kRowBytes;
+  static constexpr int kStageBytes = kABytes + kBBytes;
+  static constexpr int kLdsBytes = NST * kStageBytes;
+  static constexpr int kALoads = kABytes / 1024 / kWaves;  // 1 KB loads per wave per stage
+  static constexpr int kBLoads = kBBytes / 1024 / kWaves;
+  static constexpr int kLoadsPerTile = kALoads + kBLoads;
+  static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be 32-aligned");
+  static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "loads");
+  static_assert(kChunks == 8 || kChunks == 4, "BK must be 64 or 32");
+};
+
+template <int kChunks> DEVI int gemm_swz(int r) {
+  return kChunks == 8 ? (r & 7) : ((r >> 1) & 3);
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NST>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16 *__restrict__ B1,
              int N0, bf16 *__restrict__ C, int M, int N, int K, int n_tiles_n) {
-  using Cfg = GemmCfg<BM, BN, WM, WN>;
-  extern __shared__ __attribute__((aligned(16))) bf16 lds[];
-  bf16 *As = lds;                       // [2][BM][kLdsRow]
-  bf16 *Bs = lds + 2 * BM * kLdsRow;    // [2][BN][kLdsRow]
+  using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int n_blocks = gridDim.x;
-  const int bid = xcd_remap(blockIdx.x, n_blocks);
-  // tiles of one row of C (same A rows) stay adjacent in the logical order
-  const int tile_m = bid / n_tiles_n, tile_n = bid % n_tiles_n;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // Grouped order: runs of kGroupM tile rows are walked column by column, so
+  // the 32 consecutive logical tiles one XCD runs at a time form an
+  // 8 x 4 block of C and share 8 A row-blocks and 4 weight column-blocks in
+  // that XCD's L2.
+  constexpr int kGroupM = 8;
+  const int n_tiles_m = gridDim.x / n_tiles_n;
+  const int group = bid / (kGroupM * n_tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm_size = min(n_tiles_m - first_m, kGroupM);
+  const int in_group = bid % (kGroupM * n_tiles_n);
+  const int tile_m = first_m + in_group % gm_size, tile_n = in_group / gm_size;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-  u32x4 ra[Cfg::kChunksA], rb[Cfg::kChunksB];
-  auto load_global = [&](int k0) {
+  // Per-lane global sources of the 1 KB pieces this wave loads (row clamped
+  // into range; rows past M / N only feed outputs that are never stored).
+  auto issue = [&](int kt, int stage) {
+    char *sbase = lds + stage * Cfg::kStageBytes;
+    const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < Cfg::kChunksA; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-      const int gm = m0 + r;
-      ra[i] = gm < M ? ld16(A + (size_t)gm * K + k0 + kc) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < Cfg::kALoads; ++i) {
+      const int piece = wave + Cfg::kWaves * i;
+      const int byte = piece * 1024 + 16 * lane;
+      const int r = byte / Cfg::kRowBytes, p = (byte % Cfg::kRowBytes) / 16;
+      const int c = p ^ gemm_swz<Cfg::kChunks>(r);
+      const int gm = min(m0 + r, M - 1);
+      load_lds16(A + (size_t)gm * K + k0 + 8 * c, sbase + piece * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < Cfg::kChunksB; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-      const int gn = n0 + r;
+    for (int i = 0; i < Cfg::kBLoads; ++i) {
+      const int piece = wave + Cfg::kWaves * i;
+      const int byte = piece * 1024 + 16 * lane;
+      const int r = byte / Cfg::kRowBytes, p = (byte % Cfg::kRowBytes) / 16;
+      const int c = p ^ gemm_swz<Cfg::kChunks>(r);
+      const int gn = min(n0 + r, N - 1);
       const bf16 *src = gn < N0 ? B0 + (size_t)gn * K : B1 + (size_t)(gn - N0) * K;
-      rb[i] = gn < N ? ld16(src + k0 + kc) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_lds = [&](int buf) {
-    bf16 *as = As + buf * BM * kLdsRow, *bs = Bs + buf * BN * kLdsRow;
-#pragma unroll
-    for (int i = 0; i < Cfg::kChunksA; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      st16(as + (c / (kBK / 8)) * kLdsRow + (c % (kBK / 8)) * 8, ra[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::kChunksB; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      st16(bs + (c / (kBK / 8)) * kLdsRow + (c % (kBK / 8)) * 8, rb[i]);
+      load_lds16(src + k0 + 8 * c, sbase + Cfg::kABytes + piece * 1024);
     }
   };
 
@@ -88,38 +112,55 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
 #pragma unroll
     for (int j = 0; j < Cfg::kFN; ++j) acc[i][j] = f32x16{};
 
-  const int nk = K / kBK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-
-  const int lrow = lane & 31, lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * kBK);
-    const bf16 *as = As + buf * BM * kLdsRow + (wm * Cfg::kWaveM + lrow) * kLdsRow + lk;
-    const bf16 *bs = Bs + buf * BN * kLdsRow + (wn * Cfg::kWaveN + lrow) * kLdsRow + lk;
+  const int nk = K / BK;
+  // prologue: k-tiles 0 .. NST-2 in flight
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < nk) issue(s0, s0);
+
+  const int lrow = lane & 31, hh = lane >> 5;
+  // wait until k-tile kt has landed: everything issued after it may stay in flight
+  auto wait_tile = [&](int kt) {
+    const int after = min(nk - 1, kt + NST - 2) - kt;  // tiles issued after kt
+    if (after >= 2) __builtin_amdgcn_s_waitcnt(VmWait<2 * Cfg::kLoadsPerTile>::kImm);
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(VmWait<Cfg::kLoadsPerTile>::kImm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm);
+    __builtin_amdgcn_s_barrier();
+  };
+  static_assert(NST <= 4, "wait_tile covers up to two tiles in flight behind the current");
+
+  wait_tile(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // refill the stage read in iteration kt-1 (all waves passed its barrier)
+    if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+    const char *sbase = lds + (kt % NST) * Cfg::kStageBytes;
+    const char *as = sbase + (wm * Cfg::kWaveM + lrow) * Cfg::kRowBytes;
+    const char *bs = sbase + Cfg::kABytes + (wn * Cfg::kWaveN + lrow) * Cfg::kRowBytes;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[Cfg::kFM], bfr[Cfg::kFN];
 #pragma unroll
-      for (int i = 0; i < Cfg::kFM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8 *>(as + i * 32 * kLdsRow + kk * 16);
+      for (int i = 0; i < Cfg::kFM; ++i) {
+        const int r = wm * Cfg::kWaveM + i * 32 + lrow;
+        af[i] = *reinterpret_cast<const bf16x8 *>(
+            as + i * 32 * Cfg::kRowBytes + 16 * ((2 * kk + hh) ^ gemm_swz<Cfg::kChunks>(r)));
+      }
 #pragma unroll
-      for (int j = 0; j < Cfg::kFN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + j * 32 * kLdsRow + kk * 16);
+      for (int j = 0; j < Cfg::kFN; ++j) {
+        const int r = wn * Cfg::kWaveN + j * 32 + lrow;
+        bfr[j] = *reinterpret_cast<const bf16x8 *>(
+            bs + j * 32 * Cfg::kRowBytes + 16 * ((2 * kk + hh) ^ gemm_swz<Cfg::kChunks>(r)));
+      }
 #pragma unroll
       for (int i = 0; i < Cfg::kFM; ++i)
 #pragma unroll
         for (int j = 0; j < Cfg::kFN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_lds(buf ^ 1);
-    __syncthreads();
+    if (kt + 1 < nk) wait_tile(kt + 1);
   }
 
   // acc[i][j] holds D[n][m]: lane column m = lane % 32, rows n = 8g + 4h + r.
-  const int h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < Cfg::kFM; ++i) {
     const int gm = m0 + wm * Cfg::kWaveM + i * 32 + lrow;
@@ -128,7 +169,7 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
     for (int j = 0; j < Cfg::kFN; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int gn = n0 + wn * Cfg::kWaveN + j * 32 + 8 * g + 4 * h;
+        const int gn = n0 + wn * Cfg::kWaveN + j * 32 + 8 * g + 4 * hh;
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][g * 4 + r];
@@ -144,17 +185,17 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int NST>
 hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C, int M,
                        int N, int K, hipStream_t s) {
-  using Cfg = GemmCfg<BM, BN, WM, WN>;
+  using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
   const int tm = div_up_h(M, BM), tn = div_up_h(N, BN);
-  const size_t lds = Cfg::kLdsElems * sizeof(bf16);
-  hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_nt<BM, BN, WM, WN>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN>), dim3(tm * tn), dim3(Cfg::kThreads), lds, s,
-                     A, B0, B1, N0, C, M, N, K, tn);
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(Cfg::kThreads), Cfg::kLdsBytes, s, A, B0, B1, N0,
+                     C, M, N, K, tn);
   return hipGetLastError();
 }
 
@@ -219,11 +260,28 @@ gemv16_bf16_splitk(const bf16 *__restrict__ A, const bf16 *__restrict__ W0,
 
 hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C,
                                int M, int N, int K, hipStream_t s) {
-  // Big problems: 256x256 tiles (8 waves, 2 per SIMD). Smaller ones: 128x128
-  // tiles so that the grid still covers the 256 CUs.
-  const long tiles256 = (long)div_up_h(M, 256) * div_up_h(N, 256);
-  if (tiles256 >= 512) return launch_gemm<256, 256, 2, 4>(A, B0, B1, N0, C, M, N, K, s);
-  return launch_gemm<128, 128, 2, 2>(A, B0, B1, N0, C, M, N, K, s);
+  // Large problems: 256x256 tiles, 8 waves (2 per SIMD), two stages of BK = 64
+  // (measured best among 4/8 waves, BK 32/64, 2-4 stages on the 4B and 27B
+  // projection shapes). Pick the tile by a rounds x tile-cost model: a launch runs in rounds of
+  // 256 workgroups (one per CU); bigger tiles reuse operands better
+  // (relative per-output efficiency 1.0 / 0.9 / 0.75).
+  struct Opt { int bm, bn; double eff; };
+  const Opt opts[3] = {{256, 256, 1.0}, {128, 256, 0.9}, {128, 128, 0.75}};
+  int best = 0;
+  double best_cost = 1e300;
+  for (int i = 0; i < 3; ++i) {
+    const long tiles = (long)div_up_h(M, opts[i].bm) * div_up_h(N, opts[i].bn);
+    const double cost = (double)div_up_h(tiles, 256) * opts[i].bm * opts[i].bn / opts[i].eff;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = i;
+    }
+  }
+  switch (best) {
+    case 0: return launch_gemm<256, 256, 2, 4, 64, 2>(A, B0, B1, N0, C, M, N, K, s);
+    case 1: return launch_gemm<128, 256, 2, 4, 32, 4>(A, B0, B1, N0, C, M, N, K, s);
+    default: return launch_gemm<128, 128, 2, 2, 32, 4>(A, B0, B1, N0, C, M, N, K, s);
+  }
 }
 
 int gemv_ksplit(int N, int K) {

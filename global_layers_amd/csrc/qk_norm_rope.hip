@@ -160,32 +160,45 @@ qk_norm_rope_prefill(const T *__restrict__ qkv, const int32_t *__restrict__ pos,
   }
 }
 
-// V heads: [64 tokens][d_h] tile -> vt[b][kh][c][t0 .. t0+63] through LDS.
-// grid: x = B * (T_pad / 64), y = H_kv.
+// V heads: tiles of 64 tokens x 64 channels -> vt[b][kh][c][t0 .. t0+63]
+// through LDS, 16-byte global loads and stores (bf16) on both sides.
+// grid: x = T_pad / 64, y = ceil(d_h / 64), z = B * H_kv.
 template <typename T>
 __global__ void __launch_bounds__(256)
 v_transpose(const T *__restrict__ qkv, T *__restrict__ vt, NormRopeArgs a) {
-  __shared__ T tile[kTokBlock][kTileC + 2];
-  const int blocks_per_row = a.T_pad / kTokBlock;
-  const int b = blockIdx.x / blocks_per_row;
-  const int t0 = (blockIdx.x % blocks_per_row) * kTokBlock;
-  const int kh = blockIdx.y, d_h = a.d_h;
+  constexpr int kE = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int kPitch = 64 + 2;      // LDS row pitch (elements), breaks column conflicts
+  __shared__ T tile[64][kPitch];
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int b = blockIdx.z / a.Hk, kh = blockIdx.z % a.Hk, d_h = a.d_h;
   const int n_qkv = (a.H + 2 * a.Hk) * d_h;
   const int j = a.H + a.Hk + kh;
-  T *dst = vt + ((size_t)b * a.Hk + kh) * d_h * a.T_pad + t0;
-  for (int c0 = 0; c0 < d_h; c0 += kTileC) {
-    const int nc = min(kTileC, d_h - c0);
-    for (int e = threadIdx.x; e < kTokBlock * nc; e += blockDim.x) {
-      const int tt = e / nc, c = e % nc, t = t0 + tt;
-      tile[tt][c] =
-          t < a.T ? qkv[((size_t)b * a.T + t) * n_qkv + j * d_h + c0 + c] : from_f32<T>(0.f);
+  constexpr int kVecPerRow = 64 / kE;
+  for (int e = threadIdx.x; e < 64 * kVecPerRow; e += 256) {
+    const int tt = e / kVecPerRow, cv = (e % kVecPerRow) * kE, t = t0 + tt;
+    if (c0 + cv >= d_h) continue;  // d_h < 64 (fp32 path)
+    T v[kE];
+    if (t < a.T) {
+      const u32x4 raw = ld16(qkv + ((size_t)b * a.T + t) * n_qkv + j * d_h + c0 + cv);
+      const T *rv = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+      for (int i = 0; i < kE; ++i) v[i] = rv[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kE; ++i) v[i] = from_f32<T>(0.f);
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < kTokBlock * nc; e += blockDim.x) {
-      const int c = e / kTokBlock, tt = e % kTokBlock;
-      dst[(size_t)(c0 + c) * a.T_pad + tt] = tile[tt][c];
-    }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kE; ++i) tile[tt][cv + i] = v[i];
+  }
+  __syncthreads();
+  T *dst = vt + (((size_t)b * a.Hk + kh) * d_h + c0) * a.T_pad + t0;
+  for (int e = threadIdx.x; e < 64 * kVecPerRow; e += 256) {
+    const int c = e / kVecPerRow, tv = (e % kVecPerRow) * kE;
+    if (c0 + c >= d_h) continue;
+    T v[kE];
+#pragma unroll
+    for (int i = 0; i < kE; ++i) v[i] = tile[tv + i][c];
+    st16(dst + (size_t)c * a.T_pad + tv, *reinterpret_cast<const u32x4 *>(v));
   }
 }
 
@@ -274,8 +287,8 @@ hipError_t launch_qk_norm_rope(const T *qkv, const int32_t *pos, const T *gamma_
                      qkv, pos, gamma_q, gamma_k, q, k, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(v_transpose<T>, dim3(a.B * (a.T_pad / kTokBlock), a.Hk), dim3(256), 0, s,
-                     qkv, vt, a);
+  hipLaunchKernelGGL(v_transpose<T>, dim3(a.T_pad / 64, div_up_h(a.d_h, 64), a.B * a.Hk),
+                     dim3(256), 0, s, qkv, vt, a);
   return hipGetLastError();
 }
 
