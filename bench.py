@@ -260,7 +260,11 @@ def main():
 def bench_decode(args, torch, np, W, I, lib, dev):
     w = W.WORKLOADS[5]
     lengths = I.decode_lengths(w)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Cache flush between repetitions: reading 1 GiB leaves the 256 MB MALL
+    # full of clean lines of this buffer, so the timed reads start cold and
+    # evict nothing that must be written back first.
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
     out = {"workload": w.name, "B": w.B, "D": w.D, "H": w.H, "H_kv": w.H_kv, "d_h": w.d_h,
            "cache_slots": w.cache_len, "lengths_sum": int(lengths.sum())}
     for li, layer in enumerate(w.layers):
@@ -287,7 +291,7 @@ def bench_decode(args, torch, np, W, I, lib, dev):
         stage_t = {"qkv_proj": [], "qk_norm_cache_write": [], "attention": [], "out_proj": []}
         bits = [lib.DSTAGE_QKV_PROJ, lib.DSTAGE_QK_NORM, lib.DSTAGE_ATTN, lib.DSTAGE_OUT_PROJ]
         for _ in range(args.decode_reps):
-            flush.zero_()
+            flush.max()
             a, b = stream_events(torch)
             a.record()
             call()
@@ -296,7 +300,7 @@ def bench_decode(args, torch, np, W, I, lib, dev):
             times.append(a.elapsed_time(b))
             # stages one at a time, cache flushed before each
             for bit, key in zip(bits, stage_t):
-                flush.zero_()
+                flush.max()
                 a, b = stream_events(torch)
                 a.record()
                 call(bit)

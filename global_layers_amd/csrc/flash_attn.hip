@@ -31,6 +31,7 @@
 //    the key range of each query tile is cut into chunks handled by separate
 //    workgroups; a query tile with several chunks writes normalised partial
 //    outputs with their (m, l), merged by flash_combine.
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -44,27 +45,28 @@ constexpr int kRowsPerWave = 32;
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
 template <int D> struct AttnCfg {
-  // S of tile i+1 is issued before the softmax of tile i (needs a second S
-  // register set; at d_h = 256 that no longer fits beside O and Q).
-  static constexpr bool kPipeS = D <= 128;
   static constexpr int kKRowBytes = 2 * D;            // one key row of K
-  static constexpr int kKChunks = D / 8;              // 16-byte chunks per K row
-  static constexpr int kKTileBytes = kBN * kKRowBytes;
+  static constexpr int kKHalfBytes = 32 * kKRowBytes; // 32 keys of K (one key block)
   static constexpr int kVRowBytes = 2 * kBN;          // one channel row of V^T (128 B)
   static constexpr int kVTileBytes = D * kVRowBytes;
-  static constexpr int kLdsBytes = 2 * kKTileBytes + 2 * kVTileBytes;
-  static constexpr int kKLoads = kKTileBytes / 1024 / 4;  // 1 KB loads per wave per K tile
-  static constexpr int kVLoads = kVTileBytes / 1024 / 4;
-  static constexpr int kKS = D / 16;                      // k-steps of the QK^T contraction
-  static constexpr int kDB = D / 32;                      // 32-row blocks of O^T
+  // four K half-tile slots and two V^T tiles
+  static constexpr int kLdsBytes = 4 * kKHalfBytes + 2 * kVTileBytes;
+  static constexpr int kKHalfLoads = kKHalfBytes / 1024 / 4;  // 1 KB loads per wave per K half
+  static constexpr int kVLoads = kVTileBytes / 1024 / 4;      // per V tile
+  static constexpr int kKS = D / 16;                          // k-steps of the QK^T contraction
+  static constexpr int kDB = D / 32;                          // 32-row blocks of O^T
 };
 
-// XOR swizzles of the 16-byte chunk index inside a row. K fragment reads hit
-// rows kappa(i) for 8 lanes at a time, i.e. rows {0,1,2,3,8,9,10,11} + const;
-// V^T reads hit 8 consecutive rows. Both maps send those rows to 8 distinct
-// chunk positions mod 8, so each 128-byte LDS access spans all banks.
-DEVI int swz_k(int r) { return (r & 3) | ((r & 8) >> 1); }
-DEVI int swz_v(int r) { return r & 7; }
+// XOR swizzles of the 16-byte chunk index inside a row. The LDS serves a
+// 16-byte-per-lane read 16 lanes (256 bytes, all 64 banks) per cycle, so the
+// 16 rows that lanes 16j .. 16j+15 read must land on 16 distinct 16-byte bank
+// positions. K fragment reads of lanes 0-15 hit rows kappa(0..15), a
+// permutation of 0..15 (+32 per key block); V^T reads hit 16 consecutive rows.
+//  * rows of >= 256 bytes (K, d_h >= 128): position = chunk mod 16, so XOR with r & 15;
+//  * 128-byte rows (V^T, K at d_h = 64): position = 8 (r & 1) + chunk mod 8, so
+//    XOR with (r >> 1) & 7.
+template <int D> DEVI int swz_k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
+DEVI int swz_v(int r) { return (r >> 1) & 7; }
 
 // One direct global -> LDS load: each lane moves 16 bytes to lds + 16 * lane.
 DEVI void load_lds16(const void *g, void *lds_wave_base) {
@@ -110,7 +112,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     bf16 *__restrict__ part_o, float *__restrict__ part_ml, AttnArgs a, int gp,
                     int n_qtiles, int n_hgrp, int n_split, int chunk_keys) {
   using Cfg = AttnCfg<D>;
-  extern __shared__ __attribute__((aligned(16))) bf16 lds[];
+  extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.H / a.Hk;
@@ -126,7 +128,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int hg = w / wpg, tb = w % wpg;
   const int h = kh * G + geo.hgrp * gp + hg;
   const int wq0 = geo.t_lo + tb * kRowsPerWave;   // first query row of this wave
-  const int wq_last = min(wq0 + kRowsPerWave, a.T) - 1;
   const int len = geo.len;
   const int t_lo = geo.t_lo, t_hi = geo.t_hi;
 
@@ -153,67 +154,67 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   const char *kbase = (const char *)(k + ((size_t)b * a.Hk + kh) * a.T_pad * D);
   const char *vbase = (const char *)(vt + ((size_t)b * a.Hk + kh) * D * a.T_pad);
-  auto kbuf = [&](int i) { return (char *)lds + i * Cfg::kKTileBytes; };
-  auto vbuf = [&](int i) { return (char *)lds + 2 * Cfg::kKTileBytes + i * Cfg::kVTileBytes; };
-
-  // Wave w fills 1 KB pieces w, w + 4, ... of a tile. Lane l of piece j writes
-  // byte 16 l of it: K row r, chunk position p holds logical chunk p ^ swz_k(r).
-  auto issue_k = [&](int s0, char *dst) {
-#pragma unroll
-    for (int i = 0; i < Cfg::kKLoads; ++i) {
-      const int piece = w + 4 * i;
-      const int byte = piece * 1024 + 16 * lane;
-      const int r = byte / Cfg::kKRowBytes, pch = (byte % Cfg::kKRowBytes) / 16;
-      const int cch = pch ^ swz_k(r);
-      load_lds16(kbase + (size_t)(s0 + r) * Cfg::kKRowBytes + 16 * cch, dst + piece * 1024);
-    }
-  };
-  auto issue_v = [&](int s0, char *dst) {
-#pragma unroll
-    for (int i = 0; i < Cfg::kVLoads; ++i) {
-      const int piece = w + 4 * i;
-      const int byte = piece * 1024 + 16 * lane;
-      const int r = byte / Cfg::kVRowBytes, pch = (byte % Cfg::kVRowBytes) / 16;
-      const int cch = pch ^ swz_v(r);
-      load_lds16(vbase + (size_t)r * a.T_pad * 2 + (size_t)s0 * 2 + 16 * cch, dst + piece * 1024);
-    }
-  };
 
   const int n_tiles = my_end > my_begin ? div_up(my_end - my_begin, kBN) : 0;
+  // Loads past the last tile are clamped to it: such a load only rewrites a
+  // buffer that no later step reads.
+  auto tile_s0 = [&](int t) { return my_begin + min(t, n_tiles - 1) * kBN; };
+  // Wave w fills 1 KB pieces w, w + 4, ... of a buffer; lane l of piece j
+  // writes byte 16 l of it. K half h (tile h / 2, key block h % 2) sits in
+  // slot h % 4; its row r, chunk position p holds logical chunk p ^ swz_k(r).
+  auto issue_k_piece = [&](int half, int i) {
+    const int piece = w + 4 * i;
+    const int byte = piece * 1024 + 16 * lane;
+    const int r = byte / Cfg::kKRowBytes, pch = (byte % Cfg::kKRowBytes) / 16;
+    const int cch = pch ^ swz_k<D>(r);
+    const int row = tile_s0(half >> 1) + 32 * (half & 1) + r;
+    load_lds16(kbase + (size_t)row * Cfg::kKRowBytes + 16 * cch,
+               lds + (half & 3) * Cfg::kKHalfBytes + piece * 1024);
+  };
+  auto issue_v_piece = [&](int t, int i) {
+    const int piece = w + 4 * i;
+    const int byte = piece * 1024 + 16 * lane;
+    const int r = byte / Cfg::kVRowBytes, pch = (byte % Cfg::kVRowBytes) / 16;
+    const int cch = pch ^ swz_v(r);
+    load_lds16(vbase + (size_t)r * a.T_pad * 2 + (size_t)tile_s0(t) * 2 + 16 * cch,
+               lds + 4 * Cfg::kKHalfBytes + (t & 1) * Cfg::kVTileBytes + piece * 1024);
+  };
+
   if (n_tiles > 0) {
-    issue_k(my_begin, kbuf(0));
-    issue_v(my_begin, vbuf(0));
-    if (Cfg::kPipeS && n_tiles > 1) issue_k(my_begin + kBN, kbuf(1));
+#pragma unroll
+    for (int h = 0; h < 3; ++h)
+#pragma unroll
+      for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(h, i);
+#pragma unroll
+    for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(0, i);
   }
   // The barrier waits for every outstanding load (Q fragments, first tiles),
   // so inside the loop only the newest prefetches are ever pending.
   __syncthreads();
 
-  const int krow = kappa(col);  // permuted key row this lane feeds
-  auto wave_live = [&](int s0) {  // does any row of this wave see a key of the tile?
-    return s0 <= wq_last && !(a.local && s0 + kBN - 1 <= wq0 - a.window);
+  // Per-lane LDS byte offsets of the MFMA fragments. K: lane feeds row
+  // kappa(col) of a 32-key half and reads logical chunk 2 ks + hh; the swizzle
+  // only flips the low chunk bits, so 8 (4 at d_h = 64) base offsets plus
+  // compile-time immediates cover every k-step. V^T: row 32 db + col, chunk
+  // 2 kk + hh; 4 bases, db in the immediate.
+  constexpr int kKBases = Cfg::kKS < 8 ? Cfg::kKS : 8;
+  int koff[kKBases];
+  {
+    const int krow = kappa(col), ksw = swz_k<D>(krow);
+#pragma unroll
+    for (int j = 0; j < kKBases; ++j) koff[j] = krow * Cfg::kKRowBytes + 16 * ((2 * j + hh) ^ ksw);
+  }
+  int voff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    voff[kk] = 4 * Cfg::kKHalfBytes + col * Cfg::kVRowBytes + 16 * ((2 * kk + hh) ^ swz_v(col));
+  auto kfrag = [&](int half, int ks) {
+    return *reinterpret_cast<const bf16x8 *>(lds + (half & 3) * Cfg::kKHalfBytes +
+                                             koff[ks % kKBases] + (ks / kKBases) * 32 * kKBases);
   };
-  // S^T for the tile in kbuf: two 32-key blocks, reads batched ahead of MFMAs.
-  auto qk = [&](const char *kb_lds, f32x16 (&acc_s)[2]) {
-    constexpr int kBatch = Cfg::kKS < 8 ? Cfg::kKS : 8;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      acc_s[kb] = f32x16{};
-      const int r = 32 * kb + krow;
-      const char *rowp = kb_lds + r * Cfg::kKRowBytes;
-      const int sw = swz_k(r);
-#pragma unroll
-      for (int k0 = 0; k0 < Cfg::kKS; k0 += kBatch) {
-        bf16x8 kf[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-          kf[j] = *reinterpret_cast<const bf16x8 *>(rowp + 16 * ((2 * (k0 + j) + hh) ^ sw));
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-          acc_s[kb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[k0 + j], acc_s[kb], 0, 0, 0);
-      }
-    }
+  auto vfrag = [&](int t, int db, int kk) {
+    return *reinterpret_cast<const bf16x8 *>(lds + (t & 1) * Cfg::kVTileBytes +
+                                             db * 32 * Cfg::kVRowBytes + voff[kk]);
   };
 
   // Fixed softmax reference. |logit| <= |q_t| |k_s| (Cauchy-Schwarz) and a
@@ -241,121 +242,181 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   qq += __shfl_xor(qq, 32, kWave);
   // 1% margin covers the bf16 rounding of the stored keys
   const float m_fixed = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f * kLog2e;
-  const bool fixed_ok = __syncthreads_and(2.f * m_fixed <= 100.f);
 
-  auto run = [&](auto fixed_tag) {
+  // One half-step u = 2 it + kb handles keys s0 + 32 kb .. +31 of tile it
+  // (K half u). While its softmax and PV run, the S of half u + 1 goes to the
+  // matrix pipe and K half u + 3 and half of V tile it + 1 are prefetched into
+  // buffers last read before the previous barrier.
+  // Software pipeline in groups of 4 MFMAs: the fragments of group g+1 are
+  // read from LDS while group g's MFMAs run, and the exponentials and global
+  // prefetches are spread over the groups; scheduling fences between groups
+  // keep that order and bound the fragment registers.
+  auto half_step = [&](auto fixed_tag, auto masked_tag, auto next_tag, auto kb_tag, int it,
+                       f32x16 &s_cur, f32x16 &s_nxt) {
     constexpr bool kFixed = decltype(fixed_tag)::value;
-    f32x16 s_cur[2], s_next[2];
-    if (Cfg::kPipeS && n_tiles > 0 && wave_live(my_begin)) qk(kbuf(0), s_cur);
-    if (kFixed) m_ref = m_fixed;
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    constexpr bool kNext = decltype(next_tag)::value;
+    constexpr int kb = decltype(kb_tag)::value;
+    constexpr int kG = 4;                                  // MFMAs per group
+    constexpr int kNG = Cfg::kKS / kG;                     // groups of the S phase
+    constexpr int kEPG = 16 / kNG;                         // weights per group
+    constexpr int kVH = Cfg::kVLoads / 2;                  // V pieces per half-step
+    constexpr int kLoads = Cfg::kKHalfLoads + kVH;
+    constexpr int kLPG = (kLoads + kNG - 1) / kNG;         // prefetch pieces per group
+    constexpr int kPG = Cfg::kDB / 2;                      // PV groups (2 db x 2 kk)
+    const int u = 2 * it + kb;
+    const int s0 = my_begin + it * kBN + 32 * kb;
 
-    for (int it = 0; it < n_tiles; ++it) {
-      const int s0 = my_begin + it * kBN;
-      const int cur = it & 1, nxt = cur ^ 1;
-      // prefetch. Pipelined: K of tile it+2 into the K buffer tile `it` used
-      // (its S was formed last iteration); otherwise K of tile it+1. V of it+1.
-      if (Cfg::kPipeS) {
-        if (it + 2 < n_tiles) issue_k(s0 + 2 * kBN, kbuf(cur));
-      } else if (it + 1 < n_tiles) {
-        issue_k(s0 + kBN, kbuf(nxt));
+    if (kMasked) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int g = e >> 2, r = e & 3;
+        const int s = s0 + 16 * (g >> 1) + 8 * hh + 4 * (g & 1) + r;
+        const bool ok = s <= my_t && s < len && (!a.local || s > my_t - a.window);
+        s_cur[e] = ok ? s_cur[e] : -INFINITY;
       }
-      if (it + 1 < n_tiles) issue_v(s0 + kBN, vbuf(nxt));
-      // S of the next tile goes to the matrix pipe before this tile's softmax
-      if (Cfg::kPipeS) {
-        if (it + 1 < n_tiles && wave_live(s0 + kBN)) qk(kbuf(nxt), s_next);
-      } else if (wave_live(s0)) {
-        qk(kbuf(cur), s_cur);
+    }
+    if (!kFixed) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * kLog2e;
+      const bool need = mx > m_ref + kRescaleSlack;
+      if (__ballot(need)) {  // raise the reference (rare after the first tiles)
+        const float m_new = need ? mx : m_ref;
+        const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int db = 0; db < Cfg::kDB; ++db) acc_o[db] *= corr;
       }
+    }
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
 
-      if (wave_live(s0)) {
-        // tile-uniform mask decision for the whole workgroup
-        const bool full = (s0 + kBN - 1 <= t_lo) && (s0 + kBN - 1 < len) &&
-                          (!a.local || s0 >= t_hi - a.window);
-        float mx = -INFINITY;
+    // S phase: S of half u + 1 on the matrix pipe, this half's weights on the
+    // VALU, packed to bf16 pairs as they are formed. l sums the bf16-rounded
+    // weights the PV MFMAs use, so numerator and denominator of O / l carry
+    // the same rounding.
+    bf16x8 pf[2];
+    float psum = 0.f;
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+    bf16x8 kf[kG], kfn[kG], vf[4];
+    if (kNext) {
+      s_nxt = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int j = 0; j < kG; ++j) kf[j] = kfrag(u + 1, j);
+    }
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float x = s_cur[kb][e];
-            if (!full) {
-              const int g = e >> 2, r = e & 3;
-              const int s = s0 + 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1) + r;
-              const bool ok = s <= my_t && s < len && (!a.local || s > my_t - a.window);
-              x = ok ? x : -INFINITY;
-            }
-            s_cur[kb][e] = x;
-            if (!kFixed) mx = fmaxf(mx, x);
-          }
-        if (!kFixed) {
-          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * kLog2e;
-          const bool need = mx > m_ref + kRescaleSlack;
-          if (__ballot(need)) {  // raise the reference (rare after the first tiles)
-            const float m_new = need ? mx : m_ref;
-            const float corr =
-                m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-            m_ref = m_new;
-            l_run *= corr;
+    for (int g = 0; g < kNG; ++g) {
+      if (kNext && g + 1 < kNG) {
 #pragma unroll
-            for (int db = 0; db < Cfg::kDB; ++db) acc_o[db] *= corr;
-          }
-        }
-        const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            pf[2 * kb + (e >> 3)][e & 7] =
-                (bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][e], kLog2e, neg_m));
-        // l sums the bf16-rounded weights the PV MFMAs use, so numerator and
-        // denominator of O / l carry the same rounding
-        float psum = 0.f;
-        const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const u32x4 wv = __builtin_bit_cast(u32x4, pf[kk]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t pair = wv[j];
-            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, psum,
-                                                   false);
-          }
-        }
-        l_run += psum;
-
-        const char *vb_lds = vbuf(cur);
-#pragma unroll
-        for (int db0 = 0; db0 < Cfg::kDB; db0 += 2) {
-          bf16x8 vf[2][4];
-#pragma unroll
-          for (int d2 = 0; d2 < 2; ++d2) {
-            const int r = 32 * (db0 + d2) + col;
-            const char *rowp = vb_lds + r * Cfg::kVRowBytes;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              vf[d2][kk] =
-                  *reinterpret_cast<const bf16x8 *>(rowp + 16 * ((2 * kk + hh) ^ swz_v(r)));
-          }
-#pragma unroll
-          for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              acc_o[db0 + d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  vf[d2][kk], pf[kk], acc_o[db0 + d2], 0, 0, 0);
-        }
+        for (int j = 0; j < kG; ++j) kfn[j] = kfrag(u + 1, (g + 1) * kG + j);
       }
-      // the barrier also waits for this iteration's prefetches to land
-      __syncthreads();
-      if (Cfg::kPipeS) {
+      if (g + 1 == kNG) {  // V fragments of the first PV group
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
+        for (int j = 0; j < 4; ++j) vf[j] = vfrag(it, j >> 1, 2 * kb + (j & 1));
+      }
+#pragma unroll
+      for (int l = g * kLPG; l < (g + 1) * kLPG && l < kLoads; ++l) {
+        if (l < Cfg::kKHalfLoads)
+          issue_k_piece(u + 3, l);
+        else
+          issue_v_piece(it + 1, kb * kVH + l - Cfg::kKHalfLoads);
+      }
+      if (kNext) {
+#pragma unroll
+        for (int j = 0; j < kG; ++j)
+          s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[g * kG + j], s_nxt, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = g * kEPG; e < (g + 1) * kEPG; e += 2) {
+        bf16x2 pr;
+        pr[0] = (bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[e], kLog2e, neg_m));
+        pr[1] = (bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[e + 1], kLog2e, neg_m));
+        pf[e >> 3][e & 7] = pr[0];
+        pf[e >> 3][(e + 1) & 7] = pr[1];
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kG; ++j) kf[j] = kfn[j];
+    }
+    l_run += psum;
+
+    // PV phase: keys of this half (kk = 2 kb, 2 kb + 1), two 32-channel blocks
+    // of O^T per group, the next group's V fragments read ahead
+#pragma unroll
+    for (int pg = 0; pg < kPG; ++pg) {
+      bf16x8 vfn[4];
+      if (pg + 1 < kPG) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vfn[j] = vfrag(it, 2 * (pg + 1) + (j >> 1), 2 * kb + (j & 1));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int db = 2 * pg + (j >> 1);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j & 1], acc_o[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (pg + 1 < kPG) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vf[j] = vfn[j];
       }
     }
   };
+
+  // Tiles where no key is blocked for any row of the workgroup form one
+  // range [it_lo, it_hi] (the conditions are monotone in the tile start);
+  // they run a single straight-line body. The tiles before and after it (the
+  // start of a sliding window, the causal diagonal, padding) and the last tile
+  // take the masked body.
+  int it_lo = 0, it_hi = -1;
+  {
+    const int hi_s0 = min(t_lo, len - 1) - (kBN - 1);  // s0 <= hi_s0
+    const int lo_s0 = a.local ? t_hi - a.window : INT_MIN / 2;  // s0 >= lo_s0
+    if (hi_s0 >= my_begin) it_hi = (hi_s0 - my_begin) / kBN;
+    if (lo_s0 > my_begin) it_lo = div_up(lo_s0 - my_begin, kBN);
+  }
+  auto run = [&](auto fixed_tag, f32x16 s_a) {
+    constexpr bool kFixed = decltype(fixed_tag)::value;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    if (kFixed) m_ref = m_fixed;
+    f32x16 s_b;
+    auto masked_tile = [&](int it) {
+      half_step(fixed_tag, T_{}, T_{}, K0{}, it, s_a, s_b);
+      if (it + 1 < n_tiles)
+        half_step(fixed_tag, T_{}, T_{}, K1{}, it, s_b, s_a);
+      else
+        half_step(fixed_tag, T_{}, F_{}, K1{}, it, s_b, s_a);
+      // the barrier also waits for this tile's prefetches to land
+      __syncthreads();
+    };
+    int it = 0;
+    const int head_end = min(it_lo, n_tiles);
+    for (; it < head_end; ++it) masked_tile(it);
+    const int full_end = min(it_hi + 1, n_tiles - 1);
+    for (; it < full_end; ++it) {
+      half_step(fixed_tag, F_{}, T_{}, K0{}, it, s_a, s_b);
+      half_step(fixed_tag, F_{}, T_{}, K1{}, it, s_b, s_a);
+      __syncthreads();
+    }
+    for (; it < n_tiles; ++it) masked_tile(it);
+  };
+  // S of K half 0, formed before the barrier that precedes any write to its slot
+  f32x16 s0_first = f32x16{};
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int ks = 0; ks < Cfg::kKS; ++ks)
+      s0_first = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, ks), qf[ks], s0_first, 0, 0, 0);
+  }
+  const bool fixed_ok = __syncthreads_and(2.f * m_fixed <= 100.f);
   if (fixed_ok)
-    run(std::integral_constant<bool, true>{});
+    run(std::true_type{}, s0_first);
   else
-    run(std::integral_constant<bool, false>{});
+    run(std::false_type{}, s0_first);
 
   // Normalise; write the output row (single chunk) or a partial (several chunks).
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);

@@ -11,7 +11,7 @@
 //    first operand so that each lane ends up holding 4 consecutive output
 //    columns (one 8-byte store).
 //  * gemv16_bf16_splitk: decode (M = batch <= 16 per M block). Weight-streaming
-//    16x16x32 MFMAs, each wave one 16-column block over one K split, fp32
+//    16x16x32 MFMAs, each workgroup one 16-column block over one K split, fp32
 //    partials per split; the consumer adds the splits.
 #include "common.h"
 #include "kernels.h"
@@ -32,7 +32,7 @@ DEVI void load_lds16(const void *g, void *lds_wave_base) {
 
 // Tile of BM x BN outputs, K sliced by BK, NST LDS stages. Waves WM x WN.
 // Each stage holds A [BM][BK] and B [BN][BK] bf16, rows of BK*2 bytes, 16-byte
-// chunks XOR-swizzled by row so fragment reads by 8 consecutive rows hit all banks.
+// chunks XOR-swizzled by row so fragment reads by 16 consecutive rows hit all banks.
 template <int BM, int BN, int WM, int WN, int BK, int NST>
 struct GemmCfg {
   static constexpr int kThreads = WM * WN * kWave;
@@ -52,8 +52,12 @@ struct GemmCfg {
   static_assert(kChunks == 8 || kChunks == 4, "BK must be 64 or 32");
 };
 
+// Fragment reads of lanes 16j .. 16j+15 hit 16 consecutive rows; the LDS
+// serves 16 lanes x 16 bytes (all 64 banks) per cycle when their bank
+// positions differ: 128-byte rows sit at 8 (r & 1) + chunk mod 8, 64-byte rows
+// at 4 (r & 3) + chunk mod 4.
 template <int kChunks> DEVI int gemm_swz(int r) {
-  return kChunks == 8 ? (r & 7) : ((r >> 1) & 3);
+  return kChunks == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NST>
@@ -203,49 +207,55 @@ hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf
 // Decode projections: P[split][m][n] = sum_{k in split} A[m][k] * W[n][k]
 // ---------------------------------------------------------------------------
 constexpr int kGemvWaves = 4;
-constexpr int kGemvUnroll = 4;
+constexpr int kGemvUnroll = 8;  // weight loads a wave keeps in flight (1 KB each)
 
+// One workgroup = one 16-column block over one K split; its 4 waves take
+// consecutive quarters of the split's 32-wide k-steps and add their 16 x 16
+// accumulators through LDS, so the split count (and the partial traffic)
+// stays small while every CU still streams from many waves.
 __global__ void __launch_bounds__(kGemvWaves * 64)
 gemv16_bf16_splitk(const bf16 *__restrict__ A, const bf16 *__restrict__ W0,
                    const bf16 *__restrict__ W1, int N0, float *__restrict__ P, int M, int N, int K,
                    int k_per_split) {
+  __shared__ f32x4 red[kGemvWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nb = blockIdx.x * kGemvWaves + wave;       // 16-column block
+  const int nb = blockIdx.x;  // 16-column block
   const int split = blockIdx.y, mb = blockIdx.z;
-  if (nb * 16 >= N) return;
   const int n = nb * 16 + (lane & 15);
   const int m = mb * 16 + (lane & 15);
   const int koff = (lane >> 4) * 8;
-  const int k_begin = split * k_per_split, k_end = k_begin + k_per_split;
+  const int steps = k_per_split / 32;
+  const int per_wave = div_up(steps, kGemvWaves);
+  const int k_begin = split * k_per_split + wave * per_wave * 32;
+  const int k_end = min(split * k_per_split + k_per_split, k_begin + per_wave * 32);
   const bool n_ok = n < N, m_ok = m < M;
   const int nn = n_ok ? n : 0;
   const bf16 *wp = (nn < N0 ? W0 + (size_t)nn * K : W1 + (size_t)(nn - N0) * K) + koff;
   const bf16 *ap = A + (size_t)(m_ok ? m : 0) * K + koff;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int k = k_begin;
-  for (; k + 32 * kGemvUnroll <= k_end; k += 32 * kGemvUnroll) {
+  for (int k = k_begin; k < k_end; k += 32 * kGemvUnroll) {
     u32x4 wv[kGemvUnroll], av[kGemvUnroll];
+    // every load of the round is in flight before the first MFMA; steps past
+    // the range contribute zero operands
 #pragma unroll
     for (int u = 0; u < kGemvUnroll; ++u) {
-      wv[u] = ld16(wp + k + u * 32);
-      av[u] = ld16(ap + k + u * 32);
+      const int kk = k + u * 32;
+      const bool ok = kk < k_end;
+      wv[u] = ok && n_ok ? ld16(wp + kk) : u32x4{0, 0, 0, 0};
+      av[u] = ok && m_ok ? ld16(ap + kk) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kGemvUnroll; ++u) {
-      if (!n_ok) wv[u] = u32x4{0, 0, 0, 0};
-      if (!m_ok) av[u] = u32x4{0, 0, 0, 0};
+    for (int u = 0; u < kGemvUnroll; ++u)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
                                                      __builtin_bit_cast(bf16x8, wv[u]), acc,
                                                      0, 0, 0);
-    }
   }
-  for (; k < k_end; k += 32) {
-    u32x4 wv = n_ok ? ld16(wp + k) : u32x4{0, 0, 0, 0};
-    u32x4 av = m_ok ? ld16(ap + k) : u32x4{0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                   __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
-  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < kGemvWaves; ++w) acc += red[w][lane];
   // D[m][n]: lane column n = lane % 16, rows m = (lane / 16) * 4 + r.
   const int col = nb * 16 + (lane & 15);
   if (col >= N) return;
@@ -285,16 +295,17 @@ hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, in
 }
 
 int gemv_ksplit(int N, int K) {
-  const int nblk = div_up_h(N, 16);
+  // about 12+ waves per CU in flight (4 per workgroup), K splits of whole k-steps
+  const long nblk = div_up_h(N, 16);
   int s = 1;
-  while (s < 16 && (long)nblk * s < 2048) s *= 2;
+  while (s < 16 && nblk * s * kGemvWaves < 3072) s *= 2;
   while (s > 1 && (K / 32) % s != 0) s /= 2;
   return s;
 }
 
 hipError_t launch_gemv16_bf16(const bf16 *A, const bf16 *W0, const bf16 *W1, int N0, float *P,
                               int M, int N, int K, int ksplit, hipStream_t s) {
-  dim3 grid(div_up_h(div_up_h(N, 16), kGemvWaves), ksplit, div_up_h(M, 16));
+  dim3 grid(div_up_h(N, 16), ksplit, div_up_h(M, 16));
   hipLaunchKernelGGL(gemv16_bf16_splitk, grid, dim3(kGemvWaves * 64), 0, s, A, W0, W1, N0, P, M,
                      N, K, K / ksplit);
   return hipGetLastError();

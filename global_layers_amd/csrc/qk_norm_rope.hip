@@ -15,9 +15,7 @@
 
 namespace {
 
-constexpr int kTokBlock = 64;  // tokens per workgroup (one V transpose tile)
 constexpr int kMaxHalf = 128;  // d_h <= 256
-constexpr int kTileC = 128;    // channels per transpose pass
 
 DEVI void rope_sincos(int p, double inv_scale, double inv_freq, float &c, float &s) {
   const double two_pi = 6.283185307179586476925286766559;
@@ -67,28 +65,47 @@ template <> struct Pair8<float> {
   }
 };
 
-constexpr int kQkUnroll = 4;  // head-vector iterations whose loads are issued together
+constexpr int kQkUnroll = 2;  // head-vector iterations whose loads are issued together
+constexpr int kVtPitch = 64 + 2; // V transpose LDS row pitch (elements), breaks column conflicts
 
-// Q and K heads. One wave per token (B * T_pad tokens, 4 per block): the RoPE
-// (cos, sin) of the token's position are formed once per lane and reused by
-// every Q and K head of the token. A head vector is spread over d_h/16 lanes
-// (8 pairs per lane); a wave covers 64/(d_h/16) head vectors per iteration.
-// Key rows t in [T, T_pad) are written as zeros.
+// Q and K heads: one wave per token (4 per block). The token's RoPE (cos, sin)
+// are formed once, two pairs per lane, and shared through LDS with every Q
+// and K head of the token. A head vector is spread over d_h/16 lanes (8 pairs
+// per lane); a wave covers 64/(d_h/16) head vectors per iteration. Key rows
+// t in [T, T_pad) are written as zeros.
 template <typename T>
-__global__ void __launch_bounds__(256)
-qk_norm_rope_prefill(const T *__restrict__ qkv, const int32_t *__restrict__ pos,
-                     const T *__restrict__ gamma_q, const T *__restrict__ gamma_k,
-                     T *__restrict__ q, T *__restrict__ k, NormRopeArgs a) {
-  __shared__ double inv_freq[kMaxHalf];
+DEVI void norm_rope_tokens(const T *__restrict__ qkv, const int32_t *__restrict__ pos,
+                           const T *__restrict__ gamma_q, const T *__restrict__ gamma_k,
+                           T *__restrict__ q, T *__restrict__ k, const NormRopeArgs &a,
+                           int block, char *smem) {
+  double *inv_freq = reinterpret_cast<double *>(smem);                       // [kMaxHalf]
+  float2 *rot = reinterpret_cast<float2 *>(smem + kMaxHalf * sizeof(double)); // [4][kMaxHalf]
   const int d_h = a.d_h, half = d_h / 2;
-  for (int i = threadIdx.x; i < half; i += blockDim.x)
-    inv_freq[i] = pow((double)a.theta, -2.0 * (double)i / (double)d_h);
+  {
+    // theta^(-2i/d_h) = 2^(-(2i/d_h) log2 theta), in fp64
+    const double l2t = log2((double)a.theta);
+    for (int i = threadIdx.x; i < half; i += blockDim.x)
+      inv_freq[i] = exp2(-2.0 * (double)i / (double)d_h * l2t);
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long tok = (long)blockIdx.x * 4 + wave;  // over B * T_pad
-  if (tok >= (long)a.B * a.T_pad) return;
-  const int b = (int)(tok / a.T_pad), t = (int)(tok % a.T_pad);
+  const long tok = (long)block * 4 + wave;  // over B * T_pad
+  const bool live = tok < (long)a.B * a.T_pad;
+  const int b = live ? (int)(tok / a.T_pad) : 0, t = live ? (int)(tok % a.T_pad) : 0;
+  float2 *my_rot = rot + wave * kMaxHalf;
+  if (live && t < a.T) {
+    const int p = pos[(size_t)b * a.T + t];
+    const double inv_scale = 1.0 / (double)a.scale;
+    for (int i = lane; i < half; i += kWave) {
+      float c, sn;
+      rope_sincos(p, inv_scale, inv_freq[i], c, sn);
+      my_rot[i] = make_float2(c, sn);
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+
   const int lpv = d_h / 16;           // lanes per head vector
   const int vpw = kWave / lpv;        // head vectors per wave iteration
   const int sub = lane % lpv, vec = lane / lpv;
@@ -105,11 +122,11 @@ qk_norm_rope_prefill(const T *__restrict__ qkv, const int32_t *__restrict__ pos,
   }
 
   float cs[8], sn[8];
-  {
-    const int p = pos[(size_t)b * a.T + t];
-    const double inv_scale = 1.0 / (double)a.scale;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rope_sincos(p, inv_scale, inv_freq[i0 + i], cs[i], sn[i]);
+  for (int i = 0; i < 8; ++i) {
+    const float2 r = my_rot[i0 + i];
+    cs[i] = r.x;
+    sn[i] = r.y;
   }
   float gq1[8], gq2[8], gk1[8], gk2[8];
 #pragma unroll
@@ -162,15 +179,16 @@ qk_norm_rope_prefill(const T *__restrict__ qkv, const int32_t *__restrict__ pos,
 
 // V heads: tiles of 64 tokens x 64 channels -> vt[b][kh][c][t0 .. t0+63]
 // through LDS, 16-byte global loads and stores (bf16) on both sides.
-// grid: x = T_pad / 64, y = ceil(d_h / 64), z = B * H_kv.
+// Tile index: ((b * Hk + kh) * ceil(d_h / 64) + channel tile) * (T_pad / 64) + token tile.
 template <typename T>
-__global__ void __launch_bounds__(256)
-v_transpose(const T *__restrict__ qkv, T *__restrict__ vt, NormRopeArgs a) {
+DEVI void v_transpose_tile(const T *__restrict__ qkv, T *__restrict__ vt, const NormRopeArgs &a,
+                           int tile_id, char *smem) {
   constexpr int kE = 16 / sizeof(T);  // elements per 16-byte vector
-  constexpr int kPitch = 64 + 2;      // LDS row pitch (elements), breaks column conflicts
-  __shared__ T tile[64][kPitch];
-  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int b = blockIdx.z / a.Hk, kh = blockIdx.z % a.Hk, d_h = a.d_h;
+  T (*tile)[kVtPitch] = reinterpret_cast<T (*)[kVtPitch]>(smem);
+  const int n_tt = a.T_pad / 64, n_ct = div_up(a.d_h, 64);
+  const int t0 = (tile_id % n_tt) * 64, c0 = ((tile_id / n_tt) % n_ct) * 64;
+  const int bk = tile_id / (n_tt * n_ct);
+  const int b = bk / a.Hk, kh = bk % a.Hk, d_h = a.d_h;
   const int n_qkv = (a.H + 2 * a.Hk) * d_h;
   const int j = a.H + a.Hk + kh;
   constexpr int kVecPerRow = 64 / kE;
@@ -200,6 +218,28 @@ v_transpose(const T *__restrict__ qkv, T *__restrict__ vt, NormRopeArgs a) {
     for (int i = 0; i < kE; ++i) v[i] = tile[tv + i][c];
     st16(dst + (size_t)c * a.T_pad + tv, *reinterpret_cast<const u32x4 *>(v));
   }
+}
+
+template <typename T> constexpr int norm_smem_bytes() {
+  constexpr int rope = kMaxHalf * sizeof(double) + 4 * kMaxHalf * sizeof(float2);
+  constexpr int vt = 64 * kVtPitch * sizeof(T);
+  return rope > vt ? rope : vt;
+}
+
+// One launch for the whole stage: blocks [0, n_tok_blocks) run the Q/K heads
+// of 4 tokens each, the rest transpose one V tile each, so the two memory
+// passes overlap instead of running back to back.
+template <typename T>
+__global__ void __launch_bounds__(256)
+qk_norm_rope_prefill(const T *__restrict__ qkv, const int32_t *__restrict__ pos,
+                     const T *__restrict__ gamma_q, const T *__restrict__ gamma_k,
+                     T *__restrict__ q, T *__restrict__ k, T *__restrict__ vt, NormRopeArgs a,
+                     int n_tok_blocks) {
+  __shared__ __attribute__((aligned(16))) char smem[norm_smem_bytes<T>()];
+  if ((int)blockIdx.x < n_tok_blocks)
+    norm_rope_tokens<T>(qkv, pos, gamma_q, gamma_k, q, k, a, blockIdx.x, smem);
+  else
+    v_transpose_tile<T>(qkv, vt, a, blockIdx.x - n_tok_blocks, smem);
 }
 
 // grid: x = B, y = H + 2 Hk; one wave per (row, head vector).
@@ -283,12 +323,10 @@ hipError_t launch_qk_norm_rope(const T *qkv, const int32_t *pos, const T *gamma_
                                const T *gamma_k, T *q, T *k, T *vt, const NormRopeArgs &a,
                                hipStream_t s) {
   const long toks = (long)a.B * a.T_pad;
-  hipLaunchKernelGGL(qk_norm_rope_prefill<T>, dim3((unsigned)div_up_h(toks, 4)), dim3(256), 0, s,
-                     qkv, pos, gamma_q, gamma_k, q, k, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(v_transpose<T>, dim3(a.T_pad / 64, div_up_h(a.d_h, 64), a.B * a.Hk),
-                     dim3(256), 0, s, qkv, vt, a);
+  const int n_tok_blocks = (int)div_up_h(toks, 4);
+  const long n_vt = (long)(a.T_pad / 64) * div_up_h(a.d_h, 64) * a.B * a.Hk;
+  hipLaunchKernelGGL(qk_norm_rope_prefill<T>, dim3((unsigned)(n_tok_blocks + n_vt)), dim3(256), 0,
+                     s, qkv, pos, gamma_q, gamma_k, q, k, vt, a, n_tok_blocks);
   return hipGetLastError();
 }
 
