@@ -68,10 +68,30 @@ template <int D> struct AttnCfg {
 template <int D> DEVI int swz_k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
 DEVI int swz_v(int r) { return (r >> 1) & 7; }
 
-// One direct global -> LDS load: each lane moves 16 bytes to lds + 16 * lane.
-DEVI void load_lds16(const void *g, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave_base,
-                                   16, 0, 0);
+// One direct global -> LDS load: lane l moves the 16 bytes at
+// sbase + lane_off (sbase wave-uniform) to LDS byte lds_wave_off + 16 l
+// (lds_wave_off wave-uniform). Written as inline assembly: the compiler counts an
+// LDS-writing load as a memory access of unknown order and would then make
+// every later LDS fragment read wait for all LDS reads in flight; hidden from
+// it, those reads keep their partial waits (which stay correct whether or
+// not the load also counts in lgkmcnt: waiting for <= k outstanding still
+// retires the oldest reads). Callers wait for completion explicitly
+// (publish_tiles) before the barrier that hands the data to other waves, and
+// only ever target a buffer that no wave reads before that barrier.
+DEVI void load_lds16(const void *sbase, uint32_t lane_off, uint32_t lds_wave_off) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"(sbase), "s"(lds_wave_off)
+               : "memory", "m0");
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0) and lgkmcnt(0), expcnt free.
+constexpr int kWaitVmLgkm0 = 0x7 << 4;
+
+// All of this wave's tile loads have landed; then every wave's have.
+DEVI void publish_tiles() {
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+  __syncthreads();
 }
 
 // Key permutation inside a 32-key block (see the header comment).
@@ -104,13 +124,18 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
   return g;
 }
 
-template <int D>
+// kFixed: the fixed-reference kernel. A workgroup whose rows fail the bound
+// below records that in fallback[workgroup] and exits; the running-max
+// instantiation (kFixed = false), launched next, runs only those workgroups.
+// Two kernels keep the rare path's registers out of the common one.
+template <int D, bool kFixed>
 __global__ void __launch_bounds__(kThreads)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
                     const bf16 *__restrict__ gamma_k, bf16 *__restrict__ o,
-                    bf16 *__restrict__ part_o, float *__restrict__ part_ml, AttnArgs a, int gp,
-                    int n_qtiles, int n_hgrp, int n_split, int chunk_keys) {
+                    bf16 *__restrict__ part_o, float *__restrict__ part_ml,
+                    int32_t *__restrict__ fallback, AttnArgs a, int gp, int n_qtiles, int n_hgrp,
+                    int n_split, int chunk_keys, int force_running_max) {
   using Cfg = AttnCfg<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -122,6 +147,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int split = bid % n_split;
   const Geo geo = geometry(a, kv_len, bid / n_split, gp, n_qtiles, n_hgrp, chunk_keys);
   if (split >= geo.n_active) return;  // uniform per block
+  if (!kFixed && fallback[blockIdx.x] == 0) return;  // done by the fixed-reference kernel
   const int b = geo.b, kh = geo.kh;
 
   const int wpg = 4 / gp;  // waves per query head
@@ -162,35 +188,49 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // Wave w fills 1 KB pieces w, w + 4, ... of a buffer; lane l of piece j
   // writes byte 16 l of it. K half h (tile h / 2, key block h % 2) sits in
   // slot h % 4; its row r, chunk position p holds logical chunk p ^ swz_k(r).
-  auto issue_k_piece = [&](int half, int i) {
-    const int piece = w + 4 * i;
-    const int byte = piece * 1024 + 16 * lane;
+  // Global addresses split into a wave-uniform base and a per-lane 32-bit
+  // offset. The swizzle pattern of K pieces repeats every 2 pieces (V: every
+  // piece), and pieces i and i + 2 (V: i + 1) are a fixed number of rows apart,
+  // so two (one) lane offsets plus a uniform step cover every piece.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t k_lane[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int byte = (w + 4 * i) * 1024 + 16 * lane;
     const int r = byte / Cfg::kKRowBytes, pch = (byte % Cfg::kKRowBytes) / 16;
-    const int cch = pch ^ swz_k<D>(r);
-    const int row = tile_s0(half >> 1) + 32 * (half & 1) + r;
-    load_lds16(kbase + (size_t)row * Cfg::kKRowBytes + 16 * cch,
-               lds + (half & 3) * Cfg::kKHalfBytes + piece * 1024);
-  };
-  auto issue_v_piece = [&](int t, int i) {
-    const int piece = w + 4 * i;
-    const int byte = piece * 1024 + 16 * lane;
+    k_lane[i] = (uint32_t)(r * Cfg::kKRowBytes + 16 * (pch ^ swz_k<D>(r)));
+  }
+  uint32_t v_lane;
+  {
+    const int byte = w * 1024 + 16 * lane;
     const int r = byte / Cfg::kVRowBytes, pch = (byte % Cfg::kVRowBytes) / 16;
-    const int cch = pch ^ swz_v(r);
-    load_lds16(vbase + (size_t)r * a.T_pad * 2 + (size_t)tile_s0(t) * 2 + 16 * cch,
-               lds + 4 * Cfg::kKHalfBytes + (t & 1) * Cfg::kVTileBytes + piece * 1024);
+    v_lane = (uint32_t)(r * a.T_pad * 2 + 16 * (pch ^ swz_v(r)));
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+  // K rows 32 kbh .. 32 kbh + 31 of tile t into half slot `slot`
+  auto issue_k_piece = [&](int t, int kbh, int slot, int i) {
+    const char *src =
+        kbase + (size_t)(tile_s0(t) + 32 * kbh) * Cfg::kKRowBytes + (size_t)(i >> 1) * 8192;
+    load_lds16(src, k_lane[i & 1], lds0 + slot * Cfg::kKHalfBytes + (wu + 4 * i) * 1024);
+  };
+  // V^T columns of tile t into V buffer `buf` (piece i: channel rows 32 i + ...)
+  auto issue_v_piece = [&](int t, int buf, int i) {
+    const char *src = vbase + (size_t)tile_s0(t) * 2 + (size_t)i * 32 * a.T_pad * 2;
+    load_lds16(src, v_lane,
+               lds0 + 4 * Cfg::kKHalfBytes + buf * Cfg::kVTileBytes + (wu + 4 * i) * 1024);
   };
 
-  if (n_tiles > 0) {
+  if (n_tiles > 0) {  // K halves 0, 1, 2 (slots 0-2) and V tile 0
 #pragma unroll
     for (int h = 0; h < 3; ++h)
 #pragma unroll
-      for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(h, i);
+      for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(h >> 1, h & 1, h, i);
 #pragma unroll
-    for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(0, i);
+    for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(0, 0, i);
   }
-  // The barrier waits for every outstanding load (Q fragments, first tiles),
-  // so inside the loop only the newest prefetches are ever pending.
-  __syncthreads();
+  // Every outstanding load (Q fragments, first tiles) lands before the loop,
+  // so inside it only the newest prefetches are ever pending.
+  publish_tiles();
 
   // Per-lane LDS byte offsets of the MFMA fragments. K: lane feeds row
   // kappa(col) of a 32-key half and reads logical chunk 2 ks + hh; the swizzle
@@ -208,12 +248,12 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     voff[kk] = 4 * Cfg::kKHalfBytes + col * Cfg::kVRowBytes + 16 * ((2 * kk + hh) ^ swz_v(col));
-  auto kfrag = [&](int half, int ks) {
-    return *reinterpret_cast<const bf16x8 *>(lds + (half & 3) * Cfg::kKHalfBytes +
-                                             koff[ks % kKBases] + (ks / kKBases) * 32 * kKBases);
+  auto kfrag = [&](int slot, int ks) {
+    return *reinterpret_cast<const bf16x8 *>(lds + slot * Cfg::kKHalfBytes + koff[ks % kKBases] +
+                                             (ks / kKBases) * 32 * kKBases);
   };
-  auto vfrag = [&](int t, int db, int kk) {
-    return *reinterpret_cast<const bf16x8 *>(lds + (t & 1) * Cfg::kVTileBytes +
+  auto vfrag = [&](int buf, int db, int kk) {
+    return *reinterpret_cast<const bf16x8 *>(lds + buf * Cfg::kVTileBytes +
                                              db * 32 * Cfg::kVRowBytes + voff[kk]);
   };
 
@@ -245,26 +285,26 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // One half-step u = 2 it + kb handles keys s0 + 32 kb .. +31 of tile it
   // (K half u). While its softmax and PV run, the S of half u + 1 goes to the
-  // matrix pipe and K half u + 3 and half of V tile it + 1 are prefetched into
-  // buffers last read before the previous barrier.
+  // matrix pipe; the first half-step of a tile also prefetches K halves u + 3,
+  // u + 4 and V tile it + 1 into buffers last read before the previous barrier.
   // Software pipeline in groups of 4 MFMAs: the fragments of group g+1 are
   // read from LDS while group g's MFMAs run, and the exponentials and global
   // prefetches are spread over the groups; scheduling fences between groups
   // keep that order and bound the fragment registers.
-  auto half_step = [&](auto fixed_tag, auto masked_tag, auto next_tag, auto kb_tag, int it,
-                       f32x16 &s_cur, f32x16 &s_nxt) {
-    constexpr bool kFixed = decltype(fixed_tag)::value;
+  // par_tag: the parity of `it` when known at compile time (then every LDS
+  // slot and buffer index below is an immediate), else -1.
+  auto half_step = [&](auto masked_tag, auto next_tag, auto kb_tag, auto par_tag,
+                       int it, f32x16 &s_cur, f32x16 &s_nxt) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;
     constexpr int kb = decltype(kb_tag)::value;
+    constexpr int kPar = decltype(par_tag)::value;
+    const int par = kPar >= 0 ? kPar : (it & 1);
+    const int u_slot = 2 * par + kb;  // K half u sits in slot u_slot & 3
     constexpr int kG = 4;                                  // MFMAs per group
     constexpr int kNG = Cfg::kKS / kG;                     // groups of the S phase
     constexpr int kEPG = 16 / kNG;                         // weights per group
-    constexpr int kVH = Cfg::kVLoads / 2;                  // V pieces per half-step
-    constexpr int kLoads = Cfg::kKHalfLoads + kVH;
-    constexpr int kLPG = (kLoads + kNG - 1) / kNG;         // prefetch pieces per group
     constexpr int kPG = Cfg::kDB / 2;                      // PV groups (2 db x 2 kk)
-    const int u = 2 * it + kb;
     const int s0 = my_begin + it * kBN + 32 * kb;
 
     if (kMasked) {
@@ -301,27 +341,30 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     float psum = 0.f;
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
     bf16x8 kf[kG], kfn[kG], vf[4];
+    // Every prefetch of tile it is issued in its first half-step, so it has
+    // the whole tile to land before the barrier: K halves 2 it + 3 and
+    // 2 it + 4 here (their slots were last read before the previous barrier),
+    // V tile it + 1 at the start of the PV phase.
+    if (kb == 0) {
+#pragma unroll
+      for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(it + 1, 1, (u_slot + 3) & 3, i);
+#pragma unroll
+      for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(it + 2, 0, (u_slot + 4) & 3, i);
+    }
     if (kNext) {
       s_nxt = f32x16{};
 #pragma unroll
-      for (int j = 0; j < kG; ++j) kf[j] = kfrag(u + 1, j);
+      for (int j = 0; j < kG; ++j) kf[j] = kfrag((u_slot + 1) & 3, j);
     }
 #pragma unroll
     for (int g = 0; g < kNG; ++g) {
       if (kNext && g + 1 < kNG) {
 #pragma unroll
-        for (int j = 0; j < kG; ++j) kfn[j] = kfrag(u + 1, (g + 1) * kG + j);
+        for (int j = 0; j < kG; ++j) kfn[j] = kfrag((u_slot + 1) & 3, (g + 1) * kG + j);
       }
       if (g + 1 == kNG) {  // V fragments of the first PV group
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vf[j] = vfrag(it, j >> 1, 2 * kb + (j & 1));
-      }
-#pragma unroll
-      for (int l = g * kLPG; l < (g + 1) * kLPG && l < kLoads; ++l) {
-        if (l < Cfg::kKHalfLoads)
-          issue_k_piece(u + 3, l);
-        else
-          issue_v_piece(it + 1, kb * kVH + l - Cfg::kKHalfLoads);
+        for (int j = 0; j < 4; ++j) vf[j] = vfrag(par, j >> 1, 2 * kb + (j & 1));
       }
       if (kNext) {
 #pragma unroll
@@ -337,6 +380,15 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         pf[e >> 3][(e + 1) & 7] = pr[1];
         psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
       }
+      // order inside the group: LDS reads for the next group, then each MFMA
+      // followed by its share of the softmax arithmetic
+      if (kNext && g + 1 < kNG) __builtin_amdgcn_sched_group_barrier(0x100, kG, 0);
+      if (g + 1 == kNG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int j = 0; j < kG; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3 * kEPG / kG, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < kG; ++j) kf[j] = kfn[j];
@@ -345,18 +397,25 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
     // PV phase: keys of this half (kk = 2 kb, 2 kb + 1), two 32-channel blocks
     // of O^T per group, the next group's V fragments read ahead
+    if (kb == 0) {
+#pragma unroll
+      for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(it + 1, par ^ 1, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int pg = 0; pg < kPG; ++pg) {
       bf16x8 vfn[4];
       if (pg + 1 < kPG) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vfn[j] = vfrag(it, 2 * (pg + 1) + (j >> 1), 2 * kb + (j & 1));
+        for (int j = 0; j < 4; ++j) vfn[j] = vfrag(par, 2 * (pg + 1) + (j >> 1), 2 * kb + (j & 1));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int db = 2 * pg + (j >> 1);
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j & 1], acc_o[db], 0, 0, 0);
       }
+      if (pg + 1 < kPG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (pg + 1 < kPG) {
 #pragma unroll
@@ -377,32 +436,40 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (hi_s0 >= my_begin) it_hi = (hi_s0 - my_begin) / kBN;
     if (lo_s0 > my_begin) it_lo = div_up(lo_s0 - my_begin, kBN);
   }
-  auto run = [&](auto fixed_tag, f32x16 s_a) {
-    constexpr bool kFixed = decltype(fixed_tag)::value;
+  auto run = [&](f32x16 s_a) {
     using T_ = std::true_type;
     using F_ = std::false_type;
     using K0 = std::integral_constant<int, 0>;
     using K1 = std::integral_constant<int, 1>;
     if (kFixed) m_ref = m_fixed;
     f32x16 s_b;
+    using PR = std::integral_constant<int, -1>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     auto masked_tile = [&](int it) {
-      half_step(fixed_tag, T_{}, T_{}, K0{}, it, s_a, s_b);
+      half_step(T_{}, T_{}, K0{}, PR{}, it, s_a, s_b);
       if (it + 1 < n_tiles)
-        half_step(fixed_tag, T_{}, T_{}, K1{}, it, s_b, s_a);
+        half_step(T_{}, T_{}, K1{}, PR{}, it, s_b, s_a);
       else
-        half_step(fixed_tag, T_{}, F_{}, K1{}, it, s_b, s_a);
-      // the barrier also waits for this tile's prefetches to land
-      __syncthreads();
+        half_step(T_{}, F_{}, K1{}, PR{}, it, s_b, s_a);
+      publish_tiles();  // this tile's prefetches have landed
+    };
+    auto full_tile = [&](auto par_tag, int it) {
+      half_step(F_{}, T_{}, K0{}, par_tag, it, s_a, s_b);
+      half_step(F_{}, T_{}, K1{}, par_tag, it, s_b, s_a);
+      publish_tiles();
     };
     int it = 0;
     const int head_end = min(it_lo, n_tiles);
     for (; it < head_end; ++it) masked_tile(it);
     const int full_end = min(it_hi + 1, n_tiles - 1);
-    for (; it < full_end; ++it) {
-      half_step(fixed_tag, F_{}, T_{}, K0{}, it, s_a, s_b);
-      half_step(fixed_tag, F_{}, T_{}, K1{}, it, s_b, s_a);
-      __syncthreads();
+    // full tiles in pairs of known parity
+    if (it < full_end && (it & 1)) full_tile(P1{}, it++);
+    for (; it + 1 < full_end; it += 2) {
+      full_tile(P0{}, it);
+      full_tile(P1{}, it + 1);
     }
+    if (it < full_end) full_tile(P0{}, it++);
     for (; it < n_tiles; ++it) masked_tile(it);
   };
   // S of K half 0, formed before the barrier that precedes any write to its slot
@@ -412,11 +479,13 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int ks = 0; ks < Cfg::kKS; ++ks)
       s0_first = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, ks), qf[ks], s0_first, 0, 0, 0);
   }
-  const bool fixed_ok = __syncthreads_and(2.f * m_fixed <= 100.f);
-  if (fixed_ok)
-    run(std::true_type{}, s0_first);
-  else
-    run(std::false_type{}, s0_first);
+  if constexpr (kFixed) {
+    // every load this workgroup issued has landed (publish_tiles above)
+    const bool fixed_ok = __syncthreads_and(2.f * m_fixed <= 100.f) && !force_running_max;
+    if (tid == 0) fallback[blockIdx.x] = fixed_ok ? 0 : 1;
+    if (!fixed_ok) return;
+  }
+  run(s0_first);
 
   // Normalise; write the output row (single chunk) or a partial (several chunks).
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
@@ -539,18 +608,25 @@ Plan plan(const AttnArgs &a) {
 
 template <int D>
 hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
-                    const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
-                    hipStream_t s) {
+                    const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, int32_t *fallback,
+                    const AttnArgs &a, int force, hipStream_t s) {
   using Cfg = AttnCfg<D>;
   const Plan p = plan(a);
-  hipError_t e = hipFuncSetAttribute((const void *)flash_attn_fwd_bf16<D>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     Cfg::kLdsBytes);
+  const dim3 grid((unsigned)(p.n_base * p.n_split));
+  hipError_t e = hipFuncSetAttribute((const void *)flash_attn_fwd_bf16<D, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void *)flash_attn_fwd_bf16<D, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(flash_attn_fwd_bf16<D>, dim3((unsigned)(p.n_base * p.n_split)),
-                     dim3(kThreads), Cfg::kLdsBytes, s, q, k, vt, kv_len, gamma_k, o, part_o,
-                     part_ml, a,
-                     p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys);
+  hipLaunchKernelGGL((flash_attn_fwd_bf16<D, true>), grid, dim3(kThreads), Cfg::kLdsBytes, s, q, k,
+                     vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, p.gp, p.n_qtiles,
+                     p.n_hgrp, p.n_split, p.chunk_keys, force);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((flash_attn_fwd_bf16<D, false>), grid, dim3(kThreads), Cfg::kLdsBytes, s, q,
+                     k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, p.gp, p.n_qtiles,
+                     p.n_hgrp, p.n_split, p.chunk_keys, force);
   e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const long rows = (long)a.B * a.H * a.T;
@@ -561,22 +637,30 @@ hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t 
 
 }  // namespace
 
+// Layout: split partial outputs [n_split][B][H][T][d_h] bf16 and their
+// (m, l) pairs (only when the key range is split), then one fallback flag
+// per attention workgroup.
 size_t flash_attn_partial_bytes(const AttnArgs &a) {
   const Plan p = plan(a);
-  if (p.n_split == 1) return 0;
-  return (size_t)p.n_split * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8);
+  const size_t flags = (size_t)p.n_base * p.n_split * sizeof(int32_t);
+  if (p.n_split == 1) return flags;
+  return (size_t)p.n_split * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8) + flags;
 }
 
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
                                   const int32_t *kv_len, const bf16 *gamma_k, bf16 *o,
-                                  void *partial, const AttnArgs &a, hipStream_t s) {
-  const size_t rows = (size_t)plan(a).n_split * a.B * a.H * a.T;
+                                  void *partial, const AttnArgs &a, bool force_running_max,
+                                  hipStream_t s) {
+  const int force = force_running_max ? 1 : 0;
+  const Plan p = plan(a);
+  const size_t rows = p.n_split == 1 ? 0 : (size_t)p.n_split * a.B * a.H * a.T;
   bf16 *part_o = (bf16 *)partial;
-  float *part_ml = partial ? (float *)((char *)partial + rows * a.d_h * 2) : nullptr;
+  float *part_ml = (float *)((char *)partial + rows * a.d_h * 2);
+  int32_t *fallback = (int32_t *)((char *)part_ml + rows * 8);
   switch (a.d_h) {
-    case 64: return launch_d<64>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, s);
-    case 128: return launch_d<128>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, s);
-    case 256: return launch_d<256>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, s);
+    case 64: return launch_d<64>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, force, s);
+    case 128: return launch_d<128>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, force, s);
+    case 256: return launch_d<256>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, force, s);
     default: return hipErrorInvalidValue;
   }
 }

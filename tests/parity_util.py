@@ -59,10 +59,11 @@ def oracle_kw(kw: dict) -> dict:
                 rope_scale=kw["rope_scale"], query_scale=kw["query_scale"])
 
 
-def gpu_prefill(lib, inp_cpu: dict, kw: dict, workspace=None):
+def gpu_prefill(lib, inp_cpu: dict, kw: dict, workspace=None, stages=None):
     d = to_dev(inp_cpu)
+    extra = {} if stages is None else {"stages": stages}
     y = lib.prefill(d["x"], d["segment_pos"], weights_of(d), kv_valid_len=d.get("kv_valid_len"),
-                    workspace=workspace, **kw)
+                    workspace=workspace, **kw, **extra)
     torch.cuda.synchronize()
     return y
 
