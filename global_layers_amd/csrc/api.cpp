@@ -151,8 +151,9 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
     const AttnArgs a = attn_args(d, L.T_pad);
     if (bf)
       RUN(launch_flash_attn_bf16((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, kv_len,
-                                 (const bf16 *)w->gamma_k, (bf16 *)o, base + L.attn_part, a,
-                                 (stages & GEMMA3_STAGE_FORCE_RUNNING_MAX) != 0, s));
+                                 (const bf16 *)w->gamma_k, (bf16 *)o,
+                                 L.attn_part ? base + L.attn_part : nullptr, a,
+                                 (stages & GEMMA3_STAGE_FORCE_EXACT_MAX) != 0, s));
     else
       RUN(launch_attn_f32((const float *)q, (const float *)k, (const float *)vt, kv_len,
                           (float *)o, a, s));

@@ -3,7 +3,7 @@
 // padding mask, times the sliding mask 1[s > t-W] 1[s < t+W] on local layers;
 // blocked logits take the K_MASK fill; softmax over s; weights mix V).
 //
-// Exact tiled evaluation (online softmax) of that definition:
+// Exact tiled evaluation of that definition:
 //  * Blocked logits get exactly zero weight, as K_MASK does in fp32 whenever a
 //    row has an allowed key; the fill value itself is never formed. Tiles that
 //    no row of the workgroup may see are never visited.
@@ -11,22 +11,23 @@
 //    of a GQA group (up to 4) are packed into the workgroup, so each K/V tile
 //    staged in LDS feeds every query head that reads it.
 //  * Each wave computes S^T = K Q^T with 32x32x16 bf16 MFMAs: a lane owns one
-//    query row and 32 of the 64 keys of a tile, so row max and row sum need
-//    one cross-lane step (lane ^ 32). K rows are fed in the permuted order
-//    kappa(i) so that the S^T accumulators of a lane are, in register order,
-//    the 16-byte B operand of the PV MFMA (O^T += V^T P^T) without moving data.
+//    query row and 32 of the 64 keys of a tile. K rows are fed in the
+//    permuted order kappa(i) so that the S^T accumulators of a lane are, in
+//    register order, the 16-byte B operand of the PV MFMA (O^T += V^T P^T)
+//    without moving data.
 //  * V arrives transposed ([d_h][T]) so the PV A operand is a contiguous
 //    16-byte LDS read.
-//  * Softmax reference max m is only raised when a logit exceeds it by more
-//    than 8 (log2 units), so exp2 arguments stay <= 8 and the O/l rescale is
-//    skipped for the whole wave on most tiles. The result is unchanged: l and
-//    O share the same reference, which cancels in O / l.
-//  * Tiles move global -> LDS with direct loads (global_load_lds, 16 bytes
-//    per lane, no staging registers) into XOR-swizzled, unpadded layouts that
-//    keep the fragment reads free of bank conflicts. K runs one tile ahead of
-//    V: while the softmax of tile i runs on the vector ALUs, the S MFMAs of
-//    tile i+1 are already queued, so the matrix pipe does not wait for it.
-//    K and V^T are each double-buffered; one barrier per tile.
+//  * Softmax reference: a per-row upper bound of the logits from the query
+//    and key norms, fixed for the whole row, so there is no running maximum
+//    and no rescale of O (rows where that bound is too loose take the exact
+//    row maxima from a first pass over their keys). l and O share the
+//    reference, which cancels in O / l.
+//  * Tiles move global -> LDS with direct loads (16 bytes per lane, no
+//    staging registers) into XOR-swizzled, unpadded layouts that keep the
+//    fragment reads free of bank conflicts. Each 64-key tile runs as two
+//    32-key half-steps; the S MFMAs of the next half overlap the softmax and
+//    PV of this one, in a software pipeline of 4-MFMA groups. K sits in four
+//    32-key slots and V^T in two tile buffers; one barrier per tile.
 //  * Split-KV: when (rows x heads) give too few workgroups to fill the chip,
 //    the key range of each query tile is cut into chunks handled by separate
 //    workgroups; a query tile with several chunks writes normalised partial
@@ -42,7 +43,6 @@ namespace {
 constexpr int kBN = 64;       // keys per tile
 constexpr int kThreads = 256; // 4 waves
 constexpr int kRowsPerWave = 32;
-constexpr float kRescaleSlack = 8.f;  // log2 units
 
 template <int D> struct AttnCfg {
   static constexpr int kKRowBytes = 2 * D;            // one key row of K
@@ -124,18 +124,13 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
   return g;
 }
 
-// kFixed: the fixed-reference kernel. A workgroup whose rows fail the bound
-// below records that in fallback[workgroup] and exits; the running-max
-// instantiation (kFixed = false), launched next, runs only those workgroups.
-// Two kernels keep the rare path's registers out of the common one.
-template <int D, bool kFixed>
+template <int D>
 __global__ void __launch_bounds__(kThreads)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
                     const bf16 *__restrict__ gamma_k, bf16 *__restrict__ o,
-                    bf16 *__restrict__ part_o, float *__restrict__ part_ml,
-                    int32_t *__restrict__ fallback, AttnArgs a, int gp, int n_qtiles, int n_hgrp,
-                    int n_split, int chunk_keys, int force_running_max) {
+                    bf16 *__restrict__ part_o, float *__restrict__ part_ml, AttnArgs a, int gp,
+                    int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int force_exact_max) {
   using Cfg = AttnCfg<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -147,7 +142,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int split = bid % n_split;
   const Geo geo = geometry(a, kv_len, bid / n_split, gp, n_qtiles, n_hgrp, chunk_keys);
   if (split >= geo.n_active) return;  // uniform per block
-  if (!kFixed && fallback[blockIdx.x] == 0) return;  // done by the fixed-reference kernel
   const int b = geo.b, kh = geo.kh;
 
   const int wpg = 4 / gp;  // waves per query head
@@ -176,7 +170,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   f32x16 acc_o[Cfg::kDB];
 #pragma unroll
   for (int i = 0; i < Cfg::kDB; ++i) acc_o[i] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.f;
+  float l_run = 0.f;
 
   const char *kbase = (const char *)(k + ((size_t)b * a.Hk + kh) * a.T_pad * D);
   const char *vbase = (const char *)(vt + ((size_t)b * a.Hk + kh) * D * a.T_pad);
@@ -220,14 +214,21 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                lds0 + 4 * Cfg::kKHalfBytes + buf * Cfg::kVTileBytes + (wu + 4 * i) * 1024);
   };
 
-  if (n_tiles > 0) {  // K halves 0, 1, 2 (slots 0-2) and V tile 0
+  // max_c |1 + gamma_k[c]| (bounds the key norms, below); its loads overlap
+  // the first tile loads
+  float gmax = 0.f;
+  for (int c = tid; c < D; c += kThreads) gmax = fmaxf(gmax, fabsf(1.f + (float)gamma_k[c]));
+
+  auto issue_prologue = [&]() {  // K halves 0, 1, 2 (slots 0-2) and V tile 0
+    if (n_tiles <= 0) return;
 #pragma unroll
     for (int h = 0; h < 3; ++h)
 #pragma unroll
       for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(h >> 1, h & 1, h, i);
 #pragma unroll
     for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(0, 0, i);
-  }
+  };
+  issue_prologue();
   // Every outstanding load (Q fragments, first tiles) lands before the loop,
   // so inside it only the newest prefetches are ever pending.
   publish_tiles();
@@ -260,13 +261,12 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // Fixed softmax reference. |logit| <= |q_t| |k_s| (Cauchy-Schwarz) and a
   // key after RMSNorm has |k| <= sqrt(d_h) max_c |1 + gamma_k[c]|, so
   // U_t = |q_t| sqrt(d_h) max|1 + gamma_k| bounds every logit of row t:
-  // p = exp2((x - U_t) log2 e) <= 1 never overflows and the running max and
-  // its rescale of O disappear. While 2 U_t log2 e <= 100 the row's largest p
-  // is >= 2^-100, far from underflow; otherwise the workgroup takes the
-  // running-max path below.
+  // p = exp2((x - U_t) log2 e) <= 1 never overflows and there is no running
+  // max or rescale of O. While 2 U_t log2 e <= 100 the row's largest p is
+  // >= 2^-100, far from underflow; otherwise the workgroup first takes the
+  // exact row maxima in a pass over its key tiles and uses those instead.
+  // Either way O and l share the reference, which cancels in O / l.
   __shared__ float red4[4];
-  float gmax = 0.f;
-  for (int c = tid; c < D; c += kThreads) gmax = fmaxf(gmax, fabsf(1.f + (float)gamma_k[c]));
   gmax = wave_max(gmax);
   if (lane == 0) red4[w] = gmax;
   __syncthreads();
@@ -281,7 +281,36 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   qq += __shfl_xor(qq, 32, kWave);
   // 1% margin covers the bf16 rounding of the stored keys
-  const float m_fixed = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f * kLog2e;
+  float m_ref = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f * kLog2e;
+
+  // Blocked logits of a 32-key half starting at key s0 become -inf. Allowed
+  // keys of this lane's row form one interval; relative to the lane's first
+  // key s0 + 8 hh, element e sits at the compile-time offset
+  // 16 (g >> 1) + 4 (g & 1) + r, so one unsigned compare per element tests
+  // lo <= offset <= hi.
+  auto mask_half = [&](f32x16 &sv, int s0) {
+    const int base = s0 + 8 * hh;
+    int hi = min(my_t, len - 1) - base;
+    int lo = (a.local ? my_t - a.window + 1 : -(1 << 30)) - base;
+    if (hi < lo) {  // nothing allowed
+      lo = 1 << 30;
+      hi = lo;
+    }
+    const uint32_t span = (uint32_t)(hi - lo);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int g = e >> 2, r = e & 3;
+      const int off = 16 * (g >> 1) + 4 * (g & 1) + r;
+      sv[e] = (uint32_t)(off - lo) <= span ? sv[e] : -INFINITY;
+    }
+  };
+  auto qk_half = [&](int slot) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < Cfg::kKS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(slot, ks), qf[ks], acc, 0, 0, 0);
+    return acc;
+  };
 
   // One half-step u = 2 it + kb handles keys s0 + 32 kb .. +31 of tile it
   // (K half u). While its softmax and PV run, the S of half u + 1 goes to the
@@ -307,30 +336,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     constexpr int kPG = Cfg::kDB / 2;                      // PV groups (2 db x 2 kk)
     const int s0 = my_begin + it * kBN + 32 * kb;
 
-    if (kMasked) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int g = e >> 2, r = e & 3;
-        const int s = s0 + 16 * (g >> 1) + 8 * hh + 4 * (g & 1) + r;
-        const bool ok = s <= my_t && s < len && (!a.local || s > my_t - a.window);
-        s_cur[e] = ok ? s_cur[e] : -INFINITY;
-      }
-    }
-    if (!kFixed) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * kLog2e;
-      const bool need = mx > m_ref + kRescaleSlack;
-      if (__ballot(need)) {  // raise the reference (rare after the first tiles)
-        const float m_new = need ? mx : m_ref;
-        const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= corr;
-#pragma unroll
-        for (int db = 0; db < Cfg::kDB; ++db) acc_o[db] *= corr;
-      }
-    }
+    if (kMasked) mask_half(s_cur, s0);
     const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
 
     // S phase: S of half u + 1 on the matrix pipe, this half's weights on the
@@ -441,7 +447,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     using F_ = std::false_type;
     using K0 = std::integral_constant<int, 0>;
     using K1 = std::integral_constant<int, 1>;
-    if (kFixed) m_ref = m_fixed;
     f32x16 s_b;
     using PR = std::integral_constant<int, -1>;
     using P0 = std::integral_constant<int, 0>;
@@ -472,18 +477,34 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (it < full_end) full_tile(P0{}, it++);
     for (; it < n_tiles; ++it) masked_tile(it);
   };
-  // S of K half 0, formed before the barrier that precedes any write to its slot
+  // S of K half 0; the barrier after it orders these reads before any later
+  // write to slot 0
   f32x16 s0_first = f32x16{};
-  if (n_tiles > 0) {
+  if (n_tiles > 0) s0_first = qk_half(0);
+  if (!__syncthreads_and(2.f * m_ref <= 100.f) || force_exact_max) {
+    // Exact row maxima (log2 units) over the allowed keys: each tile's two K
+    // halves go to slots 0 and 1, S MFMAs only. Rare; kept simple.
+    float mx = -INFINITY;
+    for (int it = 0; it < n_tiles; ++it) {
 #pragma unroll
-    for (int ks = 0; ks < Cfg::kKS; ++ks)
-      s0_first = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, ks), qf[ks], s0_first, 0, 0, 0);
-  }
-  if constexpr (kFixed) {
-    // every load this workgroup issued has landed (publish_tiles above)
-    const bool fixed_ok = __syncthreads_and(2.f * m_fixed <= 100.f) && !force_running_max;
-    if (tid == 0) fallback[blockIdx.x] = fixed_ok ? 0 : 1;
-    if (!fixed_ok) return;
+      for (int kbh = 0; kbh < 2; ++kbh)
+#pragma unroll
+        for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(it, kbh, kbh, i);
+      publish_tiles();
+#pragma unroll
+      for (int kbh = 0; kbh < 2; ++kbh) {
+        f32x16 sv = qk_half(kbh);
+        mask_half(sv, my_begin + it * kBN + 32 * kbh);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+      }
+      __syncthreads();  // reads done before the next tile overwrites the slots
+    }
+    m_ref = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * kLog2e;
+    issue_prologue();
+    publish_tiles();
+    if (n_tiles > 0) s0_first = qk_half(0);
+    __syncthreads();
   }
   run(s0_first);
 
@@ -608,25 +629,16 @@ Plan plan(const AttnArgs &a) {
 
 template <int D>
 hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
-                    const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, int32_t *fallback,
-                    const AttnArgs &a, int force, hipStream_t s) {
+                    const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
+                    int force, hipStream_t s) {
   using Cfg = AttnCfg<D>;
   const Plan p = plan(a);
-  const dim3 grid((unsigned)(p.n_base * p.n_split));
-  hipError_t e = hipFuncSetAttribute((const void *)flash_attn_fwd_bf16<D, true>,
+  hipError_t e = hipFuncSetAttribute((const void *)flash_attn_fwd_bf16<D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void *)flash_attn_fwd_bf16<D, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((flash_attn_fwd_bf16<D, true>), grid, dim3(kThreads), Cfg::kLdsBytes, s, q, k,
-                     vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, p.gp, p.n_qtiles,
-                     p.n_hgrp, p.n_split, p.chunk_keys, force);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((flash_attn_fwd_bf16<D, false>), grid, dim3(kThreads), Cfg::kLdsBytes, s, q,
-                     k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, p.gp, p.n_qtiles,
-                     p.n_hgrp, p.n_split, p.chunk_keys, force);
+  hipLaunchKernelGGL(flash_attn_fwd_bf16<D>, dim3((unsigned)(p.n_base * p.n_split)),
+                     dim3(kThreads), Cfg::kLdsBytes, s, q, k, vt, kv_len, gamma_k, o, part_o,
+                     part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys, force);
   e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const long rows = (long)a.B * a.H * a.T;
@@ -637,30 +649,24 @@ hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t 
 
 }  // namespace
 
-// Layout: split partial outputs [n_split][B][H][T][d_h] bf16 and their
-// (m, l) pairs (only when the key range is split), then one fallback flag
-// per attention workgroup.
 size_t flash_attn_partial_bytes(const AttnArgs &a) {
   const Plan p = plan(a);
-  const size_t flags = (size_t)p.n_base * p.n_split * sizeof(int32_t);
-  if (p.n_split == 1) return flags;
-  return (size_t)p.n_split * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8) + flags;
+  if (p.n_split == 1) return 0;
+  return (size_t)p.n_split * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8);
 }
 
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
                                   const int32_t *kv_len, const bf16 *gamma_k, bf16 *o,
-                                  void *partial, const AttnArgs &a, bool force_running_max,
+                                  void *partial, const AttnArgs &a, bool force_exact_max,
                                   hipStream_t s) {
-  const int force = force_running_max ? 1 : 0;
-  const Plan p = plan(a);
-  const size_t rows = p.n_split == 1 ? 0 : (size_t)p.n_split * a.B * a.H * a.T;
+  const int force = force_exact_max ? 1 : 0;
+  const size_t rows = (size_t)plan(a).n_split * a.B * a.H * a.T;
   bf16 *part_o = (bf16 *)partial;
-  float *part_ml = (float *)((char *)partial + rows * a.d_h * 2);
-  int32_t *fallback = (int32_t *)((char *)part_ml + rows * 8);
+  float *part_ml = partial ? (float *)((char *)partial + rows * a.d_h * 2) : nullptr;
   switch (a.d_h) {
-    case 64: return launch_d<64>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, force, s);
-    case 128: return launch_d<128>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, force, s);
-    case 256: return launch_d<256>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, fallback, a, force, s);
+    case 64: return launch_d<64>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, force, s);
+    case 128: return launch_d<128>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, force, s);
+    case 256: return launch_d<256>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, force, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -44,14 +44,15 @@ struct AttnArgs {
   int B, T, H, Hk, d_h, T_pad;
   int local, window;
 };
-// `partial` (flash_attn_partial_bytes(a) bytes, never 0) holds the split-KV
-// partial outputs and one fallback flag per attention workgroup.
+// `partial` (flash_attn_partial_bytes(a) bytes, may be NULL when that is 0)
+// holds the split-KV partial outputs.
 size_t flash_attn_partial_bytes(const AttnArgs &a);
 // gamma_k [d_h] bounds the key norms (fixed softmax reference).
-// force_running_max: every workgroup takes the running-max softmax.
+// force_exact_max: every workgroup takes the exact-row-maximum pass that
+// normally runs only where the logit bound is too loose.
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
                                   const int32_t *kv_len, const bf16 *gamma_k, bf16 *o,
-                                  void *partial, const AttnArgs &a, bool force_running_max,
+                                  void *partial, const AttnArgs &a, bool force_exact_max,
                                   hipStream_t s);
 
 // K4 + K4c (decode attention): split-KV partials then combine into o [B, H*d_h].

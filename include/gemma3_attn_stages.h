@@ -24,11 +24,12 @@ extern "C" {
 #define GEMMA3_STAGE_ATTN 0x4u      /* masked grouped softmax attention -> o                  */
 #define GEMMA3_STAGE_OUT_PROJ 0x8u  /* y = o W_o^T (attn_vec_einsum)                          */
 #define GEMMA3_STAGE_ALL 0xFu
-/* Diagnostic option of the attention stage: every workgroup takes the
- * running-max softmax (the path normally used only when the logit bound
- * |q_t| sqrt(d_h) max|1 + gamma_k| is too large for a fixed reference), so
- * tests can check that path on ordinary inputs. Same results up to rounding. */
-#define GEMMA3_STAGE_FORCE_RUNNING_MAX 0x10u
+/* Diagnostic option of the attention stage: every workgroup takes its
+ * softmax reference from an exact pass over the row maxima (the path normally
+ * used only when the logit bound |q_t| sqrt(d_h) max|1 + gamma_k| is too
+ * large for a fixed reference), so tests can check that path on ordinary
+ * inputs. Same results up to rounding. */
+#define GEMMA3_STAGE_FORCE_EXACT_MAX 0x10u
 
 /* Decode stages ("Gemma 3 Attention Block", How it works, Cache). */
 #define GEMMA3_DSTAGE_QKV_PROJ 0x1u /* split-K projections of the B new tokens               */
@@ -47,7 +48,6 @@ extern "C" {
  *   vt   [B, H_kv, d_h, T_pad]    V transposed (columns T..T_pad-1 zero)
  *   attn_part                     split-KV partial outputs of the attention stage
  *                                 (only when the grid is too small to fill the GPU)
- *                                 and one softmax-path flag per attention workgroup
  *   T_pad = T rounded up to a multiple of 64.
  * Decode (S > 0):
  *   qkv  fp32 [ksplit_qkv, B, (H + 2 H_kv) d_h]  split-K partial projections

@@ -64,42 +64,43 @@ def test_prefill_fp32_small(gpu_lib, case):
     assert_f32_close(f64(y), oracle_prefill(inp, kw), "y")
 
 
-# The running-max softmax kernel (taken by workgroups whose logit bound
-# |q_t| sqrt(d_h) max|1 + gamma_k| is too large for a fixed reference) on
-# ordinary inputs, forced for every workgroup: masked and full tiles, padding,
-# local windows and a split key range whose merged partials come from it.
-RUNNING_MAX = [
+# The exact-row-maximum pass (taken by workgroups whose logit bound
+# |q_t| sqrt(d_h) max|1 + gamma_k| is too large for a fixed softmax reference)
+# on ordinary inputs, forced for every workgroup: masked and full tiles,
+# padding, local windows and split key ranges merged afterwards.
+EXACT_MAX = [
     (1, 300, 512, 4, 2, 128, G, 0, None),
     (2, 200, 512, 2, 1, 256, L, 70, (200, 150)),
     (1, 333, 256, 4, 1, 64, G, 0, None),
     (1, 1000, 512, 4, 1, 128, L, 600, (900,)),
     (1, 1500, 256, 2, 1, 64, G, 0, None),
+    (3, 64, 1024, 4, 4, 256, G, 0, (64, 1, 33)),
 ]
 
 
-@pytest.mark.parametrize("case", RUNNING_MAX, ids=[str(c[:8]) for c in RUNNING_MAX])
-def test_prefill_bf16_running_max_kernel(gpu_lib, case):
+@pytest.mark.parametrize("case", EXACT_MAX, ids=[str(c[:8]) for c in EXACT_MAX])
+def test_prefill_bf16_exact_max_pass(gpu_lib, case):
     B, T, D, H, Hk, d_h, t, Wn, lens = case
     log(f"case {case}")
     inp = small_prefill_inputs(8, B, T, D, H, Hk, d_h, "bf16", lens)
     kw = _kw(H, Hk, d_h, t, Wn)
-    y = gpu_prefill(gpu_lib, inp, kw, stages=gpu_lib.STAGE_ALL | gpu_lib.STAGE_FORCE_RUNNING_MAX)
+    y = gpu_prefill(gpu_lib, inp, kw, stages=gpu_lib.STAGE_ALL | gpu_lib.STAGE_FORCE_EXACT_MAX)
     assert_bf16_close(f64(y), oracle_prefill(inp, kw), "y")
 
 
 @pytest.mark.parametrize("d_h", [64, 128, 256])
-def test_large_logits_take_running_max_kernel(gpu_lib, d_h):
+def test_large_logits_take_exact_max_pass(gpu_lib, d_h):
     """alpha = 1 puts every row's logit bound beyond the fixed-reference range:
-    every workgroup then takes the running-max kernel on its own, bit for bit
+    every workgroup then takes the exact-maximum pass on its own, bit for bit
     what forcing it gives. (Against the fp64 oracle such logits are limited by
     the bf16 storage of q and k, not by the softmax.)"""
     B, T, D, H, Hk = 1, 260, 512, 4, 2
     inp = small_prefill_inputs(9, B, T, D, H, Hk, d_h, "bf16")
     kw = _kw(H, Hk, d_h, L, 90, alpha=1.0)
     y_nat = gpu_prefill(gpu_lib, inp, kw)
-    y_frc = gpu_prefill(gpu_lib, inp, kw, stages=gpu_lib.STAGE_ALL | gpu_lib.STAGE_FORCE_RUNNING_MAX)
+    y_frc = gpu_prefill(gpu_lib, inp, kw, stages=gpu_lib.STAGE_ALL | gpu_lib.STAGE_FORCE_EXACT_MAX)
     assert torch.equal(y_nat, y_frc)
-    y_fix = gpu_prefill(gpu_lib, inp, _kw(H, Hk, d_h, L, 90))  # ordinary scale: fixed kernel
+    y_fix = gpu_prefill(gpu_lib, inp, _kw(H, Hk, d_h, L, 90))  # ordinary scale: fixed reference
     assert not torch.equal(y_fix, y_nat)
 
 
