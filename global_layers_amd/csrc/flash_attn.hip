@@ -130,15 +130,17 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
                     const bf16 *__restrict__ gamma_k, bf16 *__restrict__ o,
                     bf16 *__restrict__ part_o, float *__restrict__ part_ml, AttnArgs a, int gp,
-                    int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int force_exact_max) {
+                    int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int remap,
+                    int force_exact_max) {
   using Cfg = AttnCfg<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.H / a.Hk;
   // Logical order: (b, kh, head group) runs of query tiles (longest first),
-  // the key chunks of one query tile adjacent; runs stay on one XCD.
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // the key chunks of one query tile adjacent; with `remap`, runs stay on one
+  // XCD.
+  const int bid = remap ? xcd_remap(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int split = bid % n_split;
   const Geo geo = geometry(a, kv_len, bid / n_split, gp, n_qtiles, n_hgrp, chunk_keys);
   if (split >= geo.n_active) return;  // uniform per block
@@ -591,9 +593,15 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
 }
 
 struct Plan {
-  int gp, n_qtiles, n_hgrp, n_split, chunk_keys;
+  int gp, n_qtiles, n_hgrp, n_split, chunk_keys, remap;
   long n_base;
 };
+
+// Planning constants (units: one 64-key tile of one workgroup, about 1.8 us
+// on the 1B shape). A workgroup's prologue (Q, first K/V tiles, reference)
+// costs about 2.5 tiles; merging split rows afterwards about 8.
+constexpr double kPrologueTiles = 2.5, kMergeTiles = 8.0;
+constexpr int kCUs = 256;  // MI355X compute units; one 131 KB-LDS workgroup each
 
 Plan plan(const AttnArgs &a) {
   Plan p;
@@ -602,25 +610,38 @@ Plan plan(const AttnArgs &a) {
   const int TQ = kRowsPerWave * (4 / p.gp);
   p.n_qtiles = div_up_h(a.T, TQ);
   p.n_hgrp = G / p.gp;
-  p.n_base = (long)a.B * a.Hk * p.n_hgrp * p.n_qtiles;
-  // Split only when one query tile's key range is much longer than the
-  // average per-CU load (one 131 KB-LDS workgroup per CU): the critical path
-  // then sits in a few long workgroups. Chunks cost a per-workgroup prologue
-  // and a merge, so aim at about twice the average load per chunk
-  // (measured on the 1B shape: local layer best unsplit, global best 2-way).
-  const int TQ2 = kRowsPerWave * (4 / p.gp);
-  const int max_keys = a.local ? min(a.T, TQ2 + a.window - 1) : a.T;
-  const int max_tiles = div_up_h(max_keys, kBN) + 1;
-  // key tiles over all query tiles of one (b, kh, head group), closed form
-  const double total_tiles =
-      a.local ? p.n_qtiles * (max_keys / (double)kBN + 1.0)
-              : p.n_qtiles * ((a.T + TQ2) / 2.0 / kBN + 1.0);
-  const double avg = total_tiles * (double)(p.n_base / p.n_qtiles) / 256.0;
+  const long n_groups = (long)a.B * a.Hk * p.n_hgrp;
+  p.n_base = n_groups * p.n_qtiles;
+  // XCD-contiguous order when whole (b, kh, head group) runs divide evenly
+  // among the 8 XCDs (each L2 then holds the K/V its CUs share); otherwise
+  // the plain order, which deals neighbouring query tiles to different XCDs
+  // and keeps their loads balanced.
+  p.remap = n_groups % 8 == 0;
+  // Key tiles of query tile qt (data-independent: padding is ignored here).
+  auto tiles_of = [&](int qt) {
+    const int t_lo = qt * TQ, t_hi = min(a.T, t_lo + TQ);
+    const int kv_begin = a.local ? max(0, t_lo - a.window + 1) : 0;
+    return div_up_h(t_hi - (kv_begin / kBN) * kBN, kBN);
+  };
+  int max_tiles = 0;
+  for (int qt = 0; qt < p.n_qtiles; ++qt) max_tiles = max(max_tiles, tiles_of(qt));
+  // Split key ranges only when the query tiles alone leave CUs idle: pick
+  // the chunk count minimising rounds x (chunk + prologue) (+ merge), where
+  // a round is kCUs concurrent workgroups of similar length.
   p.n_split = 1;
-  if (max_tiles > 3.0 * avg && avg > 0) {
-    p.n_split = (int)((max_tiles + 2 * avg - 1) / (2 * avg));
-    if (p.n_split > 8) p.n_split = 8;  // flash_combine merges at most 8 chunks
-    if (p.n_split < 1) p.n_split = 1;
+  if (p.n_base < kCUs) {
+    double best = max_tiles + kPrologueTiles;
+    for (int ns = 2; ns <= 8; ++ns) {  // flash_combine merges at most 8 chunks
+      const int c = div_up_h(max_tiles, ns);
+      long active = 0;
+      for (int qt = 0; qt < p.n_qtiles; ++qt) active += div_up_h(tiles_of(qt), c);
+      active *= n_groups;
+      const double cost = div_up_h(active, kCUs) * (c + kPrologueTiles) + kMergeTiles;
+      if (cost < best) {
+        best = cost;
+        p.n_split = ns;
+      }
+    }
   }
   // one chunk covers every key range when there is no split
   p.chunk_keys = p.n_split == 1 ? a.T + kBN : div_up_h(max_tiles, p.n_split) * kBN;
@@ -638,7 +659,8 @@ hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(flash_attn_fwd_bf16<D>, dim3((unsigned)(p.n_base * p.n_split)),
                      dim3(kThreads), Cfg::kLdsBytes, s, q, k, vt, kv_len, gamma_k, o, part_o,
-                     part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys, force);
+                     part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys, p.remap,
+                     force);
   e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const long rows = (long)a.B * a.H * a.T;
