@@ -133,7 +133,19 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
   const int M = d->B * d->T, Nq = d->H * d->d_h, Nkv = 2 * d->H_kv * d->d_h;
   const bool bf = d->dtype == GEMMA3_BF16;
 
-  if (stages & GEMMA3_STAGE_QKV_PROJ) {
+  // Both stages in one kernel when every projection tile holds whole Q, K or
+  // V heads: the QK-norm / RoPE / V transpose run in the GEMM's epilogue and
+  // the raw projections never reach memory.
+  const bool fused = bf && (stages & GEMMA3_STAGE_QKV_PROJ) && (stages & GEMMA3_STAGE_QK_NORM) &&
+                     Nq % 256 == 0 && (d->H_kv * d->d_h) % 256 == 0;
+  if (fused) {
+    QkvEpilogue ep{pos, (const bf16 *)w->gamma_q, (const bf16 *)w->gamma_k,
+                   (bf16 *)q, (bf16 *)k, (bf16 *)vt, d->T, L.T_pad, d->H, d->H_kv, d->d_h,
+                   d->query_scale, (double)d->rope_theta, (double)d->rope_scale};
+    RUN(launch_gemm_qkv_fused((const bf16 *)x, (const bf16 *)w->w_q, (const bf16 *)w->w_kv, Nq,
+                              M, Nq + Nkv, d->D, ep, s));
+  }
+  if ((stages & GEMMA3_STAGE_QKV_PROJ) && !fused) {
     if (bf)
       RUN(launch_gemm_bf16_nt((const bf16 *)x, (const bf16 *)w->w_q, (const bf16 *)w->w_kv, Nq,
                               (bf16 *)qkv, M, Nq + Nkv, d->D, s));
@@ -141,7 +153,7 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
       RUN(launch_gemm_f32_nt((const float *)x, (const float *)w->w_q, (const float *)w->w_kv, Nq,
                              (float *)qkv, M, Nq + Nkv, d->D, s));
   }
-  if (stages & GEMMA3_STAGE_QK_NORM) {
+  if ((stages & GEMMA3_STAGE_QK_NORM) && !fused) {
     NormRopeArgs a{d->B, d->T, d->H, d->H_kv, d->d_h, L.T_pad,
                    d->rope_theta, d->rope_scale, d->query_scale};
     RUN(launch_qk_norm_rope<T>(qkv, pos, (const T *)w->gamma_q, (const T *)w->gamma_k, q, k, vt,

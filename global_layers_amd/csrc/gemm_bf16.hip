@@ -60,10 +60,163 @@ template <int kChunks> DEVI int gemm_swz(int r) {
   return kChunks == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST>
+// Row pitch (bytes) of the bf16 C tile staged in LDS by the fused epilogue:
+// an 8-byte pad per row spreads a column of 8-byte writes over all banks.
+template <int BN> constexpr int qkv_tile_pitch() { return BN * 2 + 8; }
+
+// Fused epilogue of the QKV projection ("QK-Norm", How it works; "Gemma 3
+// Attention Block", How it works): the BM x 256 tile, rounded to bf16 as the
+// projection output would be, is staged in LDS. A tile is all Q, all K or all
+// V columns (the caller checks that H d_h and H_kv d_h are multiples of 256).
+// Q and K head vectors are divided by sqrt(mean(v^2) + 1e-6), multiplied by
+// (1 + gamma) (and alpha for Q), rotated by RoPE and written to q / k; V is
+// written transposed to vt. The tile holding a batch row's last token also
+// zeroes that row's K rows and V^T columns T .. T_pad - 1.
+//
+// RoPE angle of pair i at position p: (p / scale) theta^(-2i/d_h) radians,
+// i.e. p f_i revolutions with f_i = theta^(-2i/d_h) / (2 pi scale). The
+// product is reduced modulo 1 in fp64 (positions reach 131071), and the
+// reduced angle goes to the hardware sine and cosine, which take revolutions.
+template <int BM, int BN, int WM, int WN, int kFM, int kFN>
+DEVI void qkv_epilogue_impl(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, int n0, int M,
+                            const QkvEpilogue &ep) {
+  constexpr int kThreads = WM * WN * kWave;
+  constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
+  constexpr int kPitch = qkv_tile_pitch<BN>();
+  static_assert(BN == 256, "one tile row = 256 columns");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lrow = lane & 31, hh = lane >> 5;
+
+  __syncthreads();  // every wave is done with the k-loop stages
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = wm * kWaveM + i * 32 + lrow;
+        const int c = wn * kWaveN + j * 32 + 8 * g + 4 * hh;
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][g * 4 + r];
+        *reinterpret_cast<bf16x4 *>(lds + row * kPitch + c * 2) = v;
+      }
+  __syncthreads();
+
+  const int d_h = ep.d_h, half = d_h / 2;
+  const int head0 = n0 / d_h;  // global head index of tile column 0
+  const int T = ep.T, T_pad = ep.T_pad;
+  const int kind = head0 < ep.H ? 0 : head0 < ep.H + ep.Hk ? 1 : 2;  // Q, K, V (tile-uniform)
+
+  if (kind < 2) {
+    // 16 lanes per row: lane16 / lpv picks the head inside the tile, each lane
+    // holds channel pairs (i0 + x, half + i0 + x), x < 8.
+    const int lpv = d_h / 16;
+    const int lane16 = lane & 15, hv = lane16 / lpv, i0 = 8 * (lane16 % lpv);
+    const bf16 *gam = kind == 0 ? ep.gamma_q : ep.gamma_k;
+    const float mul = kind == 0 ? ep.alpha : 1.f;
+    float g1[8], g2[8];
+    double f[8];
+    const double l2t = log2(ep.theta), rev_scale = 1.0 / (6.283185307179586476925286766559 * ep.scale);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      g1[x] = (1.f + (float)gam[i0 + x]) * mul;
+      g2[x] = (1.f + (float)gam[half + i0 + x]) * mul;
+      f[x] = exp2(-2.0 * (double)(i0 + x) / (double)d_h * l2t) * rev_scale;
+    }
+    const int head = head0 + hv;
+    constexpr int kRowsPerPass = kThreads / 16;
+    for (int row = tid / 16; row < BM; row += kRowsPerPass) {
+      const int m = m0 + row;
+      const bool ok = m < M;  // uniform within the row's 16 lanes
+      const char *src = lds + row * kPitch + (hv * d_h + i0) * 2;
+      const bf16x8 u = *reinterpret_cast<const bf16x8 *>(src);
+      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(src + half * 2);
+      float x1[8], x2[8], ss = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        x1[x] = (float)u[x];
+        x2[x] = (float)v[x];
+        ss += x1[x] * x1[x] + x2[x] * x2[x];
+      }
+      for (int o = lpv / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+      if (!ok) continue;
+      const float r = rsqrtf(ss / (float)d_h + 1e-6f);
+      const int b = m / T, t = m - b * T;
+      const double p = (double)ep.pos[m];
+      bf16x8 o1, o2;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        double rev = p * f[x];
+        rev -= rint(rev);
+        const float cs = __builtin_amdgcn_cosf((float)rev), sn = __builtin_amdgcn_sinf((float)rev);
+        const float y1 = x1[x] * r * g1[x], y2 = x2[x] * r * g2[x];
+        o1[x] = (bf16)(y1 * cs - y2 * sn);
+        o2[x] = (bf16)(y2 * cs + y1 * sn);
+      }
+      bf16 *dst = kind == 0 ? ep.q + (((size_t)b * ep.H + head) * T + t) * d_h + i0
+                            : ep.k + (((size_t)b * ep.Hk + (head - ep.H)) * T_pad + t) * d_h + i0;
+      st16(dst, __builtin_bit_cast(u32x4, o1));
+      st16(dst + half, __builtin_bit_cast(u32x4, o2));
+    }
+  } else {
+    // V^T: one lane per (tile column, 8 consecutive rows); 16-byte stores when
+    // the 8 tokens sit in one batch row at an 8-aligned position.
+    for (int item = tid; item < BN * (BM / 8); item += kThreads) {
+      const int c = item % BN, rg = item / BN;
+      const int row = rg * 8, m = m0 + row;
+      if (m >= M) continue;
+      const int head = head0 + c / d_h, ch = c % d_h, kh = head - ep.H - ep.Hk;
+      bf16x8 v;
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        v[x] = *reinterpret_cast<const bf16 *>(lds + (row + x) * kPitch + c * 2);
+      const int b = m / T, t = m - b * T;
+      bf16 *dst = ep.vt + (((size_t)b * ep.Hk + kh) * d_h + ch) * T_pad;
+      if (m + 7 < M && t + 7 < T && (t & 7) == 0) {
+        st16(dst + t, __builtin_bit_cast(u32x4, v));
+      } else {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int mx = m + x;
+          if (mx >= M) break;
+          const int bx = mx / T, tx = mx - bx * T;
+          ep.vt[(((size_t)bx * ep.Hk + kh) * d_h + ch) * T_pad + tx] = v[x];
+        }
+      }
+    }
+  }
+
+  // Zero the padding rows (K) / columns (V^T) T .. T_pad-1 of every batch row
+  // whose last token falls in this tile.
+  if (kind > 0 && T_pad > T) {
+    const int pad = T_pad - T;
+    const int m_hi = min(m0 + BM, M);
+    for (int b = m0 / T; b * T + T - 1 < m_hi; ++b) {
+      if (b * T + T - 1 < m0) continue;
+      for (int e = tid; e < pad * BN; e += kThreads) {
+        const int c = e % BN, tp = T + e / BN;
+        const int head = head0 + c / d_h, ch = c % d_h;
+        if (kind == 1)
+          ep.k[(((size_t)b * ep.Hk + (head - ep.H)) * T_pad + tp) * d_h + ch] = (bf16)0.f;
+        else
+          ep.vt[(((size_t)b * ep.Hk + (head - ep.H - ep.Hk)) * d_h + ch) * T_pad + tp] = (bf16)0.f;
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int kFM, int kFN>
+DEVI void qkv_epilogue(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, int n0, int M,
+                       const QkvEpilogue &ep) {
+  qkv_epilogue_impl<BM, BN, WM, WN, kFM, kFN>(acc, lds, m0, n0, M, ep);
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NST, bool kQkv>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16 *__restrict__ B1,
-             int N0, bf16 *__restrict__ C, int M, int N, int K, int n_tiles_n) {
+             int N0, bf16 *__restrict__ C, int M, int N, int K, int n_tiles_n, QkvEpilogue ep) {
   using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -164,6 +317,10 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
     if (kt + 1 < nk) wait_tile(kt + 1);
   }
 
+  if constexpr (kQkv) {
+    qkv_epilogue<BM, BN, WM, WN, Cfg::kFM, Cfg::kFN>(acc, lds, m0, n0, M, ep);
+    return;
+  }
   // acc[i][j] holds D[n][m]: lane column m = lane % 32, rows n = 8g + 4h + r.
 #pragma unroll
   for (int i = 0; i < Cfg::kFM; ++i) {
@@ -189,17 +346,19 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST>
+template <int BM, int BN, int WM, int WN, int BK, int NST, bool kQkv = false>
 hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C, int M,
-                       int N, int K, hipStream_t s) {
+                       int N, int K, hipStream_t s, const QkvEpilogue &ep = QkvEpilogue{}) {
   using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
   const int tm = div_up_h(M, BM), tn = div_up_h(N, BN);
-  auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST>;
+  auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST, kQkv>;
+  constexpr int kTileLds = kQkv ? BM * qkv_tile_pitch<BN>() : 0;
+  constexpr int kLds = Cfg::kLdsBytes > kTileLds ? Cfg::kLdsBytes : kTileLds;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(Cfg::kThreads), Cfg::kLdsBytes, s, A, B0, B1, N0,
-                     C, M, N, K, tn);
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(Cfg::kThreads), kLds, s, A, B0, B1, N0, C, M, N,
+                     K, tn, ep);
   return hipGetLastError();
 }
 
@@ -292,6 +451,19 @@ hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, in
     case 1: return launch_gemm<128, 256, 2, 4, 32, 4>(A, B0, B1, N0, C, M, N, K, s);
     default: return launch_gemm<128, 128, 2, 2, 32, 4>(A, B0, B1, N0, C, M, N, K, s);
   }
+}
+
+hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_kv, int N0, int M,
+                                 int N, int K, const QkvEpilogue &ep, hipStream_t s) {
+  // 256-column tiles (whole heads); 256 or 128 rows by the same rounds x
+  // tile-cost model as the plain projection
+  const long t256 = (long)div_up_h(M, 256) * div_up_h(N, 256);
+  const long t128 = (long)div_up_h(M, 128) * div_up_h(N, 256);
+  const double c256 = (double)div_up_h(t256, 256) * 256 * 256 / 1.0;
+  const double c128 = (double)div_up_h(t128, 256) * 128 * 256 / 0.9;
+  if (c256 <= c128)
+    return launch_gemm<256, 256, 2, 4, 64, 2, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
+  return launch_gemm<128, 256, 2, 4, 32, 4, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
 }
 
 int gemv_ksplit(int N, int K) {

@@ -12,6 +12,21 @@ static inline int div_up_h(long a, long b) { return (int)((a + b - 1) / b); }
 // [0, N0) come from B0 and rows [N0, N) from B1 (W_q and W_kv are separate
 // caller buffers that together form the [Q|K|V] projection).
 // K1: C[M,N] (bf16) = A[M,K] * B[N,K]^T; K % 64 == 0, 16-byte aligned rows.
+// Fused epilogue of the bf16 QKV projection: QK-norm, RoPE and alpha on the Q
+// and K columns, V written transposed (see launch_gemm_qkv_fused).
+struct QkvEpilogue {
+  const int32_t *pos;              // [B, T] (flattened rows m = b T + t)
+  const bf16 *gamma_q, *gamma_k;   // [d_h]
+  bf16 *q, *k, *vt;                // [B,H,T,d_h], [B,Hk,T_pad,d_h], [B,Hk,d_h,T_pad]
+  int T, T_pad, H, Hk, d_h;
+  float alpha;
+  double theta, scale;
+};
+// y = x [w_q; w_kv]^T with the epilogue above instead of a raw store.
+// Requires (H d_h) % 256 == 0 and (H_kv d_h) % 256 == 0.
+hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_kv, int N0, int M,
+                                 int N, int K, const QkvEpilogue &ep, hipStream_t s);
+
 hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C,
                                int M, int N, int K, hipStream_t s);
 // K1d: P[ksplit][M][N] (fp32 partials) = A[M,K] * W[N,K]^T per K split; K % (32 ksplit) == 0.

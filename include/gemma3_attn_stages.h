@@ -42,7 +42,10 @@ extern "C" {
  * Byte offsets of the intermediates inside the workspace (all 256-byte
  * aligned). Element type is desc.dtype unless marked fp32.
  * Prefill (S == 0):
- *   qkv  [B*T, (H + 2 H_kv) d_h]  raw projections; reused for o [B*T, H d_h]
+ *   qkv  [B*T, (H + 2 H_kv) d_h]  raw projections; reused for o [B*T, H d_h].
+ *                                 Not written when QKV_PROJ and QK_NORM run in
+ *                                 one call on bf16 with H d_h and H_kv d_h
+ *                                 multiples of 256 (one fused kernel then)
  *   q    [B, H, T, d_h]           normalised, rotated, times alpha
  *   k    [B, H_kv, T_pad, d_h]    normalised, rotated (rows T..T_pad-1 zero)
  *   vt   [B, H_kv, d_h, T_pad]    V transposed (columns T..T_pad-1 zero)

@@ -140,6 +140,42 @@ def test_intermediates(gpu_lib, dtype):
     assert np.all(f64(it_gpu["k"])[:, :, T:Tp] == 0) and np.all(f64(it_gpu["vt"])[..., T:Tp] == 0)
 
 
+@pytest.mark.parametrize("B,T,H,Hk,d_h", [(3, 77, 2, 1, 256), (2, 200, 8, 2, 128),
+                                           (1, 300, 8, 4, 64)])
+def test_fused_qkv_epilogue_matches_two_kernels(gpu_lib, B, T, H, Hk, d_h):
+    """The projection + QK-norm/RoPE/V-transpose kernel (both stages in one
+    call) against the two-kernel path (stages run separately): V^T bit for bit,
+    padding zero, Q and K within a bf16 rounding step (the fused epilogue takes
+    sin/cos from the hardware units)."""
+    D = 256
+    inp = small_prefill_inputs(10, B, T, D, H, Hk, d_h, "bf16")
+    inp["segment_pos"] = inp["segment_pos"] + torch.tensor([[0], [5000], [131071 - T]][:B],
+                                                           dtype=torch.int32)
+    kw = _kw(H, Hk, d_h, G, 0, theta=1e6, scale=8.0, alpha=0.3)
+    d = to_dev(inp)
+    desc = gpu_lib.make_desc(B=B, T=T, D=D, dtype=d["x"].dtype, **kw)
+    outs = []
+    for stage_list in ([gpu_lib.STAGE_QKV_PROJ | gpu_lib.STAGE_QK_NORM],
+                       [gpu_lib.STAGE_QKV_PROJ, gpu_lib.STAGE_QK_NORM]):
+        ws = gpu_lib.new_workspace(desc)
+        ws.fill_(0xFF)  # NaN bf16 everywhere the kernels do not write
+        for st in stage_list:
+            gpu_lib.prefill(d["x"], d["segment_pos"], weights_of(d), workspace=ws, stages=st, **kw)
+        torch.cuda.synchronize()
+        outs.append({n: t.clone() for n, t in gpu_lib.prefill_intermediates(ws, desc).items()
+                     if n in ("q", "k", "vt")})
+    fz, sp = outs
+    assert torch.equal(fz["vt"], sp["vt"])
+    Tp = fz["k"].shape[2]
+    assert torch.all(fz["k"][:, :, T:Tp] == 0) and torch.all(fz["vt"][..., T:Tp] == 0)
+    for n in ("q", "k"):
+        a, b = fz[n].float(), sp[n].float()
+        assert torch.isfinite(a).all()
+        err = (a - b).abs()
+        assert err.max().item() <= 1e-2 * b.abs().max().item(), (n, err.max().item())
+        assert (err <= 8e-3 * b.abs() + 1e-3).float().mean().item() > 0.999, n
+
+
 def test_cfg2_full_both_layers(gpu_lib):
     w = W.WORKLOADS[2]
     for li, layer in enumerate(w.layers):
