@@ -170,8 +170,10 @@ def main():
     log(f"prefill step {ms_per_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall) "
         f"-> {value:.1f} TFLOP/s ({value / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
 
-    # per-stage kernel times (events on the launch stream, each stage repeated alone)
-    stage_names = {lib.STAGE_QKV_PROJ: "qkv_proj", lib.STAGE_QK_NORM: "qk_norm_rope",
+    # per-stage kernel times (events on the launch stream, each stage repeated
+    # alone). The projection and QK-norm/RoPE run as one stage: on this shape
+    # they are one kernel (norm, RoPE and V transpose in the GEMM epilogue).
+    stage_names = {lib.STAGE_QKV_PROJ | lib.STAGE_QK_NORM: "qkv_proj+qk_norm_rope",
                    lib.STAGE_ATTN: "attention", lib.STAGE_OUT_PROJ: "out_proj"}
     stage_ms = {n: 0.0 for n in stage_names.values()}
     per_layer = []
@@ -193,28 +195,22 @@ def main():
     step()  # leave the workspaces consistent
     torch.cuda.synchronize()
 
-    proj_flops = {"qkv_proj": sum(2 * w.B * w.T * w.D * (w.H + 2 * w.H_kv) * w.d_h
-                                  for _ in layers),
+    proj_flops = {"qkv_proj+qk_norm_rope": sum(2 * w.B * w.T * w.D * (w.H + 2 * w.H_kv) * w.d_h
+                                               for _ in layers),
                   "out_proj": sum(2 * w.B * w.T * w.H * w.d_h * w.D for _ in layers),
                   "attention": sum(L["attn"] for L in layers)}
     dominant = max(stage_ms, key=stage_ms.get)
-    if dominant in proj_flops:
-        ach = proj_flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
-        traffic = (measured_traffic(os.path.join(ROOT, "global_layers_amd", "csrc",
-                                                 "flash_attn.hip"))
-                   if dominant == "attention" else None)
-        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                    "launches_per_step": len(layers),
-                    "flops_per_launch": proj_flops[dominant] // len(layers),
-                    "us_per_launch": round(stage_ms[dominant] * 1e3 / len(layers), 2)}
-    else:  # the norm/RoPE pass is HBM-bound
-        nbytes = sum(w.B * w.T * (w.H + 2 * w.H_kv) * w.d_h * 2 * 2 for _ in layers)
-        ach = nbytes / (stage_ms[dominant] * 1e-3) / 1e9
-        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(ach, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                    "traffic": None}
+    ach = proj_flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
+    traffic = (measured_traffic(os.path.join(ROOT, "global_layers_amd", "csrc", "flash_attn.hip"))
+               if dominant == "attention" else None)
+    roofline = {"kernel": dominant + (" (flash_attn_fwd_bf16 + split merge)"
+                                      if dominant == "attention" else ""),
+                "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "launches_per_step": len(layers),
+                "flops_per_launch": proj_flops[dominant] // len(layers),
+                "us_per_launch": round(stage_ms[dominant] * 1e3 / len(layers), 2)}
     attn_tflops = proj_flops["attention"] / (stage_ms["attention"] * 1e-3) / 1e12
     log(f"  dominant kernel {dominant}: {roofline['achieved']} {roofline['unit']}; "
         f"attention core {attn_tflops:.1f} TFLOP/s")
