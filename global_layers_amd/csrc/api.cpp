@@ -132,6 +132,9 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
   T *q = (T *)(base + L.q), *k = (T *)(base + L.k), *vt = (T *)(base + L.vt);
   const int M = d->B * d->T, Nq = d->H * d->d_h, Nkv = 2 * d->H_kv * d->d_h;
   const bool bf = d->dtype == GEMMA3_BF16;
+  // The bf16 attention kernel takes its logits in base-2 units: its queries
+  // carry alpha log2(e) (one scale folded in before the single bf16 rounding).
+  const float q_scale = bf ? (float)(d->query_scale * 1.4426950408889634) : d->query_scale;
 
   // Both stages in one kernel when every projection tile holds whole Q, K or
   // V heads: the QK-norm / RoPE / V transpose run in the GEMM's epilogue and
@@ -141,7 +144,7 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
   if (fused) {
     QkvEpilogue ep{pos, (const bf16 *)w->gamma_q, (const bf16 *)w->gamma_k,
                    (bf16 *)q, (bf16 *)k, (bf16 *)vt, d->T, L.T_pad, d->H, d->H_kv, d->d_h,
-                   d->query_scale, (double)d->rope_theta, (double)d->rope_scale};
+                   q_scale, (double)d->rope_theta, (double)d->rope_scale};
     RUN(launch_gemm_qkv_fused((const bf16 *)x, (const bf16 *)w->w_q, (const bf16 *)w->w_kv, Nq,
                               M, Nq + Nkv, d->D, ep, s));
   }
@@ -155,7 +158,7 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
   }
   if ((stages & GEMMA3_STAGE_QK_NORM) && !fused) {
     NormRopeArgs a{d->B, d->T, d->H, d->H_kv, d->d_h, L.T_pad,
-                   d->rope_theta, d->rope_scale, d->query_scale};
+                   d->rope_theta, d->rope_scale, q_scale};
     RUN(launch_qk_norm_rope<T>(qkv, pos, (const T *)w->gamma_q, (const T *)w->gamma_k, q, k, vt,
                                a, s));
   }

@@ -34,6 +34,7 @@
 //    outputs with their (m, l), merged by flash_combine.
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -94,11 +95,54 @@ DEVI void publish_tiles() {
   __syncthreads();
 }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), so the body
+// can use its index in constant expressions.
+template <typename F, int... I>
+DEVI void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> DEVI void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Key permutation inside a 32-key block (see the header comment).
 DEVI int kappa(int i) {
   const int g = i >> 3, h = (i >> 2) & 1, r = i & 3;
   return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + r;
 }
+
+// Group schedule of one 64-key tile (see the tile step in the attention
+// kernel): for each 32-key half, kNG groups of 4 S MFMAs then kPG groups of 4
+// PV MFMAs.
+template <int D> struct TileSched {
+  using Cfg = AttnCfg<D>;
+  static constexpr int kG = 4;                   // MFMAs per group
+  static constexpr int kNG = Cfg::kKS / kG;      // S groups per half
+  static constexpr int kPG = Cfg::kDB / 2;       // PV groups per half
+  static constexpr int kNGT = kNG + kPG;         // groups per half
+  static constexpr int kQPG = 4 / kNG;           // weight quads whose exponentials share an S group
+  static constexpr int kPieces = 2 * Cfg::kKHalfLoads + Cfg::kVLoads;  // prefetch loads per tile
+  static constexpr int kPPG = (kPieces + kNGT - 1) / kNGT;             // of them per first-half group
+  // The 16 weights of a half (4 quads of 4) pass three stages: exp2, packing
+  // to bf16 pairs (the PV B operand), and the row sum of the packed values
+  // (l sums the bf16-rounded weights the PV MFMAs use, so numerator and
+  // denominator of O / l carry the same rounding). A quad's stages sit in
+  // successive groups, so no instruction waits on the one just before it and
+  // the in-order issue keeps feeding the matrix pipe: exps of quad q in S
+  // group q / kQPG, its packing one group later, its sum one more. The PV
+  // MFMAs take the first bf16 operand (quads 0, 1) before the second.
+  static constexpr int e_grp(int qd) { return qd / kQPG; }
+  static constexpr int c_grp(int qd) { return kNG > 1 ? qd / kQPG + 1 : 0; }
+  static constexpr int d_grp(int qd) { return (qd / kQPG + 2 < kNGT) ? qd / kQPG + 2 : kNGT - 1; }
+  // VALU instructions of group g: AGPR read + exp per weight, one pack and
+  // one dot per pair
+  static constexpr int valu_of(int g) {
+    int n = 0;
+    for (int qd = 0; qd < 4; ++qd)
+      n += (e_grp(qd) == g ? 8 : 0) + (c_grp(qd) == g ? 2 : 0) + (d_grp(qd) == g ? 2 : 0);
+    return n;
+  }
+};
 
 struct Geo {  // per-workgroup geometry, identical in the attention and combine kernels
   int b, kh, hgrp, qt, t_lo, t_hi, len, kv_begin, kv_end, tile_begin, n_active;
@@ -260,14 +304,16 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                              db * 32 * Cfg::kVRowBytes + voff[kk]);
   };
 
-  // Fixed softmax reference. |logit| <= |q_t| |k_s| (Cauchy-Schwarz) and a
-  // key after RMSNorm has |k| <= sqrt(d_h) max_c |1 + gamma_k[c]|, so
-  // U_t = |q_t| sqrt(d_h) max|1 + gamma_k| bounds every logit of row t:
-  // p = exp2((x - U_t) log2 e) <= 1 never overflows and there is no running
-  // max or rescale of O. While 2 U_t log2 e <= 100 the row's largest p is
-  // >= 2^-100, far from underflow; otherwise the workgroup first takes the
-  // exact row maxima in a pass over its key tiles and uses those instead.
-  // Either way O and l share the reference, which cancels in O / l.
+  // Fixed softmax reference. The queries arrive scaled by log2(e), so a
+  // logit x is already in base-2 units and p = exp2(x - U). |x| <= |q_t| |k_s|
+  // (Cauchy-Schwarz) and a key after RMSNorm has |k| <= sqrt(d_h)
+  // max_c |1 + gamma_k[c]|, so U_t = |q_t| sqrt(d_h) max|1 + gamma_k| bounds
+  // every logit of row t: p <= 1 never overflows and there is no running max
+  // or rescale of O. While 2 U_t <= 100 the row's largest p is >= 2^-100, far
+  // from underflow; otherwise the workgroup first takes the exact row maxima
+  // in a pass over its key tiles and uses those instead. Either way O and l
+  // share the reference, which cancels in O / l. The S accumulators start at
+  // -U_t, so the MFMAs deliver x - U_t directly.
   __shared__ float red4[4];
   gmax = wave_max(gmax);
   if (lane == 0) red4[w] = gmax;
@@ -283,7 +329,15 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   qq += __shfl_xor(qq, 32, kWave);
   // 1% margin covers the bf16 rounding of the stored keys
-  float m_ref = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f * kLog2e;
+  float m_ref = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f;
+  auto neg_ref = [&]() {
+    const float v = m_ref == -INFINITY ? 0.f : -m_ref;
+    f32x16 r;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r[e] = v;
+    return r;
+  };
+  f32x16 negm = neg_ref();
 
   // Blocked logits of a 32-key half starting at key s0 become -inf. Allowed
   // keys of this lane's row form one interval; relative to the lane's first
@@ -306,130 +360,143 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       sv[e] = (uint32_t)(off - lo) <= span ? sv[e] : -INFINITY;
     }
   };
-  auto qk_half = [&](int slot) {
-    f32x16 acc = f32x16{};
+  auto qk_half = [&](int slot, const f32x16 &init) {
+    f32x16 acc = init;
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(slot, ks), qf[ks], acc, 0, 0, 0);
     return acc;
   };
 
-  // One half-step u = 2 it + kb handles keys s0 + 32 kb .. +31 of tile it
-  // (K half u). While its softmax and PV run, the S of half u + 1 goes to the
-  // matrix pipe; the first half-step of a tile also prefetches K halves u + 3,
-  // u + 4 and V tile it + 1 into buffers last read before the previous barrier.
-  // Software pipeline in groups of 4 MFMAs: the fragments of group g+1 are
-  // read from LDS while group g's MFMAs run, and the exponentials and global
-  // prefetches are spread over the groups; scheduling fences between groups
-  // keep that order and bound the fragment registers.
-  // par_tag: the parity of `it` when known at compile time (then every LDS
-  // slot and buffer index below is an immediate), else -1.
-  auto half_step = [&](auto masked_tag, auto next_tag, auto kb_tag, auto par_tag,
-                       int it, f32x16 &s_cur, f32x16 &s_nxt) {
+  // One step per 64-key tile it, as two 32-key halves (K halves u = 2 it and
+  // 2 it + 1). While the softmax and PV of half u run, the S of half u + 1
+  // goes to the matrix pipe. The work is a fixed sequence of groups of 4
+  // MFMAs: for each half, kNG groups of S MFMAs then kPG groups of PV MFMAs.
+  // The fragments of group i + 1 are read from LDS while group i runs (across
+  // the halves; only the tile's first group waits for its reads), each group
+  // carries its share of the softmax arithmetic, and the first half issues
+  // the tile's prefetches (K halves 2 it + 3, 2 it + 4 and V tile it + 1, into
+  // buffers last read before the previous barrier), a few per group.
+  // Scheduling fences between groups keep that order and bound the fragment
+  // registers. par_tag: the parity of `it` when known at compile time (then
+  // every LDS slot and buffer index is an immediate), else -1.
+  using Sc = TileSched<D>;
+  constexpr int kG = Sc::kG, kNG = Sc::kNG, kNGT = Sc::kNGT, kPieces = Sc::kPieces, kPPG = Sc::kPPG;
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+
+  auto tile_step = [&](auto masked_tag, auto next_tag, auto par_tag, int it, f32x16 &s_a,
+                       f32x16 &s_b) {
     constexpr bool kMasked = decltype(masked_tag)::value;
-    constexpr bool kNext = decltype(next_tag)::value;
-    constexpr int kb = decltype(kb_tag)::value;
+    constexpr bool kNext = decltype(next_tag)::value;  // S of half 2 it + 2 is needed
     constexpr int kPar = decltype(par_tag)::value;
     const int par = kPar >= 0 ? kPar : (it & 1);
-    const int u_slot = 2 * par + kb;  // K half u sits in slot u_slot & 3
-    constexpr int kG = 4;                                  // MFMAs per group
-    constexpr int kNG = Cfg::kKS / kG;                     // groups of the S phase
-    constexpr int kEPG = 16 / kNG;                         // weights per group
-    constexpr int kPG = Cfg::kDB / 2;                      // PV groups (2 db x 2 kk)
-    const int s0 = my_begin + it * kBN + 32 * kb;
+    const int s_tile = my_begin + it * kBN;
 
-    if (kMasked) mask_half(s_cur, s0);
-    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+    // fragments of group gi of the tile (4 of them)
+    auto read_frags = [&](auto gi_tag, bf16x8 (&fr)[4]) {
+      constexpr int gi = decltype(gi_tag)::value;
+      constexpr int kb = gi / kNGT, gl = gi % kNGT;
+      if constexpr (gl < kNG) {
+        if constexpr (kb == 0 || kNext) {
+#pragma unroll
+          for (int j = 0; j < kG; ++j) fr[j] = kfrag((2 * par + kb + 1) & 3, gl * kG + j);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = 4 * (gl - kNG) + j;  // PV MFMA m: channel block m % kDB, keys 16 (m / kDB) +
+          fr[j] = vfrag(par, m % Cfg::kDB, 2 * kb + m / Cfg::kDB);
+        }
+      }
+    };
+    auto issue_piece = [&](int pc) {
+      if (pc < Cfg::kKHalfLoads)
+        issue_k_piece(it + 1, 1, (2 * par + 3) & 3, pc);
+      else if (pc < 2 * Cfg::kKHalfLoads)
+        issue_k_piece(it + 2, 0, (2 * par) & 3, pc - Cfg::kKHalfLoads);
+      else
+        issue_v_piece(it + 1, par ^ 1, pc - 2 * Cfg::kKHalfLoads);
+    };
 
-    // S phase: S of half u + 1 on the matrix pipe, this half's weights on the
-    // VALU, packed to bf16 pairs as they are formed. l sums the bf16-rounded
-    // weights the PV MFMAs use, so numerator and denominator of O / l carry
-    // the same rounding.
+    float ex[16];
     bf16x8 pf[2];
-    float psum = 0.f;
-    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-    bf16x8 kf[kG], kfn[kG], vf[4];
-    // Every prefetch of tile it is issued in its first half-step, so it has
-    // the whole tile to land before the barrier: K halves 2 it + 3 and
-    // 2 it + 4 here (their slots were last read before the previous barrier),
-    // V tile it + 1 at the start of the PV phase.
-    if (kb == 0) {
+    float psum[4];
+    bf16x8 fr[4], frn[4];
+    if (kMasked) mask_half(s_a, s_tile);
+    read_frags(std::integral_constant<int, 0>{}, fr);
+    static_for<2 * kNGT>([&](auto g_tag) {
+      constexpr int gi = decltype(g_tag)::value;
+      constexpr int kb = gi / kNGT, g = gi % kNGT;
+      constexpr bool kS = g < kNG;
+      constexpr bool kSActive = kS && (kb == 0 || kNext);
+      f32x16 &s_cur = kb == 0 ? s_a : s_b;
+      f32x16 &s_nxt = kb == 0 ? s_b : s_a;
+      if constexpr (g == 0) {
+        if (kb == 1 && kMasked) mask_half(s_b, s_tile + 32);
 #pragma unroll
-      for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(it + 1, 1, (u_slot + 3) & 3, i);
-#pragma unroll
-      for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(it + 2, 0, (u_slot + 4) & 3, i);
-    }
-    if (kNext) {
-      s_nxt = f32x16{};
-#pragma unroll
-      for (int j = 0; j < kG; ++j) kf[j] = kfrag((u_slot + 1) & 3, j);
-    }
-#pragma unroll
-    for (int g = 0; g < kNG; ++g) {
-      if (kNext && g + 1 < kNG) {
-#pragma unroll
-        for (int j = 0; j < kG; ++j) kfn[j] = kfrag((u_slot + 1) & 3, (g + 1) * kG + j);
+        for (int qd = 0; qd < 4; ++qd) psum[qd] = 0.f;
       }
-      if (g + 1 == kNG) {  // V fragments of the first PV group
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vf[j] = vfrag(par, j >> 1, 2 * kb + (j & 1));
-      }
-      if (kNext) {
+      if constexpr (gi + 1 < 2 * kNGT) read_frags(std::integral_constant<int, gi + 1>{}, frn);
+      constexpr int n_reads = (gi + 1 < 2 * kNGT)
+                                  ? (((gi + 1) % kNGT < kNG && (gi + 1) / kNGT == 1 && !kNext) ? 0 : 4)
+                                  : 0;
+      if constexpr (kSActive) {
 #pragma unroll
         for (int j = 0; j < kG; ++j)
-          s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[g * kG + j], s_nxt, 0, 0, 0);
-      }
+          s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[g * kG + j],
+                                                          (g == 0 && j == 0) ? negm : s_nxt, 0, 0, 0);
+      } else if constexpr (!kS) {
 #pragma unroll
-      for (int e = g * kEPG; e < (g + 1) * kEPG; e += 2) {
-        bf16x2 pr;
-        pr[0] = (bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[e], kLog2e, neg_m));
-        pr[1] = (bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[e + 1], kLog2e, neg_m));
-        pf[e >> 3][e & 7] = pr[0];
-        pf[e >> 3][(e + 1) & 7] = pr[1];
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+        for (int j = 0; j < 4; ++j) {
+          const int m = 4 * (g - kNG) + j;
+          acc_o[m % Cfg::kDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              fr[j], pf[m / Cfg::kDB], acc_o[m % Cfg::kDB], 0, 0, 0);
+        }
       }
+      constexpr int n_mfma = (kSActive || !kS) ? 4 : 0;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        if (Sc::e_grp(qd) == g) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ex[4 * qd + i] = __builtin_amdgcn_exp2f(s_cur[4 * qd + i]);
+        }
+        if (Sc::c_grp(qd) == g) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pf[qd >> 1][4 * (qd & 1) + i] = (bf16)ex[4 * qd + i];
+        }
+        if (Sc::d_grp(qd) == g) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const bf16x2 pr = {pf[qd >> 1][4 * (qd & 1) + 2 * i],
+                               pf[qd >> 1][4 * (qd & 1) + 2 * i + 1]};
+            psum[qd] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[qd], false);
+          }
+        }
+      }
+      if constexpr (kb == 0) {
+#pragma unroll
+        for (int i = 0; i < kPPG; ++i)
+          if (g * kPPG + i < kPieces) issue_piece(g * kPPG + i);
+      }
+      constexpr int n_valu = Sc::valu_of(g);
       // order inside the group: LDS reads for the next group, then each MFMA
       // followed by its share of the softmax arithmetic
-      if (kNext && g + 1 < kNG) __builtin_amdgcn_sched_group_barrier(0x100, kG, 0);
-      if (g + 1 == kNG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if constexpr (n_reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, n_reads, 0);
+      if constexpr (n_mfma > 0) {
 #pragma unroll
-      for (int j = 0; j < kG; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3 * kEPG / kG, 0);
+        for (int j = 0; j < 4; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if constexpr (n_valu > 0) __builtin_amdgcn_sched_group_barrier(0x002, (n_valu + 3) / 4, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (g == kNGT - 1) l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+      if constexpr (gi + 1 < 2 * kNGT) {
 #pragma unroll
-      for (int j = 0; j < kG; ++j) kf[j] = kfn[j];
-    }
-    l_run += psum;
-
-    // PV phase: keys of this half (kk = 2 kb, 2 kb + 1), two 32-channel blocks
-    // of O^T per group, the next group's V fragments read ahead
-    if (kb == 0) {
-#pragma unroll
-      for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(it + 1, par ^ 1, i);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int pg = 0; pg < kPG; ++pg) {
-      bf16x8 vfn[4];
-      if (pg + 1 < kPG) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vfn[j] = vfrag(par, 2 * (pg + 1) + (j >> 1), 2 * kb + (j & 1));
+        for (int j = 0; j < 4; ++j) fr[j] = frn[j];
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int db = 2 * pg + (j >> 1);
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j & 1], acc_o[db], 0, 0, 0);
-      }
-      if (pg + 1 < kPG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (pg + 1 < kPG) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vf[j] = vfn[j];
-      }
-    }
+    });
+    publish_tiles();  // this tile's prefetches have landed
   };
 
   // Tiles where no key is blocked for any row of the workgroup form one
@@ -447,25 +514,17 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   auto run = [&](f32x16 s_a) {
     using T_ = std::true_type;
     using F_ = std::false_type;
-    using K0 = std::integral_constant<int, 0>;
-    using K1 = std::integral_constant<int, 1>;
     f32x16 s_b;
     using PR = std::integral_constant<int, -1>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     auto masked_tile = [&](int it) {
-      half_step(T_{}, T_{}, K0{}, PR{}, it, s_a, s_b);
       if (it + 1 < n_tiles)
-        half_step(T_{}, T_{}, K1{}, PR{}, it, s_b, s_a);
+        tile_step(T_{}, T_{}, PR{}, it, s_a, s_b);
       else
-        half_step(T_{}, F_{}, K1{}, PR{}, it, s_b, s_a);
-      publish_tiles();  // this tile's prefetches have landed
+        tile_step(T_{}, F_{}, PR{}, it, s_a, s_b);
     };
-    auto full_tile = [&](auto par_tag, int it) {
-      half_step(F_{}, T_{}, K0{}, par_tag, it, s_a, s_b);
-      half_step(F_{}, T_{}, K1{}, par_tag, it, s_b, s_a);
-      publish_tiles();
-    };
+    auto full_tile = [&](auto par_tag, int it) { tile_step(F_{}, T_{}, par_tag, it, s_a, s_b); };
     int it = 0;
     const int head_end = min(it_lo, n_tiles);
     for (; it < head_end; ++it) masked_tile(it);
@@ -482,7 +541,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // S of K half 0; the barrier after it orders these reads before any later
   // write to slot 0
   f32x16 s0_first = f32x16{};
-  if (n_tiles > 0) s0_first = qk_half(0);
+  if (n_tiles > 0) s0_first = qk_half(0, negm);
   if (!__syncthreads_and(2.f * m_ref <= 100.f) || force_exact_max) {
     // Exact row maxima (log2 units) over the allowed keys: each tile's two K
     // halves go to slots 0 and 1, S MFMAs only. Rare; kept simple.
@@ -495,17 +554,18 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       publish_tiles();
 #pragma unroll
       for (int kbh = 0; kbh < 2; ++kbh) {
-        f32x16 sv = qk_half(kbh);
+        f32x16 sv = qk_half(kbh, f32x16{});
         mask_half(sv, my_begin + it * kBN + 32 * kbh);
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[e]);
       }
       __syncthreads();  // reads done before the next tile overwrites the slots
     }
-    m_ref = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * kLog2e;
+    m_ref = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    negm = neg_ref();
     issue_prologue();
     publish_tiles();
-    if (n_tiles > 0) s0_first = qk_half(0);
+    if (n_tiles > 0) s0_first = qk_half(0, negm);
     __syncthreads();
   }
   run(s0_first);

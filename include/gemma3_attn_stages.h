@@ -46,7 +46,8 @@ extern "C" {
  *                                 Not written when QKV_PROJ and QK_NORM run in
  *                                 one call on bf16 with H d_h and H_kv d_h
  *                                 multiples of 256 (one fused kernel then)
- *   q    [B, H, T, d_h]           normalised, rotated, times alpha
+ *   q    [B, H, T, d_h]           normalised, rotated, times alpha (bf16: times
+ *                                 alpha log2(e), the attention kernel's base-2 logit scale)
  *   k    [B, H_kv, T_pad, d_h]    normalised, rotated (rows T..T_pad-1 zero)
  *   vt   [B, H_kv, d_h, T_pad]    V transposed (columns T..T_pad-1 zero)
  *   attn_part                     split-KV partial outputs of the attention stage

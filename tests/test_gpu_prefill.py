@@ -3,6 +3,8 @@ same seeded inputs. Small cases cover every kernel variant with ragged tails;
 the workload cases run at full size (all rows for the 1B-shaped pair, sampled
 rows for the 4B-like tile and the 27B-shaped pair)."""
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -114,7 +116,8 @@ def test_cfg1_fp32_local_layer(gpu_lib):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_intermediates(gpu_lib, dtype):
-    """Q (normalised, rotated, times alpha), K (normalised, rotated) and V^T in
+    """Q (normalised, rotated, times alpha; on bf16 also times log2(e), the
+    attention kernel's base-2 logit scale), K (normalised, rotated) and V^T in
     the workspace against the oracle's intermediates; padding rows are zero."""
     B, T, D, H, Hk, d_h = 2, 100, 128, 4, 2, 128
     inp = small_prefill_inputs(3, B, T, D, H, Hk, d_h, dtype)
@@ -134,7 +137,7 @@ def test_intermediates(gpu_lib, dtype):
     v = f64(it_gpu["vt"])[:, :, :, :T].transpose(0, 3, 1, 2)
     check = assert_bf16_close if dtype == "bf16" else (
         lambda g, r, n: assert_f32_close(g, r, n, atol=2e-5))
-    check(q, it["q_tilde"], "q")
+    check(q, it["q_tilde"] * (math.log2(math.e) if dtype == "bf16" else 1.0), "q")
     check(k, it["k_rope"], "k")
     check(v, it["v"], "v")
     assert np.all(f64(it_gpu["k"])[:, :, T:Tp] == 0) and np.all(f64(it_gpu["vt"])[..., T:Tp] == 0)
