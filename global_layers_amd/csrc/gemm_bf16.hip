@@ -24,10 +24,18 @@ template <int N> struct VmWait {
   static constexpr int kImm = (N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 };
 
-// One direct global -> LDS load: lane l moves 16 bytes to lds + 16 l.
-DEVI void load_lds16(const void *g, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave_base,
-                                   16, 0, 0);
+// One direct global -> LDS load: lane l moves the 16 bytes at sbase + lane_off
+// (sbase wave-uniform) to LDS byte lds_wave_off + 16 l (wave-uniform offset).
+// Inline assembly: the compiler would count an LDS-writing load as a memory
+// access of unknown order and make every later fragment read wait for all
+// LDS reads in flight; hidden from it, the reads keep their partial waits. The
+// k loop waits for these loads explicitly (vmcnt) before the barrier that
+// publishes a stage.
+DEVI void load_lds16(const void *sbase, uint32_t lane_off, uint32_t lds_wave_off) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"(sbase), "s"(lds_wave_off)
+               : "memory", "m0");
 }
 
 // Tile of BM x BN outputs, K sliced by BK, NST LDS stages. Waves WM x WN.
@@ -216,7 +224,8 @@ DEVI void qkv_epilogue(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, int n0,
 template <int BM, int BN, int WM, int WN, int BK, int NST, bool kQkv>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16 *__restrict__ B1,
-             int N0, bf16 *__restrict__ C, int M, int N, int K, int n_tiles_n, QkvEpilogue ep) {
+             int N0, bf16 *__restrict__ C, int ldc, int M, int N, int K, int n_tiles_n,
+             QkvEpilogue ep) {
   using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -237,30 +246,41 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   const int tile_m = first_m + in_group % gm_size, tile_n = in_group / gm_size;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-  // Per-lane global sources of the 1 KB pieces this wave loads (row clamped
-  // into range; rows past M / N only feed outputs that are never stored).
+  // The 1 KB pieces this wave loads per stage: piece = wave + kWaves i; lane
+  // l of it covers byte 16 l, i.e. row r, logical chunk p ^ swz(r) of the
+  // slice. Rows past M / N are clamped (they only feed outputs never stored).
+  // Per-lane byte offsets from the tile's first row do not depend on the k
+  // slice; the slice only moves the wave-uniform base. A tile never straddles
+  // N0 (the launcher splits such problems), so its weight rows come from one
+  // matrix.
+  const bf16 *b_tile = n0 < N0 ? B0 + (size_t)n0 * K : B1 + (size_t)(n0 - N0) * K;
+  const bf16 *a_tile = A + (size_t)m0 * K;
+  uint32_t a_off[Cfg::kALoads], b_off[Cfg::kBLoads];
+#pragma unroll
+  for (int i = 0; i < Cfg::kALoads; ++i) {
+    const int byte = (wave + Cfg::kWaves * i) * 1024 + 16 * lane;
+    const int r = byte / Cfg::kRowBytes, p = (byte % Cfg::kRowBytes) / 16;
+    const int c = p ^ gemm_swz<Cfg::kChunks>(r);
+    a_off[i] = (uint32_t)(((size_t)(min(m0 + r, M - 1) - m0) * K + 8 * c) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::kBLoads; ++i) {
+    const int byte = (wave + Cfg::kWaves * i) * 1024 + 16 * lane;
+    const int r = byte / Cfg::kRowBytes, p = (byte % Cfg::kRowBytes) / 16;
+    const int c = p ^ gemm_swz<Cfg::kChunks>(r);
+    b_off[i] = (uint32_t)(((size_t)(min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
+  }
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
   auto issue = [&](int kt, int stage) {
-    char *sbase = lds + stage * Cfg::kStageBytes;
-    const int k0 = kt * BK;
+    const uint32_t sb = lds0 + stage * Cfg::kStageBytes;
+    const bf16 *ak = a_tile + kt * BK, *bk = b_tile + kt * BK;
 #pragma unroll
-    for (int i = 0; i < Cfg::kALoads; ++i) {
-      const int piece = wave + Cfg::kWaves * i;
-      const int byte = piece * 1024 + 16 * lane;
-      const int r = byte / Cfg::kRowBytes, p = (byte % Cfg::kRowBytes) / 16;
-      const int c = p ^ gemm_swz<Cfg::kChunks>(r);
-      const int gm = min(m0 + r, M - 1);
-      load_lds16(A + (size_t)gm * K + k0 + 8 * c, sbase + piece * 1024);
-    }
+    for (int i = 0; i < Cfg::kALoads; ++i)
+      load_lds16(ak, a_off[i], sb + (wu + Cfg::kWaves * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < Cfg::kBLoads; ++i) {
-      const int piece = wave + Cfg::kWaves * i;
-      const int byte = piece * 1024 + 16 * lane;
-      const int r = byte / Cfg::kRowBytes, p = (byte % Cfg::kRowBytes) / 16;
-      const int c = p ^ gemm_swz<Cfg::kChunks>(r);
-      const int gn = min(n0 + r, N - 1);
-      const bf16 *src = gn < N0 ? B0 + (size_t)gn * K : B1 + (size_t)(gn - N0) * K;
-      load_lds16(src + k0 + 8 * c, sbase + Cfg::kABytes + piece * 1024);
-    }
+    for (int i = 0; i < Cfg::kBLoads; ++i)
+      load_lds16(bk, b_off[i], sb + Cfg::kABytes + (wu + Cfg::kWaves * i) * 1024);
   };
 
   f32x16 acc[Cfg::kFM][Cfg::kFN];
@@ -270,52 +290,78 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
     for (int j = 0; j < Cfg::kFN; ++j) acc[i][j] = f32x16{};
 
   const int nk = K / BK;
+  // Every iteration issues one k-tile (past the end: the last one again, into
+  // a stage nothing reads any more), so exactly NST - 2 tiles are in flight
+  // behind the one an iteration waits for.
+  auto issue_clamped = [&](int kt) { issue(min(kt, nk - 1), kt % NST); };
   // prologue: k-tiles 0 .. NST-2 in flight
 #pragma unroll
-  for (int s0 = 0; s0 < NST - 1; ++s0)
-    if (s0 < nk) issue(s0, s0);
+  for (int s0 = 0; s0 < NST - 1; ++s0) issue_clamped(s0);
 
   const int lrow = lane & 31, hh = lane >> 5;
-  // wait until k-tile kt has landed: everything issued after it may stay in flight
-  auto wait_tile = [&](int kt) {
-    const int after = min(nk - 1, kt + NST - 2) - kt;  // tiles issued after kt
-    if (after >= 2) __builtin_amdgcn_s_waitcnt(VmWait<2 * Cfg::kLoadsPerTile>::kImm);
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(VmWait<Cfg::kLoadsPerTile>::kImm);
-    else __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm);
+  // wait until the oldest k-tile in flight has landed, then for every wave
+  auto wait_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(VmWait<(NST - 2) * Cfg::kLoadsPerTile>::kImm);
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
-  static_assert(NST <= 4, "wait_tile covers up to two tiles in flight behind the current");
 
-  wait_tile(0);
+  // Fragment byte offsets inside a stage: row r of the A (B) slice, logical
+  // chunk 2 kk + hh. The swizzle flips only the low chunk bits, so per
+  // fragment one base plus a compile-time kk term covers the slice.
+  constexpr int kKK = BK / 16;
+  uint32_t a_fo[Cfg::kFM], b_fo[Cfg::kFN];
+  int a_sw[Cfg::kFM], b_sw[Cfg::kFN];
+#pragma unroll
+  for (int i = 0; i < Cfg::kFM; ++i) {
+    const int r = wm * Cfg::kWaveM + i * 32 + lrow;
+    a_fo[i] = r * Cfg::kRowBytes;
+    a_sw[i] = gemm_swz<Cfg::kChunks>(r);
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg::kFN; ++j) {
+    const int r = wn * Cfg::kWaveN + j * 32 + lrow;
+    b_fo[j] = Cfg::kABytes + r * Cfg::kRowBytes;
+    b_sw[j] = gemm_swz<Cfg::kChunks>(r);
+  }
+  // fragments of slice step kk of stage st (double-buffered: the reads of
+  // step kk + 1 are in flight while step kk's MFMAs run)
+  bf16x8 af[2][Cfg::kFM], bfr[2][Cfg::kFN];
+  auto read_frags = [&](int st, int kk, bf16x8 (&a)[Cfg::kFM], bf16x8 (&b)[Cfg::kFN]) {
+    const char *sb = lds + st * Cfg::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < Cfg::kFM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8 *>(sb + a_fo[i] + 16 * ((2 * kk + hh) ^ a_sw[i]));
+#pragma unroll
+    for (int j = 0; j < Cfg::kFN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8 *>(sb + b_fo[j] + 16 * ((2 * kk + hh) ^ b_sw[j]));
+  };
+
   for (int kt = 0; kt < nk; ++kt) {
-    // refill the stage read in iteration kt-1 (all waves passed its barrier)
-    if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
-    const char *sbase = lds + (kt % NST) * Cfg::kStageBytes;
-    const char *as = sbase + (wm * Cfg::kWaveM + lrow) * Cfg::kRowBytes;
-    const char *bs = sbase + Cfg::kABytes + (wn * Cfg::kWaveN + lrow) * Cfg::kRowBytes;
+    // k-tile kt has landed for every wave; the MFMAs of the previous slice's
+    // last step are still in the pipe while this slice's first reads go out
+    wait_tile();
+    const int st = kt % NST;
+    read_frags(st, 0, af[0], bfr[0]);
+    // refill the stage read in iteration kt-1 (all waves passed the barrier)
+    issue_clamped(kt + NST - 1);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[Cfg::kFM], bfr[Cfg::kFN];
-#pragma unroll
-      for (int i = 0; i < Cfg::kFM; ++i) {
-        const int r = wm * Cfg::kWaveM + i * 32 + lrow;
-        af[i] = *reinterpret_cast<const bf16x8 *>(
-            as + i * 32 * Cfg::kRowBytes + 16 * ((2 * kk + hh) ^ gemm_swz<Cfg::kChunks>(r)));
-      }
-#pragma unroll
-      for (int j = 0; j < Cfg::kFN; ++j) {
-        const int r = wn * Cfg::kWaveN + j * 32 + lrow;
-        bfr[j] = *reinterpret_cast<const bf16x8 *>(
-            bs + j * 32 * Cfg::kRowBytes + 16 * ((2 * kk + hh) ^ gemm_swz<Cfg::kChunks>(r)));
-      }
+    for (int kk = 0; kk < kKK; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < kKK) read_frags(st, kk + 1, af[cur ^ 1], bfr[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < Cfg::kFM; ++i)
 #pragma unroll
         for (int j = 0; j < Cfg::kFN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j],
+                                                              0, 0, 0);
+      // the next step's reads go out first, then the MFMAs
+      if (kk + 1 < kKK) __builtin_amdgcn_sched_group_barrier(0x100, Cfg::kFM + Cfg::kFN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, Cfg::kFM * Cfg::kFN, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) wait_tile(kt + 1);
   }
+  static_assert(kKK % 2 == 0, "step 0 of every slice reads into buffer 0");
 
   if constexpr (kQkv) {
     qkv_epilogue<BM, BN, WM, WN, Cfg::kFM, Cfg::kFN>(acc, lds, m0, n0, M, ep);
@@ -335,11 +381,11 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][g * 4 + r];
         if (gn + 3 < N) {
-          *reinterpret_cast<bf16x4 *>(C + (size_t)gm * N + gn) = v;
+          *reinterpret_cast<bf16x4 *>(C + (size_t)gm * ldc + gn) = v;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (gn + r < N) C[(size_t)gm * N + gn + r] = v[r];
+            if (gn + r < N) C[(size_t)gm * ldc + gn + r] = v[r];
         }
       }
     }
@@ -348,7 +394,18 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
 
 template <int BM, int BN, int WM, int WN, int BK, int NST, bool kQkv = false>
 hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C, int M,
-                       int N, int K, hipStream_t s, const QkvEpilogue &ep = QkvEpilogue{}) {
+                       int N, int K, hipStream_t s, const QkvEpilogue &ep = QkvEpilogue{},
+                       int ldc = -1) {
+  if (ldc < 0) ldc = N;
+  // every tile's weight rows come from one matrix
+  if (N0 < N && N0 % BN != 0) {
+    if (kQkv) return hipErrorInvalidValue;
+    hipError_t e = launch_gemm<BM, BN, WM, WN, BK, NST>(A, B0, B0, N0, C, M, N0, K, s,
+                                                       QkvEpilogue{}, ldc);
+    if (e != hipSuccess) return e;
+    return launch_gemm<BM, BN, WM, WN, BK, NST>(A, B1, B1, N - N0, C + N0, M, N - N0, K, s,
+                                               QkvEpilogue{}, ldc);
+  }
   using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
   const int tm = div_up_h(M, BM), tn = div_up_h(N, BN);
   auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST, kQkv>;
@@ -357,8 +414,8 @@ hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(Cfg::kThreads), kLds, s, A, B0, B1, N0, C, M, N,
-                     K, tn, ep);
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(Cfg::kThreads), kLds, s, A, B0, B1, N0, C, ldc, M,
+                     N, K, tn, ep);
   return hipGetLastError();
 }
 
@@ -448,8 +505,8 @@ hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, in
   }
   switch (best) {
     case 0: return launch_gemm<256, 256, 2, 4, 64, 2>(A, B0, B1, N0, C, M, N, K, s);
-    case 1: return launch_gemm<128, 256, 2, 4, 32, 4>(A, B0, B1, N0, C, M, N, K, s);
-    default: return launch_gemm<128, 128, 2, 2, 32, 4>(A, B0, B1, N0, C, M, N, K, s);
+    case 1: return launch_gemm<128, 256, 2, 4, 64, 3>(A, B0, B1, N0, C, M, N, K, s);
+    default: return launch_gemm<128, 128, 2, 2, 64, 3>(A, B0, B1, N0, C, M, N, K, s);
   }
 }
 
@@ -463,7 +520,7 @@ hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_k
   const double c128 = (double)div_up_h(t128, 256) * 128 * 256 / 0.9;
   if (c256 <= c128)
     return launch_gemm<256, 256, 2, 4, 64, 2, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
-  return launch_gemm<128, 256, 2, 4, 32, 4, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
+  return launch_gemm<128, 256, 2, 4, 64, 3, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
 }
 
 int gemv_ksplit(int N, int K) {
