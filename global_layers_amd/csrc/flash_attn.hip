@@ -43,7 +43,6 @@ namespace {
 
 constexpr int kBN = 64;       // keys per tile
 constexpr int kThreads = 256; // 4 waves
-constexpr int kRowsPerWave = 32;
 
 template <int D> struct AttnCfg {
   static constexpr int kKRowBytes = 2 * D;            // one key row of K
@@ -149,7 +148,7 @@ struct Geo {  // per-workgroup geometry, identical in the attention and combine 
 };
 
 DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp, int n_qtiles,
-                  int n_hgrp, int chunk_keys) {
+                  int n_hgrp, int chunk_keys, int rows_per_wave) {
   Geo g;
   g.qt = n_qtiles - 1 - base_id % n_qtiles;  // longest (latest) query tile first
   int rest = base_id / n_qtiles;
@@ -157,7 +156,7 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
   rest /= n_hgrp;
   g.kh = rest % a.Hk;
   g.b = rest / a.Hk;
-  const int TQ = kRowsPerWave * (4 / gp);
+  const int TQ = rows_per_wave * (4 / gp);
   g.t_lo = g.qt * TQ;
   g.t_hi = min(a.T, g.t_lo + TQ);
   g.len = kv_len ? kv_len[g.b] : a.T;
@@ -168,7 +167,13 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
   return g;
 }
 
-template <int D>
+// RB: blocks of 32 query rows per wave. Each K / V^T fragment read from LDS
+// feeds RB MFMAs; one wave per SIMD reads LDS at less than one 1 KB fragment
+// per MFMA, so two blocks run closer to the matrix pipe's rate. Used at
+// d_h = 128 on layers without a sliding window (at d_h = 256 two blocks' O
+// and Q do not fit the register file, and on sliding-window layers the
+// larger share of masked tiles runs slower with the extra registers).
+template <int D, int RB>
 __global__ void __launch_bounds__(kThreads)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
@@ -186,14 +191,15 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // XCD.
   const int bid = remap ? xcd_remap(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int split = bid % n_split;
-  const Geo geo = geometry(a, kv_len, bid / n_split, gp, n_qtiles, n_hgrp, chunk_keys);
+  constexpr int kRB = RB, kRPW = 32 * RB;
+  const Geo geo = geometry(a, kv_len, bid / n_split, gp, n_qtiles, n_hgrp, chunk_keys, kRPW);
   if (split >= geo.n_active) return;  // uniform per block
   const int b = geo.b, kh = geo.kh;
 
   const int wpg = 4 / gp;  // waves per query head
   const int hg = w / wpg, tb = w % wpg;
   const int h = kh * G + geo.hgrp * gp + hg;
-  const int wq0 = geo.t_lo + tb * kRowsPerWave;   // first query row of this wave
+  const int wq0 = geo.t_lo + tb * kRPW;   // first query row of this wave
   const int len = geo.len;
   const int t_lo = geo.t_lo, t_hi = geo.t_hi;
 
@@ -201,22 +207,29 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int my_end = geo.kv_end > geo.kv_begin ? min(geo.kv_end, my_begin + chunk_keys) : my_begin;
 
   const int col = lane & 31, hh = lane >> 5;
-  const int my_t = wq0 + col;  // this lane's query row
+  int my_t[kRB];  // this lane's query row in each row block
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) my_t[rb] = wq0 + 32 * rb + col;
 
   // Q^T fragments (B operand): query my_t, channels 16 ks + 8 hh + [0, 8).
-  bf16x8 qf[Cfg::kKS];
-  {
-    const bool ok = my_t < a.T;
-    const bf16 *qp = q + (((size_t)b * a.H + h) * a.T + (ok ? my_t : 0)) * D + 8 * hh;
+  bf16x8 qf[kRB][Cfg::kKS];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const bool ok = my_t[rb] < a.T;
+    const bf16 *qp = q + (((size_t)b * a.H + h) * a.T + (ok ? my_t[rb] : 0)) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
-      qf[ks] = ok ? *reinterpret_cast<const bf16x8 *>(qp + 16 * ks) : bf16x8{};
+      qf[rb][ks] = ok ? *reinterpret_cast<const bf16x8 *>(qp + 16 * ks) : bf16x8{};
   }
 
-  f32x16 acc_o[Cfg::kDB];
+  f32x16 acc_o[kRB][Cfg::kDB];
 #pragma unroll
-  for (int i = 0; i < Cfg::kDB; ++i) acc_o[i] = f32x16{};
-  float l_run = 0.f;
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int i = 0; i < Cfg::kDB; ++i) acc_o[rb][i] = f32x16{};
+  float l_run[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) l_run[rb] = 0.f;
 
   const char *kbase = (const char *)(k + ((size_t)b * a.Hk + kh) * a.T_pad * D);
   const char *vbase = (const char *)(vt + ((size_t)b * a.Hk + kh) * D * a.T_pad);
@@ -319,52 +332,66 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   if (lane == 0) red4[w] = gmax;
   __syncthreads();
   gmax = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
-  float qq = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < Cfg::kKS; ++ks)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = (float)qf[ks][j];
-      qq = fmaf(v, v, qq);
-    }
-  qq += __shfl_xor(qq, 32, kWave);
-  // 1% margin covers the bf16 rounding of the stored keys
-  float m_ref = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f;
-  auto neg_ref = [&]() {
-    const float v = m_ref == -INFINITY ? 0.f : -m_ref;
+  float m_ref[kRB];
+  f32x16 negm[kRB];
+  auto neg_ref = [&](int rb) {
+    const float v = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
     f32x16 r;
 #pragma unroll
     for (int e = 0; e < 16; ++e) r[e] = v;
     return r;
   };
-  f32x16 negm = neg_ref();
+  bool bound_ok = true;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    float qq = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::kKS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = (float)qf[rb][ks][j];
+        qq = fmaf(v, v, qq);
+      }
+    qq += __shfl_xor(qq, 32, kWave);
+    // 1% margin covers the bf16 rounding of the stored keys
+    m_ref[rb] = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f;
+    bound_ok = bound_ok && 2.f * m_ref[rb] <= 100.f;
+    negm[rb] = neg_ref(rb);
+  }
 
-  // Blocked logits of a 32-key half starting at key s0 become -inf. Allowed
-  // keys of this lane's row form one interval; relative to the lane's first
-  // key s0 + 8 hh, element e sits at the compile-time offset
-  // 16 (g >> 1) + 4 (g & 1) + r, so one unsigned compare per element tests
-  // lo <= offset <= hi.
-  auto mask_half = [&](f32x16 &sv, int s0) {
+  // Which logits of a 32-key half starting at key s0 are allowed (bit e of
+  // the result for element e); blocked ones become -inf. Allowed keys of this
+  // lane's row form one interval; relative to the lane's first key s0 + 8 hh,
+  // element e sits at the compile-time offset 16 (g >> 1) + 4 (g & 1) + r, so
+  // one unsigned compare per element tests lo <= offset <= hi.
+  auto mask_bits = [&](int s0, int rb) {
     const int base = s0 + 8 * hh;
-    int hi = min(my_t, len - 1) - base;
-    int lo = (a.local ? my_t - a.window + 1 : -(1 << 30)) - base;
+    int hi = min(my_t[rb], len - 1) - base;
+    int lo = (a.local ? my_t[rb] - a.window + 1 : -(1 << 30)) - base;
     if (hi < lo) {  // nothing allowed
       lo = 1 << 30;
       hi = lo;
     }
     const uint32_t span = (uint32_t)(hi - lo);
+    uint32_t bits = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int g = e >> 2, r = e & 3;
       const int off = 16 * (g >> 1) + 4 * (g & 1) + r;
-      sv[e] = (uint32_t)(off - lo) <= span ? sv[e] : -INFINITY;
+      bits |= ((uint32_t)(off - lo) <= span ? 1u : 0u) << e;
     }
+    return bits;
   };
-  auto qk_half = [&](int slot, const f32x16 &init) {
+  auto mask_half = [&](f32x16 &sv, int s0, int rb) {
+    const uint32_t bits = mask_bits(s0, rb);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sv[e] = (bits >> e) & 1 ? sv[e] : -INFINITY;
+  };
+  auto qk_half = [&](int slot, const f32x16 &init, int rb) {
     f32x16 acc = init;
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(slot, ks), qf[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(slot, ks), qf[rb][ks], acc, 0, 0, 0);
     return acc;
   };
 
@@ -384,8 +411,8 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int kG = Sc::kG, kNG = Sc::kNG, kNGT = Sc::kNGT, kPieces = Sc::kPieces, kPPG = Sc::kPPG;
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  auto tile_step = [&](auto masked_tag, auto next_tag, auto par_tag, int it, f32x16 &s_a,
-                       f32x16 &s_b) {
+  auto tile_step = [&](auto masked_tag, auto next_tag, auto par_tag, int it,
+                       f32x16 (&s_a)[kRB], f32x16 (&s_b)[kRB]) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;  // S of half 2 it + 2 is needed
     constexpr int kPar = decltype(par_tag)::value;
@@ -418,23 +445,30 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         issue_v_piece(it + 1, par ^ 1, pc - 2 * Cfg::kKHalfLoads);
     };
 
-    float ex[16];
-    bf16x8 pf[2];
-    float psum[4];
+    float ex[kRB][16];
+    bf16x8 pf[kRB][2];
+    float psum[kRB][4];
     bf16x8 fr[4], frn[4];
-    if (kMasked) mask_half(s_a, s_tile);
+    // masked tiles: allowed-logit bits of the current half (applied as the
+    // exponentials read the S accumulators)
+    uint32_t mb[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) mb[rb] = kMasked ? mask_bits(s_tile, rb) : 0xFFFFu;
     read_frags(std::integral_constant<int, 0>{}, fr);
     static_for<2 * kNGT>([&](auto g_tag) {
       constexpr int gi = decltype(g_tag)::value;
       constexpr int kb = gi / kNGT, g = gi % kNGT;
       constexpr bool kS = g < kNG;
       constexpr bool kSActive = kS && (kb == 0 || kNext);
-      f32x16 &s_cur = kb == 0 ? s_a : s_b;
-      f32x16 &s_nxt = kb == 0 ? s_b : s_a;
+      f32x16(&s_cur)[kRB] = kb == 0 ? s_a : s_b;
+      f32x16(&s_nxt)[kRB] = kb == 0 ? s_b : s_a;
       if constexpr (g == 0) {
-        if (kb == 1 && kMasked) mask_half(s_b, s_tile + 32);
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) psum[qd] = 0.f;
+        for (int rb = 0; rb < kRB; ++rb) {
+          if (kb == 1 && kMasked) mb[rb] = mask_bits(s_tile + 32, rb);
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) psum[rb][qd] = 0.f;
+        }
       }
       if constexpr (gi + 1 < 2 * kNGT) read_frags(std::integral_constant<int, gi + 1>{}, frn);
       constexpr int n_reads = (gi + 1 < 2 * kNGT)
@@ -443,54 +477,69 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if constexpr (kSActive) {
 #pragma unroll
         for (int j = 0; j < kG; ++j)
-          s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[g * kG + j],
-                                                          (g == 0 && j == 0) ? negm : s_nxt, 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+            s_nxt[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                fr[j], qf[rb][g * kG + j], (g == 0 && j == 0) ? negm[rb] : s_nxt[rb], 0, 0, 0);
       } else if constexpr (!kS) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int m = 4 * (g - kNG) + j;
-          acc_o[m % Cfg::kDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              fr[j], pf[m / Cfg::kDB], acc_o[m % Cfg::kDB], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+            acc_o[rb][m % Cfg::kDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                fr[j], pf[rb][m / Cfg::kDB], acc_o[rb][m % Cfg::kDB], 0, 0, 0);
         }
       }
-      constexpr int n_mfma = (kSActive || !kS) ? 4 : 0;
+      constexpr int n_mfma = (kSActive || !kS) ? 4 * kRB : 0;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        if (Sc::e_grp(qd) == g) {
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ex[4 * qd + i] = __builtin_amdgcn_exp2f(s_cur[4 * qd + i]);
-        }
-        if (Sc::c_grp(qd) == g) {
+        for (int qd = 0; qd < 4; ++qd) {
+          if (Sc::e_grp(qd) == g) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pf[qd >> 1][4 * (qd & 1) + i] = (bf16)ex[4 * qd + i];
-        }
-        if (Sc::d_grp(qd) == g) {
+            for (int i = 0; i < 4; ++i) {
+              const float x = s_cur[rb][4 * qd + i];
+              ex[rb][4 * qd + i] =
+                  __builtin_amdgcn_exp2f(!kMasked || ((mb[rb] >> (4 * qd + i)) & 1) ? x : -INFINITY);
+            }
+          }
+          if (Sc::c_grp(qd) == g) {
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const bf16x2 pr = {pf[qd >> 1][4 * (qd & 1) + 2 * i],
-                               pf[qd >> 1][4 * (qd & 1) + 2 * i + 1]};
-            psum[qd] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[qd], false);
+            for (int i = 0; i < 4; ++i) pf[rb][qd >> 1][4 * (qd & 1) + i] = (bf16)ex[rb][4 * qd + i];
+          }
+          if (Sc::d_grp(qd) == g) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const bf16x2 pr = {pf[rb][qd >> 1][4 * (qd & 1) + 2 * i],
+                                 pf[rb][qd >> 1][4 * (qd & 1) + 2 * i + 1]};
+              psum[rb][qd] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[rb][qd], false);
+            }
           }
         }
-      }
       if constexpr (kb == 0) {
 #pragma unroll
         for (int i = 0; i < kPPG; ++i)
           if (g * kPPG + i < kPieces) issue_piece(g * kPPG + i);
       }
-      constexpr int n_valu = Sc::valu_of(g);
+      constexpr int n_valu = kRB * Sc::valu_of(g);
       // order inside the group: LDS reads for the next group, then each MFMA
       // followed by its share of the softmax arithmetic
       if constexpr (n_reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, n_reads, 0);
       if constexpr (n_mfma > 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < n_mfma; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if constexpr (n_valu > 0) __builtin_amdgcn_sched_group_barrier(0x002, (n_valu + 3) / 4, 0);
+          if constexpr (n_valu > 0)
+            __builtin_amdgcn_sched_group_barrier(0x002, (n_valu + n_mfma - 1) / n_mfma, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (g == kNGT - 1) l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+      if constexpr (g == kNGT - 1) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          l_run[rb] += (psum[rb][0] + psum[rb][1]) + (psum[rb][2] + psum[rb][3]);
+      }
       if constexpr (gi + 1 < 2 * kNGT) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) fr[j] = frn[j];
@@ -511,41 +560,48 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (hi_s0 >= my_begin) it_hi = (hi_s0 - my_begin) / kBN;
     if (lo_s0 > my_begin) it_lo = div_up(lo_s0 - my_begin, kBN);
   }
-  auto run = [&](f32x16 s_a) {
+  auto run = [&](f32x16 (&s_a)[kRB]) {
     using T_ = std::true_type;
     using F_ = std::false_type;
-    f32x16 s_b;
+    f32x16 s_b[kRB];
     using PR = std::integral_constant<int, -1>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    auto masked_tile = [&](int it) {
-      if (it + 1 < n_tiles)
-        tile_step(T_{}, T_{}, PR{}, it, s_a, s_b);
-      else
-        tile_step(T_{}, F_{}, PR{}, it, s_a, s_b);
-    };
+    // Masked tiles always form the S of the next half (one code copy, fewer
+    // registers); after the last tile that reads a K slot holding a clamped
+    // copy of the last tile, and the result is unused.
+    auto masked_tile = [&](int it) { tile_step(T_{}, T_{}, PR{}, it, s_a, s_b); };
     auto full_tile = [&](auto par_tag, int it) { tile_step(F_{}, T_{}, par_tag, it, s_a, s_b); };
-    int it = 0;
     const int head_end = min(it_lo, n_tiles);
-    for (; it < head_end; ++it) masked_tile(it);
     const int full_end = min(it_hi + 1, n_tiles - 1);
-    // full tiles in pairs of known parity
-    if (it < full_end && (it & 1)) full_tile(P1{}, it++);
-    for (; it + 1 < full_end; it += 2) {
-      full_tile(P0{}, it);
-      full_tile(P1{}, it + 1);
+    // One masked loop (one copy of its code): the head segment, then the full
+    // tiles in pairs of known parity, then the tail segment.
+    int it = 0;
+#pragma nounroll
+    for (int seg = 0; seg < 2; ++seg) {
+      const int seg_end = seg == 0 ? head_end : n_tiles;
+      for (; it < seg_end; ++it) masked_tile(it);
+      if (seg == 0) {
+        if (it < full_end && (it & 1)) full_tile(P1{}, it++);
+        for (; it + 1 < full_end; it += 2) {
+          full_tile(P0{}, it);
+          full_tile(P1{}, it + 1);
+        }
+        if (it < full_end) full_tile(P0{}, it++);
+      }
     }
-    if (it < full_end) full_tile(P0{}, it++);
-    for (; it < n_tiles; ++it) masked_tile(it);
   };
   // S of K half 0; the barrier after it orders these reads before any later
   // write to slot 0
-  f32x16 s0_first = f32x16{};
-  if (n_tiles > 0) s0_first = qk_half(0, negm);
-  if (!__syncthreads_and(2.f * m_ref <= 100.f) || force_exact_max) {
+  f32x16 s0_first[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) s0_first[rb] = n_tiles > 0 ? qk_half(0, negm[rb], rb) : f32x16{};
+  if (!__syncthreads_and(bound_ok) || force_exact_max) {
     // Exact row maxima (log2 units) over the allowed keys: each tile's two K
     // halves go to slots 0 and 1, S MFMAs only. Rare; kept simple.
-    float mx = -INFINITY;
+    float mx[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) mx[rb] = -INFINITY;
     for (int it = 0; it < n_tiles; ++it) {
 #pragma unroll
       for (int kbh = 0; kbh < 2; ++kbh)
@@ -553,47 +609,57 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(it, kbh, kbh, i);
       publish_tiles();
 #pragma unroll
-      for (int kbh = 0; kbh < 2; ++kbh) {
-        f32x16 sv = qk_half(kbh, f32x16{});
-        mask_half(sv, my_begin + it * kBN + 32 * kbh);
+      for (int kbh = 0; kbh < 2; ++kbh)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[e]);
-      }
+        for (int rb = 0; rb < kRB; ++rb) {
+          f32x16 sv = qk_half(kbh, f32x16{}, rb);
+          mask_half(sv, my_begin + it * kBN + 32 * kbh, rb);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx[rb] = fmaxf(mx[rb], sv[e]);
+        }
       __syncthreads();  // reads done before the next tile overwrites the slots
     }
-    m_ref = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    negm = neg_ref();
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      m_ref[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32, kWave));
+      negm[rb] = neg_ref(rb);
+    }
     issue_prologue();
     publish_tiles();
-    if (n_tiles > 0) s0_first = qk_half(0, negm);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      s0_first[rb] = n_tiles > 0 ? qk_half(0, negm[rb], rb) : f32x16{};
     __syncthreads();
   }
   run(s0_first);
 
-  // Normalise; write the output row (single chunk) or a partial (several chunks).
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (my_t >= a.T) return;
-  bf16 *op;
-  if (geo.n_active == 1) {
-    op = o + ((size_t)b * a.T + my_t) * ((size_t)a.H * D) + (size_t)h * D;
-  } else {
-    const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t;
-    op = part_o + row * D;
-    if (hh == 0) {
-      part_ml[2 * row] = m_ref;
-      part_ml[2 * row + 1] = l_tot;
+  // Normalise; write the output rows (single chunk) or partials (several chunks).
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, kWave);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (my_t[rb] >= a.T) continue;
+    bf16 *op;
+    if (geo.n_active == 1) {
+      op = o + ((size_t)b * a.T + my_t[rb]) * ((size_t)a.H * D) + (size_t)h * D;
+    } else {
+      const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t[rb];
+      op = part_o + row * D;
+      if (hh == 0) {
+        part_ml[2 * row] = m_ref[rb];
+        part_ml[2 * row + 1] = l_tot;
+      }
     }
+#pragma unroll
+    for (int db = 0; db < Cfg::kDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc_o[rb][db][4 * g + r] * inv);
+        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * hh) = v;
+      }
   }
-#pragma unroll
-  for (int db = 0; db < Cfg::kDB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc_o[db][4 * g + r] * inv);
-      *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * hh) = v;
-    }
 }
 
 // Merge the key chunks of query tiles that had more than one:
@@ -604,7 +670,7 @@ template <int D>
 __global__ void __launch_bounds__(256)
 flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
               const bf16 *__restrict__ part_o, const float *__restrict__ part_ml, AttnArgs a,
-              int gp, int n_qtiles, int n_hgrp, int n_split, int chunk_keys) {
+              int gp, int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int rpw) {
   constexpr int kPer = D / 64;  // channels per lane
   const int lane = threadIdx.x & 63;
   const long row_id = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // over B*H*T
@@ -614,9 +680,9 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
   const int b = (int)(row_id / ((long)a.T * a.H));
   const int G = a.H / a.Hk;
   const int kh = h / G, hgrp = (h % G) / gp;
-  const int qt = t / (kRowsPerWave * (4 / gp));
+  const int qt = t / (rpw * (4 / gp));
   const int base_id = ((b * a.Hk + kh) * n_hgrp + hgrp) * n_qtiles + (n_qtiles - 1 - qt);
-  const Geo geo = geometry(a, kv_len, base_id, gp, n_qtiles, n_hgrp, chunk_keys);
+  const Geo geo = geometry(a, kv_len, base_id, gp, n_qtiles, n_hgrp, chunk_keys, rpw);
   if (geo.n_active <= 1) return;
 
   // every load of the row is issued before any arithmetic (n_active <= 8)
@@ -653,7 +719,7 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
 }
 
 struct Plan {
-  int gp, n_qtiles, n_hgrp, n_split, chunk_keys, remap;
+  int rb, gp, n_qtiles, n_hgrp, n_split, chunk_keys, remap;
   long n_base;
 };
 
@@ -667,7 +733,8 @@ Plan plan(const AttnArgs &a) {
   Plan p;
   const int G = a.H / a.Hk;
   p.gp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const int TQ = kRowsPerWave * (4 / p.gp);
+  p.rb = (a.d_h == 128 && !a.local) ? 2 : 1;
+  const int TQ = 32 * p.rb * (4 / p.gp);
   p.n_qtiles = div_up_h(a.T, TQ);
   p.n_hgrp = G / p.gp;
   const long n_groups = (long)a.B * a.Hk * p.n_hgrp;
@@ -708,16 +775,16 @@ Plan plan(const AttnArgs &a) {
   return p;
 }
 
-template <int D>
-hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
-                    const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
-                    int force, hipStream_t s) {
+template <int D, int RB>
+hipError_t launch_rb(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
+                     const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml,
+                     const AttnArgs &a, const Plan &p, int force, hipStream_t s) {
   using Cfg = AttnCfg<D>;
-  const Plan p = plan(a);
-  hipError_t e = hipFuncSetAttribute((const void *)flash_attn_fwd_bf16<D>,
+  auto kern = flash_attn_fwd_bf16<D, RB>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(flash_attn_fwd_bf16<D>, dim3((unsigned)(p.n_base * p.n_split)),
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.n_base * p.n_split)),
                      dim3(kThreads), Cfg::kLdsBytes, s, q, k, vt, kv_len, gamma_k, o, part_o,
                      part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys, p.remap,
                      force);
@@ -725,8 +792,21 @@ hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t 
   if (e != hipSuccess || p.n_split == 1) return e;
   const long rows = (long)a.B * a.H * a.T;
   hipLaunchKernelGGL(flash_combine<D>, dim3((unsigned)div_up_h(rows, 4)), dim3(256), 0, s, kv_len,
-                     o, part_o, part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys);
+                     o, part_o, part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys,
+                     32 * RB);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
+                    const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
+                    int force, hipStream_t s) {
+  const Plan p = plan(a);
+  if constexpr (D == 128) {
+    if (p.rb == 2)
+      return launch_rb<D, 2>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+  }
+  return launch_rb<D, 1>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
 }
 
 }  // namespace
