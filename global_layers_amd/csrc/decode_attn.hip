@@ -25,12 +25,18 @@ constexpr int kDecUnroll = 4;  // slots per slot group per iteration
 constexpr int kChansPerLane = 16;
 
 // Raw 16-channel slice of one cache row held in registers until it is used.
+// Lane `sub` of the LPS lanes sharing a slot holds the 16-byte pieces sub,
+// sub + LPS, sub + 2 LPS, ... of the row, so each load instruction of the
+// slot group covers one contiguous run of 16 LPS bytes (whole cache lines).
+// Channel of element i: chan(sub, i).
 template <typename T> struct Slice;
 template <> struct Slice<bf16> {
+  static constexpr int kPer = 8;  // channels per 16-byte piece
   u32x4 v[2];
-  DEVI void load(const bf16 *p) {
-    v[0] = ld16(p);
-    v[1] = ld16(p + 8);
+  template <int LPS> DEVI static int chan(int sub, int i) { return (i / 8) * 8 * LPS + 8 * sub + i % 8; }
+  template <int LPS> DEVI void load(const bf16 *row, int sub) {
+    v[0] = ld16(row + 8 * sub);
+    v[1] = ld16(row + 8 * LPS + 8 * sub);
   }
   DEVI void zero() { v[0] = v[1] = u32x4{0, 0, 0, 0}; }
   DEVI float get(int i) const {
@@ -40,9 +46,10 @@ template <> struct Slice<bf16> {
 };
 template <> struct Slice<float> {
   u32x4 v[4];
-  DEVI void load(const float *p) {
+  template <int LPS> DEVI static int chan(int sub, int i) { return (i / 4) * 4 * LPS + 4 * sub + i % 4; }
+  template <int LPS> DEVI void load(const float *row, int sub) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ld16(p + 4 * i);
+    for (int i = 0; i < 4; ++i) v[i] = ld16(row + 4 * LPS * i + 4 * sub);
   }
   DEVI void zero() {
 #pragma unroll
@@ -89,14 +96,14 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane % LPS;             // which 16-channel slice
   const int grp = wave * kGroupsPerWave + lane / LPS;
-  const int c0 = sub * kChansPerLane;
 
   float qv[GQ][kChansPerLane];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) {
-    const float *qp = q + ((size_t)b * a.H + h0 + g) * D + c0;
+    const float *qp = q + ((size_t)b * a.H + h0 + g) * D;
 #pragma unroll
-    for (int i = 0; i < kChansPerLane; ++i) qv[g][i] = qp[i] * kLog2e;
+    for (int i = 0; i < kChansPerLane; ++i)
+      qv[g][i] = qp[Slice<T>::template chan<LPS>(sub, i)] * kLog2e;
   }
   float m[GQ], l[GQ], acc[GQ][kChansPerLane];
 #pragma unroll
@@ -108,8 +115,8 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   }
 
   const size_t slot_stride = (size_t)a.Hk * D;
-  const T *kb = k_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D + c0;
-  const T *vb = v_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D + c0;
+  const T *kb = k_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D;
+  const T *vb = v_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D;
 
   for (int s_base = c_lo + grp; s_base <= c_hi; s_base += NG * kDecUnroll) {
     Slice<T> ks[kDecUnroll], vs[kDecUnroll];
@@ -120,8 +127,8 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
       const int s = s_base + u * NG;
       ok[u] = s <= c_hi;
       if (ok[u]) {
-        ks[u].load(kb + (size_t)s * slot_stride);
-        vs[u].load(vb + (size_t)s * slot_stride);
+        ks[u].template load<LPS>(kb + (size_t)s * slot_stride, sub);
+        vs[u].template load<LPS>(vb + (size_t)s * slot_stride, sub);
       } else {
         ks[u].zero();
         vs[u].zero();
@@ -187,7 +194,8 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
 #pragma unroll
-      for (int i = 0; i < kChansPerLane; ++i) red[wave][g][c0 + i] = acc[g][i];
+      for (int i = 0; i < kChansPerLane; ++i)
+        red[wave][g][Slice<T>::template chan<LPS>(sub, i)] = acc[g][i];
       if (lane == 0) {
         red[wave][g][D] = m[g];
         red[wave][g][D + 1] = l[g];
