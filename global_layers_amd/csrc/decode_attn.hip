@@ -15,6 +15,8 @@
 //  * A second kernel merges the chunks of each (row, head) the same way and
 //    divides by the total weight. Logits are in log2 units (q pre-scaled by
 //    log2 e), so every exponential is an exp2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -60,6 +62,24 @@ template <> struct Slice<float> {
     return __builtin_bit_cast(float, w);
   }
 };
+
+// Sum over aligned groups of n <= 16 lanes with DPP lane moves (no LDS
+// round trip): neighbour swap, pair swap, then mirrors inside 8 and 16 lanes.
+// Every step adds two operands in either order, so all lanes of a group end
+// with the same bits.
+template <int n> DEVI float group_sum_dpp(float v) {
+  static_assert(n == 1 || n == 2 || n == 4 || n == 8 || n == 16, "group of at most 16 lanes");
+  auto mv = [](float x, auto ctrl) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value, 0xF,
+                                        0xF, true));
+  };
+  if constexpr (n >= 2) v += mv(v, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
+  if constexpr (n >= 4) v += mv(v, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
+  if constexpr (n >= 8) v += mv(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (n >= 16) v += mv(v, std::integral_constant<int, 0x140>{}); // row_mirror
+  return v;
+}
 
 DEVI void row_range(const int32_t *pos, int b, int S, int local, int window, int &lo, int &hi) {
   const int p = pos[b];
@@ -142,7 +162,7 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
         float d = 0.f;
 #pragma unroll
         for (int i = 0; i < kChansPerLane; ++i) d = fmaf(qv[g][i], ks[u].get(i), d);
-        d = group_sum<LPS>(d);
+        d = group_sum_dpp<LPS>(d);
         x[u][g] = ok[u] ? d : -INFINITY;
       }
 #pragma unroll
@@ -151,14 +171,14 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) mx = fmaxf(mx, x[u][g]);
       // slot s_base is valid, so mx is finite
-      const float corr = exp2f(m[g] - mx);
+      const float corr = __builtin_amdgcn_exp2f(m[g] - mx);
       m[g] = mx;
       l[g] *= corr;
 #pragma unroll
       for (int i = 0; i < kChansPerLane; ++i) acc[g][i] *= corr;
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) {
-        x[u][g] = exp2f(x[u][g] - mx);
+        x[u][g] = __builtin_amdgcn_exp2f(x[u][g] - mx);
         l[g] += x[u][g];
       }
     }
@@ -227,7 +247,7 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
 
 // grid: x = H, y = B; D threads. Chunk weights exp2(m_j - M) are formed once
 // per block in LDS; each thread then sums its channel over the chunks.
-constexpr int kMaxChunks = 64;  // decode_chunk keeps every row at <= 64 chunks
+constexpr int kMaxChunks = 128;  // decode_chunk keeps every row at <= 128 chunks
 
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
@@ -317,10 +337,11 @@ __global__ void splitk_reduce(const float *__restrict__ part, int ksplit, T *__r
 int decode_chunk(int local, int window, int S, int d_h) {
   (void)d_h;
   // local: short chunks so the W slots still spread over many workgroups;
-  // global: at most 64 chunks per row (long streams per workgroup, cheap combine)
+  // global: at most 128 chunks per row, so no workgroup streams for long
+  // after the others (a shorter tail) while the combine stays cheap
   const int range = local && window < S ? window : S;
-  int c = local ? 64 : 256;
-  while (div_up_h(range, c) > 64) c *= 2;
+  int c = local ? 64 : 256;  // a workgroup covers 16 slot groups x kDecUnroll slots per pass
+  while (div_up_h(range, c) > kMaxChunks) c *= 2;
   return c;
 }
 
