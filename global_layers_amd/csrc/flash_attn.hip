@@ -733,7 +733,8 @@ Plan plan(const AttnArgs &a) {
   Plan p;
   const int G = a.H / a.Hk;
   p.gp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  p.rb = (a.d_h == 128 && !a.local) ? 2 : 1;
+  // a window covering every key is the global layer: same plan, same bits
+  p.rb = (a.d_h == 128 && (!a.local || a.window >= a.T)) ? 2 : 1;
   const int TQ = 32 * p.rb * (4 / p.gp);
   p.n_qtiles = div_up_h(a.T, TQ);
   p.n_hgrp = G / p.gp;

@@ -221,8 +221,9 @@ def test_cfg4_sampled_rows(gpu_lib):
 
 
 # ---------------------------------------------------------------- structure
-def test_window_at_least_T_is_bitwise_global(gpu_lib):
-    B, T, D, H, Hk, d_h = 1, 600, 128, 4, 1, 256
+@pytest.mark.parametrize("d_h", [128, 256])
+def test_window_at_least_T_is_bitwise_global(gpu_lib, d_h):
+    B, T, D, H, Hk = 1, 600, 128, 4, 1
     inp = small_prefill_inputs(4, B, T, D, H, Hk, d_h, "bf16")
     yg = gpu_prefill(gpu_lib, inp, _kw(H, Hk, d_h, G, 0))
     for Wn in (T, T + 1, 1 << 20):
