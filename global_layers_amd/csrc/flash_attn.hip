@@ -663,59 +663,77 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 }
 
 // Merge the key chunks of query tiles that had more than one:
-// o = sum_j 2^(m_j - M) l_j o_j / sum_j 2^(m_j - M) l_j. One wave per output
-// row (b, h, t); rows whose query tile had a single chunk were written by the
-// attention kernel and are skipped.
+// o = sum_j 2^(m_j - M) l_j o_j / sum_j 2^(m_j - M) l_j. kCombineSlices
+// workgroups per query tile (blockIdx.x in the attention kernel's base
+// order); tiles with a single chunk were written by the attention kernel and
+// exit at once. A thread handles 8 channels of a row per item: every chunk's
+// 16-byte piece of the item is loaded before any arithmetic, several items
+// at a time.
+constexpr int kCombineItems = 2;   // items in flight per thread
+constexpr int kCombineSlices = 8;  // workgroups per query tile
+
 template <int D>
 __global__ void __launch_bounds__(256)
 flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
               const bf16 *__restrict__ part_o, const float *__restrict__ part_ml, AttnArgs a,
               int gp, int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int rpw) {
-  constexpr int kPer = D / 64;  // channels per lane
-  const int lane = threadIdx.x & 63;
-  const long row_id = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // over B*H*T
-  if (row_id >= (long)a.B * a.H * a.T) return;
-  const int t = (int)(row_id % a.T);
-  const int h = (int)((row_id / a.T) % a.H);
-  const int b = (int)(row_id / ((long)a.T * a.H));
+  const Geo geo = geometry(a, kv_len, blockIdx.x, gp, n_qtiles, n_hgrp, chunk_keys, rpw);
+  if (geo.n_active <= 1) return;  // uniform per block
+  constexpr int kC8 = D / 8;  // 8-channel pieces per row
   const int G = a.H / a.Hk;
-  const int kh = h / G, hgrp = (h % G) / gp;
-  const int qt = t / (rpw * (4 / gp));
-  const int base_id = ((b * a.Hk + kh) * n_hgrp + hgrp) * n_qtiles + (n_qtiles - 1 - qt);
-  const Geo geo = geometry(a, kv_len, base_id, gp, n_qtiles, n_hgrp, chunk_keys, rpw);
-  if (geo.n_active <= 1) return;
-
-  // every load of the row is issued before any arithmetic (n_active <= 8)
-  float mj[8], lj[8], oj[8][kPer];
+  const int h0 = geo.kh * G + geo.hgrp * gp;
+  const int nt = geo.t_hi - geo.t_lo;
+  const int n_items = gp * nt * kC8;
+  const int na = geo.n_active;
+  for (int base = blockIdx.y * 256 + threadIdx.x; base < n_items;
+       base += 256 * kCombineSlices * kCombineItems) {
+    float w[kCombineItems][8];
+    u32x4 v[kCombineItems][8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    mj[j] = -INFINITY;
-    lj[j] = 0.f;
+    for (int u = 0; u < kCombineItems; ++u) {
+      const int item = base + 256 * kCombineSlices * u;
+      const bool ok = item < n_items;
+      const int c8 = item % kC8, r = item / kC8;
+      const int h = h0 + r / nt, t = geo.t_lo + r % nt;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) oj[j][i] = 0.f;
-    if (j < geo.n_active) {
-      const size_t row = (((size_t)j * a.B + b) * a.H + h) * a.T + t;
-      mj[j] = part_ml[2 * row];
-      lj[j] = part_ml[2 * row + 1];
+      for (int j = 0; j < 8; ++j) {
+        w[u][j] = -INFINITY;
+        v[u][j] = u32x4{0, 0, 0, 0};
+        if (ok && j < na) {
+          const size_t row = (((size_t)j * a.B + geo.b) * a.H + h) * a.T + t;
+          w[u][j] = part_ml[2 * row];  // m_j for now
+          v[u][j] = *reinterpret_cast<const u32x4 *>(part_o + row * D + 8 * c8);
+        }
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) oj[j][i] = (float)part_o[row * D + lane * kPer + i];
+    for (int u = 0; u < kCombineItems; ++u) {
+      const int item = base + 256 * kCombineSlices * u;
+      if (item >= n_items) break;
+      const int c8 = item % kC8, r = item / kC8;
+      const int h = h0 + r / nt, t = geo.t_lo + r % nt;
+      float M = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, w[u][j]);
+      const float mu = M == -INFINITY ? 0.f : M;
+      float num[8] = {}, den = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= na) break;
+        const size_t row = (((size_t)j * a.B + geo.b) * a.H + h) * a.T + t;
+        const float wl = exp2f(w[u][j] - mu) * part_ml[2 * row + 1];
+        den += wl;
+        const bf16x8 pv = __builtin_bit_cast(bf16x8, v[u][j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) num[i] = fmaf(wl, (float)pv[i], num[i]);
+      }
+      bf16x8 out;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = (bf16)(den > 0.f ? num[i] / den : 0.f);
+      *reinterpret_cast<bf16x8 *>(o + ((size_t)geo.b * a.T + t) * ((size_t)a.H * D) +
+                                  (size_t)h * D + 8 * c8) = out;
     }
   }
-  float M = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) M = fmaxf(M, mj[j]);
-  const float mu = M == -INFINITY ? 0.f : M;
-  float num[kPer] = {}, den = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float wl = j < geo.n_active ? exp2f(mj[j] - mu) * lj[j] : 0.f;
-    den += wl;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) num[i] = fmaf(wl, oj[j][i], num[i]);
-  }
-  bf16 *op = o + ((size_t)b * a.T + t) * ((size_t)a.H * D) + (size_t)h * D + lane * kPer;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) op[i] = (bf16)(den > 0.f ? num[i] / den : 0.f);
 }
 
 struct Plan {
@@ -725,7 +743,8 @@ struct Plan {
 
 // Planning constants (units: one 64-key tile of one workgroup, about 1.8 us
 // on the 1B shape). A workgroup's prologue (Q, first K/V tiles, reference)
-// costs about 2.5 tiles; merging split rows afterwards about 8.
+// costs about 2.5 tiles; a split adds the merge launch and its reads, about
+// 8 (measured: splitting the 1B-shaped local layer in two is slower).
 constexpr double kPrologueTiles = 2.5, kMergeTiles = 8.0;
 constexpr int kCUs = 256;  // MI355X compute units; one 131 KB-LDS workgroup each
 
@@ -791,8 +810,8 @@ hipError_t launch_rb(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t
                      force);
   e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
-  const long rows = (long)a.B * a.H * a.T;
-  hipLaunchKernelGGL(flash_combine<D>, dim3((unsigned)div_up_h(rows, 4)), dim3(256), 0, s, kv_len,
+  hipLaunchKernelGGL(flash_combine<D>, dim3((unsigned)p.n_base, kCombineSlices), dim3(256), 0, s,
+                     kv_len,
                      o, part_o, part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys,
                      32 * RB);
   return hipGetLastError();
