@@ -273,11 +273,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                lds0 + 4 * Cfg::kKHalfBytes + buf * Cfg::kVTileBytes + (wu + 4 * i) * 1024);
   };
 
-  // max_c |1 + gamma_k[c]| (bounds the key norms, below); its loads overlap
-  // the first tile loads
-  float gmax = 0.f;
-  for (int c = tid; c < D; c += kThreads) gmax = fmaxf(gmax, fabsf(1.f + (float)gamma_k[c]));
-
   auto issue_prologue = [&]() {  // K halves 0, 1, 2 (slots 0-2) and V tile 0
     if (n_tiles <= 0) return;
 #pragma unroll
@@ -288,6 +283,10 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(0, 0, i);
   };
   issue_prologue();
+  // max_c |1 + gamma_k[c]| (bounds the key norms, below); its loads, the Q
+  // fragments and the first tiles are in flight together
+  float gmax = 0.f;
+  for (int c = tid; c < D; c += kThreads) gmax = fmaxf(gmax, fabsf(1.f + (float)gamma_k[c]));
   // Every outstanding load (Q fragments, first tiles) lands before the loop,
   // so inside it only the newest prefetches are ever pending.
   publish_tiles();
@@ -633,23 +632,19 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
   run(s0_first);
 
-  // Normalise; write the output rows (single chunk) or partials (several chunks).
+  // Normalise; write the output rows (single chunk) or partials (several
+  // chunks). The K/V buffers are free after the last tile's barrier: each wave
+  // stages a 32-row block (bf16, a 16-byte pad per row) in a region of its
+  // own, then writes it back as whole rows of 16-byte pieces. A lane holds
+  // channels 32 db + 8 g + 4 hh + [0, 4) of its row.
+  constexpr int kPitch = 2 * D + 16;
+  static_assert(4 * 32 * kPitch <= Cfg::kLdsBytes, "output staging fits the tile buffers");
+  char *stage = lds + w * 32 * kPitch;
+  constexpr int kPieces16 = D / 8;  // 16-byte pieces per row
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, kWave);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_t[rb] >= a.T) continue;
-    bf16 *op;
-    if (geo.n_active == 1) {
-      op = o + ((size_t)b * a.T + my_t[rb]) * ((size_t)a.H * D) + (size_t)h * D;
-    } else {
-      const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t[rb];
-      op = part_o + row * D;
-      if (hh == 0) {
-        part_ml[2 * row] = m_ref[rb];
-        part_ml[2 * row + 1] = l_tot;
-      }
-    }
 #pragma unroll
     for (int db = 0; db < Cfg::kDB; ++db)
 #pragma unroll
@@ -657,8 +652,27 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc_o[rb][db][4 * g + r] * inv);
-        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * hh) = v;
+        *reinterpret_cast<bf16x4 *>(stage + col * kPitch + 2 * (32 * db + 8 * g + 4 * hh)) = v;
       }
+    if (geo.n_active > 1 && hh == 0 && my_t[rb] < a.T) {
+      const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t[rb];
+      part_ml[2 * row] = m_ref[rb];
+      part_ml[2 * row + 1] = l_tot;
+    }
+    // the same wave reads its region back (LDS keeps a wave's accesses in
+    // order), and the next block's writes come after these reads
+#pragma unroll
+    for (int i = 0; i < 32 * kPieces16 / kWave; ++i) {
+      const int item = i * kWave + lane;
+      const int r = item / kPieces16, c = item % kPieces16;
+      const int t = wq0 + 32 * rb + r;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + 16 * c);
+      if (t >= a.T) continue;
+      bf16 *dst = geo.n_active == 1
+                      ? o + ((size_t)b * a.T + t) * ((size_t)a.H * D) + (size_t)h * D
+                      : part_o + ((((size_t)split * a.B + b) * a.H + h) * a.T + t) * D;
+      *reinterpret_cast<u32x4 *>(dst + 8 * c) = v;
+    }
   }
 }
 
