@@ -71,6 +71,8 @@ template <int kChunks> DEVI int gemm_swz(int r) {
 // Row pitch (bytes) of the bf16 C tile staged in LDS by the fused epilogue:
 // an 8-byte pad per row spreads a column of 8-byte writes over all banks.
 template <int BN> constexpr int qkv_tile_pitch() { return BN * 2 + 8; }
+// The plain epilogue reads its staged tile back in 16-byte pieces: a 16-byte pad.
+template <int BN> constexpr int plain_tile_pitch() { return BN * 2 + 16; }
 
 // Fused epilogue of the QKV projection ("QK-Norm", How it works; "Gemma 3
 // Attention Block", How it works): the BM x 256 tile, rounded to bf16 as the
@@ -368,26 +370,40 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
     return;
   }
   // acc[i][j] holds D[n][m]: lane column m = lane % 32, rows n = 8g + 4h + r.
+  // The bf16 tile is staged in LDS (the k-loop stages are free once every
+  // wave has passed the barrier below) and written back as whole rows of
+  // 16-byte pieces.
+  constexpr int kPitch = plain_tile_pitch<BN>();
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < Cfg::kFM; ++i) {
-    const int gm = m0 + wm * Cfg::kWaveM + i * 32 + lrow;
-    if (gm >= M) continue;
+  for (int i = 0; i < Cfg::kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::kFN; ++j) {
+    for (int j = 0; j < Cfg::kFN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int gn = n0 + wn * Cfg::kWaveN + j * 32 + 8 * g + 4 * hh;
+        const int row = wm * Cfg::kWaveM + i * 32 + lrow;
+        const int c = wn * Cfg::kWaveN + j * 32 + 8 * g + 4 * hh;
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][g * 4 + r];
-        if (gn + 3 < N) {
-          *reinterpret_cast<bf16x4 *>(C + (size_t)gm * ldc + gn) = v;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (gn + r < N) C[(size_t)gm * ldc + gn + r] = v[r];
-        }
+        *reinterpret_cast<bf16x4 *>(lds + row * kPitch + c * 2) = v;
       }
+  __syncthreads();
+  constexpr int kP16 = BN / 8;  // 16-byte pieces per tile row
+#pragma unroll 4
+  for (int item = tid; item < BM * kP16; item += Cfg::kThreads) {
+    const int row = item / kP16, c = item % kP16;
+    const int gm = m0 + row, gn = n0 + 8 * c;
+    if (gm >= M || gn >= N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * kPitch + 16 * c);
+    bf16 *dst = C + (size_t)gm * ldc + gn;
+    if (gn + 7 < N && (((uintptr_t)dst) & 15) == 0) {
+      *reinterpret_cast<u32x4 *>(dst) = v;
+    } else {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        if (gn + x < N) dst[x] = h[x];
     }
   }
 }
@@ -409,7 +425,7 @@ hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf
   using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
   const int tm = div_up_h(M, BM), tn = div_up_h(N, BN);
   auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST, kQkv>;
-  constexpr int kTileLds = kQkv ? BM * qkv_tile_pitch<BN>() : 0;
+  constexpr int kTileLds = kQkv ? BM * qkv_tile_pitch<BN>() : BM * plain_tile_pitch<BN>();
   constexpr int kLds = Cfg::kLdsBytes > kTileLds ? Cfg::kLdsBytes : kTileLds;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
