@@ -63,24 +63,6 @@ template <> struct Slice<float> {
   }
 };
 
-// Sum over aligned groups of n <= 16 lanes with DPP lane moves (no LDS
-// round trip): neighbour swap, pair swap, then mirrors inside 8 and 16 lanes.
-// Every step adds two operands in either order, so all lanes of a group end
-// with the same bits.
-template <int n> DEVI float group_sum_dpp(float v) {
-  static_assert(n == 1 || n == 2 || n == 4 || n == 8 || n == 16, "group of at most 16 lanes");
-  auto mv = [](float x, auto ctrl) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value, 0xF,
-                                        0xF, true));
-  };
-  if constexpr (n >= 2) v += mv(v, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
-  if constexpr (n >= 4) v += mv(v, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
-  if constexpr (n >= 8) v += mv(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
-  if constexpr (n >= 16) v += mv(v, std::integral_constant<int, 0x140>{}); // row_mirror
-  return v;
-}
-
 DEVI void row_range(const int32_t *pos, int b, int S, int local, int window, int &lo, int &hi) {
   const int p = pos[b];
   if (p < 0 || p >= S) {

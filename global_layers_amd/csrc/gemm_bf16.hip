@@ -128,12 +128,16 @@ DEVI void qkv_epilogue_impl(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, in
     const float mul = kind == 0 ? ep.alpha : 1.f;
     float g1[8], g2[8];
     double f[8];
+    // f_i = theta^(-2i/d_h) / (2 pi scale): one fp64 exp2 for f_i0, then the
+    // ratio theta^(-2/d_h) for the next seven (relative error ~1e-15)
     const double l2t = log2(ep.theta), rev_scale = 1.0 / (6.283185307179586476925286766559 * ep.scale);
+    const double step = exp2(-2.0 / (double)d_h * l2t);
+    f[0] = exp2(-2.0 * (double)i0 / (double)d_h * l2t) * rev_scale;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       g1[x] = (1.f + (float)gam[i0 + x]) * mul;
       g2[x] = (1.f + (float)gam[half + i0 + x]) * mul;
-      f[x] = exp2(-2.0 * (double)(i0 + x) / (double)d_h * l2t) * rev_scale;
+      if (x > 0) f[x] = f[x - 1] * step;
     }
     const int head = head0 + hv;
     constexpr int kRowsPerPass = kThreads / 16;
@@ -150,7 +154,8 @@ DEVI void qkv_epilogue_impl(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, in
         x2[x] = (float)v[x];
         ss += x1[x] * x1[x] + x2[x] * x2[x];
       }
-      for (int o = lpv / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+      ss = d_h == 256 ? group_sum_dpp<16>(ss) : d_h == 128 ? group_sum_dpp<8>(ss)
+                                                         : group_sum_dpp<4>(ss);
       if (!ok) continue;
       const float r = rsqrtf(ss / (float)d_h + 1e-6f);
       const int b = m / T, t = m - b * T;
