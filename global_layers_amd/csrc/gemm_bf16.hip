@@ -444,62 +444,80 @@ hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf
 // Decode projections: P[split][m][n] = sum_{k in split} A[m][k] * W[n][k]
 // ---------------------------------------------------------------------------
 constexpr int kGemvWaves = 4;
-constexpr int kGemvUnroll = 8;  // weight loads a wave keeps in flight (1 KB each)
+constexpr int kGemvNB = 4;      // 16-column blocks per workgroup (one activation load feeds 4)
+constexpr int kGemvUnroll = 8;  // k-steps a wave keeps in flight (5 KB of loads each)
 
-// One workgroup = one 16-column block over one K split; its 4 waves take
+// One workgroup = kGemvNB 16-column blocks over one K split; its 4 waves take
 // consecutive quarters of the split's 32-wide k-steps and add their 16 x 16
 // accumulators through LDS, so the split count (and the partial traffic)
-// stays small while every CU still streams from many waves.
+// stays small while every CU still streams from many waves. Each activation
+// fragment feeds kGemvNB MFMAs, so nearly all load traffic is weights.
 __global__ void __launch_bounds__(kGemvWaves * 64)
 gemv16_bf16_splitk(const bf16 *__restrict__ A, const bf16 *__restrict__ W0,
                    const bf16 *__restrict__ W1, int N0, float *__restrict__ P, int M, int N, int K,
                    int k_per_split) {
-  __shared__ f32x4 red[kGemvWaves][64];
+  __shared__ f32x4 red[kGemvWaves][kGemvNB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nb = blockIdx.x;  // 16-column block
+  const int nb = blockIdx.x;  // group of kGemvNB 16-column blocks
   const int split = blockIdx.y, mb = blockIdx.z;
-  const int n = nb * 16 + (lane & 15);
   const int m = mb * 16 + (lane & 15);
   const int koff = (lane >> 4) * 8;
   const int steps = k_per_split / 32;
   const int per_wave = div_up(steps, kGemvWaves);
   const int k_begin = split * k_per_split + wave * per_wave * 32;
   const int k_end = min(split * k_per_split + k_per_split, k_begin + per_wave * 32);
-  const bool n_ok = n < N, m_ok = m < M;
-  const int nn = n_ok ? n : 0;
-  const bf16 *wp = (nn < N0 ? W0 + (size_t)nn * K : W1 + (size_t)(nn - N0) * K) + koff;
+  const bool m_ok = m < M;
   const bf16 *ap = A + (size_t)(m_ok ? m : 0) * K + koff;
+  // a group never straddles N0 (the caller keeps N0 a multiple of 16 kGemvNB)
+  const bf16 *wp[kGemvNB];
+  bool n_ok[kGemvNB];
+#pragma unroll
+  for (int j = 0; j < kGemvNB; ++j) {
+    const int n = (nb * kGemvNB + j) * 16 + (lane & 15);
+    n_ok[j] = n < N;
+    const int nn = n_ok[j] ? n : 0;
+    wp[j] = (nn < N0 ? W0 + (size_t)nn * K : W1 + (size_t)(nn - N0) * K) + koff;
+  }
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[kGemvNB];
+#pragma unroll
+  for (int j = 0; j < kGemvNB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = k_begin; k < k_end; k += 32 * kGemvUnroll) {
-    u32x4 wv[kGemvUnroll], av[kGemvUnroll];
+    u32x4 wv[kGemvUnroll][kGemvNB], av[kGemvUnroll];
     // every load of the round is in flight before the first MFMA; steps past
     // the range contribute zero operands
 #pragma unroll
     for (int u = 0; u < kGemvUnroll; ++u) {
       const int kk = k + u * 32;
       const bool ok = kk < k_end;
-      wv[u] = ok && n_ok ? ld16(wp + kk) : u32x4{0, 0, 0, 0};
       av[u] = ok && m_ok ? ld16(ap + kk) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < kGemvNB; ++j)
+        wv[u][j] = ok && n_ok[j] ? ld16(wp[j] + kk) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < kGemvUnroll; ++u)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                     __builtin_bit_cast(bf16x8, wv[u]), acc,
-                                                     0, 0, 0);
-  }
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
 #pragma unroll
-  for (int w = 1; w < kGemvWaves; ++w) acc += red[w][lane];
+      for (int j = 0; j < kGemvNB; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                         __builtin_bit_cast(bf16x8, wv[u][j]),
+                                                         acc[j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kGemvNB; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();
+  // wave w finishes column block w (kGemvNB == kGemvWaves)
+  static_assert(kGemvNB == kGemvWaves, "one column block per finishing wave");
+  f32x4 sum = red[0][wave][lane];
+#pragma unroll
+  for (int w = 1; w < kGemvWaves; ++w) sum += red[w][wave][lane];
   // D[m][n]: lane column n = lane % 16, rows m = (lane / 16) * 4 + r.
-  const int col = nb * 16 + (lane & 15);
+  const int col = (nb * kGemvNB + wave) * 16 + (lane & 15);
   if (col >= N) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = mb * 16 + (lane >> 4) * 4 + r;
-    if (row < M) P[((size_t)split * M + row) * N + col] = acc[r];
+    if (row < M) P[((size_t)split * M + row) * N + col] = sum[r];
   }
 }
 
@@ -545,17 +563,19 @@ hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_k
 }
 
 int gemv_ksplit(int N, int K) {
-  // about 12+ waves per CU in flight (4 per workgroup), K splits of whole k-steps
-  const long nblk = div_up_h(N, 16);
+  // about 6+ waves per CU in flight (4 per workgroup, up to 40 KB of loads each), K
+  // splits of whole k-steps; more splits cost more partial traffic than they gain
+  const long nblk = div_up_h(N, 16 * kGemvNB);
   int s = 1;
-  while (s < 16 && nblk * s * kGemvWaves < 3072) s *= 2;
+  while (s < 16 && nblk * s * kGemvWaves < 1536) s *= 2;
   while (s > 1 && (K / 32) % s != 0) s /= 2;
   return s;
 }
 
 hipError_t launch_gemv16_bf16(const bf16 *A, const bf16 *W0, const bf16 *W1, int N0, float *P,
                               int M, int N, int K, int ksplit, hipStream_t s) {
-  dim3 grid(div_up_h(N, 16), ksplit, div_up_h(M, 16));
+  if (N0 < N && N0 % (16 * kGemvNB) != 0) return hipErrorInvalidValue;
+  dim3 grid(div_up_h(N, 16 * kGemvNB), ksplit, div_up_h(M, 16));
   hipLaunchKernelGGL(gemv16_bf16_splitk, grid, dim3(kGemvWaves * 64), 0, s, A, W0, W1, N0, P, M,
                      N, K, K / ksplit);
   return hipGetLastError();
