@@ -7,9 +7,10 @@
 //  * Blocked logits get exactly zero weight, as K_MASK does in fp32 whenever a
 //    row has an allowed key; the fill value itself is never formed. Tiles that
 //    no row of the workgroup may see are never visited.
-//  * One workgroup = 4 waves = 128 query rows of one KV head: the query heads
-//    of a GQA group (up to 4) are packed into the workgroup, so each K/V tile
-//    staged in LDS feeds every query head that reads it.
+//  * One workgroup = 4 waves = 128 query rows (256 when each wave owns two
+//    32-row blocks) of one KV head: the query heads of a GQA group (up to 4)
+//    are packed into the workgroup, so each K/V tile staged in LDS feeds every
+//    query head that reads it.
 //  * Each wave computes S^T = K Q^T with 32x32x16 bf16 MFMAs: a lane owns one
 //    query row and 32 of the 64 keys of a tile. K rows are fed in the
 //    permuted order kappa(i) so that the S^T accumulators of a lane are, in
@@ -25,9 +26,9 @@
 //  * Tiles move global -> LDS with direct loads (16 bytes per lane, no
 //    staging registers) into XOR-swizzled, unpadded layouts that keep the
 //    fragment reads free of bank conflicts. Each 64-key tile runs as two
-//    32-key half-steps; the S MFMAs of the next half overlap the softmax and
-//    PV of this one, in a software pipeline of 4-MFMA groups. K sits in four
-//    32-key slots and V^T in two tile buffers; one barrier per tile.
+//    32-key halves in one fixed sequence of 4-MFMA groups; the S MFMAs of the
+//    next half overlap the softmax and PV of this one. K sits in four 32-key
+//    slots and V^T in two tile buffers; one barrier per tile.
 //  * Split-KV: when (rows x heads) give too few workgroups to fill the chip,
 //    the key range of each query tile is cut into chunks handled by separate
 //    workgroups; a query tile with several chunks writes normalised partial

@@ -529,12 +529,13 @@ hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, in
   // (measured best among 4/8 waves, BK 32/64, 2-4 stages on the 4B and 27B
   // projection shapes). Pick the tile by a rounds x tile-cost model: a launch runs in rounds of
   // 256 workgroups (one per CU); bigger tiles reuse operands better
-  // (relative per-output efficiency 1.0 / 0.9 / 0.75).
+  // (relative per-output efficiency 1.0 / 0.9 / 0.75 / 0.8; 128x192 lets a
+  // 1152-wide output fill whole tiles).
   struct Opt { int bm, bn; double eff; };
-  const Opt opts[3] = {{256, 256, 1.0}, {128, 256, 0.9}, {128, 128, 0.75}};
+  const Opt opts[4] = {{256, 256, 1.0}, {128, 256, 0.9}, {128, 128, 0.75}, {128, 192, 0.8}};
   int best = 0;
   double best_cost = 1e300;
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const long tiles = (long)div_up_h(M, opts[i].bm) * div_up_h(N, opts[i].bn);
     const double cost = (double)div_up_h(tiles, 256) * opts[i].bm * opts[i].bn / opts[i].eff;
     if (cost < best_cost) {
@@ -545,7 +546,8 @@ hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, in
   switch (best) {
     case 0: return launch_gemm<256, 256, 2, 4, 64, 2>(A, B0, B1, N0, C, M, N, K, s);
     case 1: return launch_gemm<128, 256, 2, 4, 64, 3>(A, B0, B1, N0, C, M, N, K, s);
-    default: return launch_gemm<128, 128, 2, 2, 64, 3>(A, B0, B1, N0, C, M, N, K, s);
+    case 2: return launch_gemm<128, 128, 2, 2, 64, 3>(A, B0, B1, N0, C, M, N, K, s);
+    default: return launch_gemm<128, 192, 4, 2, 64, 3>(A, B0, B1, N0, C, M, N, K, s);
   }
 }
 
