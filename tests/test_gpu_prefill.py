@@ -189,6 +189,18 @@ def test_cfg2_full_both_layers(gpu_lib):
         assert_bf16_close(f64(y), oracle_prefill(inp, kw), f"cfg2 layer {li} y")
 
 
+def test_output_projection_on_192_wide_tiles(gpu_lib):
+    """An 1152-wide output (the 1B-shaped output projection) runs on 128x192
+    GEMM tiles; at T = 4000 the last row tile is ragged. Rows from the first,
+    middle and last row tiles against the oracle."""
+    B, T, D, H, Hk, d_h = 1, 4000, 1152, 4, 1, 256
+    inp = small_prefill_inputs(11, B, T, D, H, Hk, d_h, "bf16")
+    kw = _kw(H, Hk, d_h, G, 0, theta=1e6, scale=8.0)
+    y = f64(gpu_prefill(gpu_lib, inp, kw))
+    rows = [0, 1, 127, 128, 2047, 3967, 3968, 3990, 3999]
+    assert_bf16_close(y[:, rows], oracle_prefill(inp, kw, rows=rows), "y")
+
+
 def _sampled(gpu_lib, w, layer_ids, rows):
     x_cache = None
     for li in layer_ids:
