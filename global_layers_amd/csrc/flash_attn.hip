@@ -212,17 +212,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) my_t[rb] = wq0 + 32 * rb + col;
 
-  // Q^T fragments (B operand): query my_t, channels 16 ks + 8 hh + [0, 8).
-  bf16x8 qf[kRB][Cfg::kKS];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const bool ok = my_t[rb] < a.T;
-    const bf16 *qp = q + (((size_t)b * a.H + h) * a.T + (ok ? my_t[rb] : 0)) * D + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < Cfg::kKS; ++ks)
-      qf[rb][ks] = ok ? *reinterpret_cast<const bf16x8 *>(qp + 16 * ks) : bf16x8{};
-  }
-
   f32x16 acc_o[kRB][Cfg::kDB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb)
@@ -283,7 +272,20 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int i = 0; i < Cfg::kVLoads; ++i) issue_v_piece(0, 0, i);
   };
+  // The first tiles go out before the Q fragments: the fragment selects below
+  // wait for the Q data, and the tiles' loads then already overlap them.
   issue_prologue();
+  // Q^T fragments (B operand): query my_t, channels 16 ks + 8 hh + [0, 8).
+  bf16x8 qf[kRB][Cfg::kKS];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const bool ok = my_t[rb] < a.T;
+    const bf16 *qp = q + (((size_t)b * a.H + h) * a.T + (ok ? my_t[rb] : 0)) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::kKS; ++ks)
+      qf[rb][ks] = ok ? *reinterpret_cast<const bf16x8 *>(qp + 16 * ks) : bf16x8{};
+  }
+
   // max_c |1 + gamma_k[c]| (bounds the key norms, below); its loads, the Q
   // fragments and the first tiles are in flight together
   float gmax = 0.f;

@@ -244,6 +244,43 @@ def test_window_at_least_T_is_bitwise_global(gpu_lib, d_h):
     assert not torch.equal(gpu_prefill(gpu_lib, inp, _kw(H, Hk, d_h, L, T - 1)), yg)
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("t,Wn", [(L, 600), (G, 0)])
+def test_split_merge_on_reused_workspace(gpu_lib, fused, t, Wn):
+    """Key ranges split over workgroups and merged. One workspace, first filled
+    with 0xFF bytes, serves calls with different inputs (the QK-norm stage
+    fused into the projection, or run as its own kernel): every call must
+    merge its own partials, so a stale partial from an earlier call, or one
+    left unwritten, shows as an O(1) error or a NaN. The attention stage alone
+    then runs twice more on the last inputs and must repeat its output."""
+    B, T, D, H, Hk, d_h = 1, 1000, 1024, 4, 1, 256
+    kw = _kw(H, Hk, d_h, t, Wn, theta=1e6 if t == G else 1e4, scale=8.0 if t == G else 1.0)
+    desc = gpu_lib.make_desc(B=B, T=T, D=D, dtype=torch.bfloat16, **kw)
+    assert gpu_lib.workspace_layout(desc).attn_part != 0, "this shape should split key ranges"
+    ws = gpu_lib.new_workspace(desc)
+    ws.fill_(0xFF)
+    for seed in (21, 22, 23):
+        log(f"seed {seed} fused {fused} {t}")
+        inp = small_prefill_inputs(seed, B, T, D, H, Hk, d_h, "bf16", (T - 37 * (seed - 21),))
+        d = to_dev(inp)
+        args = (d["x"], d["segment_pos"], weights_of(d))
+        if fused:
+            y = gpu_lib.prefill(*args, kv_valid_len=d["kv_valid_len"], workspace=ws, **kw)
+        else:
+            for st in (gpu_lib.STAGE_QKV_PROJ, gpu_lib.STAGE_QK_NORM):
+                gpu_lib.prefill(*args, kv_valid_len=d["kv_valid_len"], workspace=ws, stages=st,
+                                **kw)
+            y = gpu_lib.prefill(*args, kv_valid_len=d["kv_valid_len"], workspace=ws,
+                                stages=gpu_lib.STAGE_ATTN | gpu_lib.STAGE_OUT_PROJ, **kw)
+        torch.cuda.synchronize()
+        assert_bf16_close(f64(y), oracle_prefill(inp, kw), f"y seed {seed}")
+    for _ in range(2):
+        y2 = gpu_lib.prefill(*args, kv_valid_len=d["kv_valid_len"], workspace=ws,
+                             stages=gpu_lib.STAGE_ATTN | gpu_lib.STAGE_OUT_PROJ, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y)
+
+
 def _attn_core_only(gpu_lib, inp, kw):
     d = to_dev(inp)
     B, T, D = d["x"].shape
