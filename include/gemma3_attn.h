@@ -28,9 +28,11 @@
  *     sits at pos_b = segment_pos[b] and its rotated key and its value are
  *     written to slot pos_b before attending to slots s <= pos_b (and
  *     s > pos_b - W on local layers).
- *   - A row with no allowed key (unreachable with causal masks: key t itself,
- *     or key 0, is always allowed unless kv_valid_len[b] == 0) outputs 0
- *     instead of the fill-value result (uniform mean over all keys).
+ *   - A row with no allowed key outputs 0 instead of the fill-value result
+ *     (uniform mean over all keys). Causal masking alone never produces one
+ *     (key t is allowed); padding does when kv_valid_len[b] == 0, or on a
+ *     local layer for rows t >= kv_valid_len[b] + W - 1 (a padded tail
+ *     longer than the window).
  *
  * Layouts (all row-major, element type per desc.dtype):
  *   x            [B, T, D]

@@ -36,6 +36,9 @@ SMALL_BF16 = [
     # few workgroups: key ranges split over several workgroups, then merged
     (1, 1000, 512, 4, 1, 128, L, 600, (900,)),
     (1, 1500, 256, 2, 1, 64, G, 0, None),
+    # split work where one workgroup runs the end of one query tile and the
+    # start of the next (across the two batch rows too), with padding
+    (2, 1500, 1024, 4, 1, 256, G, 0, (1500, 1100)),
 ]
 
 
@@ -77,6 +80,7 @@ EXACT_MAX = [
     (1, 1000, 512, 4, 1, 128, L, 600, (900,)),
     (1, 1500, 256, 2, 1, 64, G, 0, None),
     (3, 64, 1024, 4, 4, 256, G, 0, (64, 1, 33)),
+    (2, 1500, 1024, 4, 1, 256, G, 0, (1500, 1100)),
 ]
 
 
@@ -279,6 +283,34 @@ def test_split_merge_on_reused_workspace(gpu_lib, fused, t, Wn):
                              stages=gpu_lib.STAGE_ATTN | gpu_lib.STAGE_OUT_PROJ, **kw)
         torch.cuda.synchronize()
         assert torch.equal(y2, y)
+
+
+@pytest.mark.parametrize("d_h", [128, 256])
+def test_padding_longer_than_window_leaves_rows_without_keys(gpu_lib, d_h):
+    """On a local layer a padded tail longer than the window leaves rows t >=
+    len + W - 1 with no allowed key. The library outputs 0 for those rows (its
+    documented choice; the K_MASK fill would average V over every key), while
+    every other row matches the oracle."""
+    B, T, D, H, Hk, Wn = 2, 200, 512, 4, 1, 16
+    lens = (200, 150)
+    inp = small_prefill_inputs(13, B, T, D, H, Hk, d_h, "bf16", lens)
+    kw = _kw(H, Hk, d_h, L, Wn)
+    d = to_dev(inp)
+    desc = gpu_lib.make_desc(B=B, T=T, D=D, dtype=d["x"].dtype, **kw)
+    ws = gpu_lib.new_workspace(desc)
+    ws.fill_(0xFF)
+    y = gpu_lib.prefill(d["x"], d["segment_pos"], weights_of(d), kv_valid_len=d["kv_valid_len"],
+                        workspace=ws, **kw)
+    torch.cuda.synchronize()
+    first_empty = lens[1] + Wn - 1
+    o = gpu_lib.prefill_intermediates(ws, desc)["o"]
+    assert torch.all(o[1, first_empty:] == 0) and torch.all(y[1, first_empty:] == 0)
+    assert torch.isfinite(o.float()).all()
+    rows = list(range(first_empty))
+    assert_bf16_close(f64(y)[:, rows], oracle_prefill(inp, kw, rows=rows), "y rows with keys")
+    assert_bf16_close(f64(y)[0, first_empty:],
+                      oracle_prefill(inp, kw, rows=list(range(first_empty, T)))[0],
+                      "row 0 tail (unpadded)")
 
 
 def _attn_core_only(gpu_lib, inp, kw):
