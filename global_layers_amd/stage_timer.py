@@ -1,0 +1,104 @@
+"""Per-stage timing of the prefill path on the seeded synthetic workloads.
+
+    python global_layers_amd/stage_timer.py --workload 4 [--reps 10] [--warmup 3]
+
+Every layer of the workload goes through the C ABI one stage at a time
+(gemma3_attn_prefill_stages): the projection with its QK-norm / RoPE
+epilogue, the attention core, the output projection. Each stage is timed with
+HIP events on the call stream over `reps` back-to-back repetitions after
+`warmup` untimed ones (so the clocks are at their working level, unlike a
+single cold call), and printed in microseconds with its algorithmic TFLOP/s:
+projections 2 M K N, attention 4 d_h H per allowed (query, key) pair. A
+profiling aid (for example under rocprofv3); the benchmark line is bench.py's.
+"""
+
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from global_layers_amd import lib  # noqa: E402
+import workloads as W  # noqa: E402
+from workloads import inputs as I  # noqa: E402
+
+
+def allowed_pairs(T: int, attn_type: str, window: int, kv_len: int) -> int:
+    t = np.arange(T)
+    hi = np.minimum(t, kv_len - 1)
+    lo = np.maximum(0, t - window + 1) if attn_type == W.LOCAL_SLIDING else np.zeros_like(t)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def stage_flops(w, layer) -> dict:
+    M = w.B * w.T
+    lens = w.kv_valid_len() or (w.T,) * w.B
+    pairs = sum(allowed_pairs(w.T, layer.attn_type, w.window, L) for L in lens)
+    return {"qkv": 2 * M * w.D * (w.H + 2 * w.H_kv) * w.d_h,
+            "attention": 4 * w.d_h * w.H * pairs,
+            "out": 2 * M * w.H * w.d_h * w.D}
+
+
+def time_layer(w, layer_id: int, reps: int, warmup: int) -> dict:
+    layer = w.layers[layer_id]
+    inp = I.prefill_inputs(w, layer_id)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    weights = {k: d[k] for k in ("w_q", "w_kv", "w_o", "gamma_q", "gamma_k")}
+    kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
+              rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
+              query_scale=w.query_scale)
+    B, T, D = d["x"].shape
+    desc = lib.make_desc(B=B, T=T, D=D, dtype=d["x"].dtype, **kw)
+    ws = lib.new_workspace(desc)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, st in (("qkv", lib.STAGE_QKV_PROJ | lib.STAGE_QK_NORM),
+                     ("attention", lib.STAGE_ATTN), ("out", lib.STAGE_OUT_PROJ)):
+        run = lambda: lib.prefill(d["x"], d["segment_pos"], weights,  # noqa: E731
+                                  kv_valid_len=d.get("kv_valid_len"), workspace=ws, stages=st,
+                                  **kw)
+        for _ in range(warmup):
+            run()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / reps
+    return out
+
+
+def main() -> None:
+    p = argparse.ArgumentParser()
+    p.add_argument("--workload", default="4", help="workload ids, comma separated (2, 3, 4)")
+    p.add_argument("--reps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    args = p.parse_args()
+    if not torch.cuda.is_available():
+        sys.exit("stage_timer needs a GPU")
+    for wid in (int(x) for x in args.workload.split(",")):
+        w = W.WORKLOADS[wid]
+        if w.T == 1:
+            sys.exit(f"workload {wid} is a decode workload")
+        # one layer of each attention type (the others repeat its shapes)
+        seen = {}
+        for li, layer in enumerate(w.layers):
+            seen.setdefault(layer.attn_type, li)
+        for attn_type, li in seen.items():
+            times = time_layer(w, li, args.reps, args.warmup)
+            flops = stage_flops(w, w.layers[li])
+            parts = [f"{n} {t:9.1f} us {flops[n] / t / 1e6:7.1f} TFLOP/s" for n, t in times.items()]
+            print(f"workload {wid} layer {li} {attn_type:13s} " + " | ".join(parts), flush=True)
+
+
+if __name__ == "__main__":
+    main()
