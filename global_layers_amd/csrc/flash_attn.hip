@@ -684,8 +684,8 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // workgroups per query tile (blockIdx.x in the attention kernel's base
 // order); tiles with a single chunk were written by the attention kernel and
 // exit at once. A thread handles 8 channels of a row per item: every chunk's
-// 16-byte piece of the item is loaded before any arithmetic, several items
-// at a time.
+// 16-byte piece and (m, l) pair of the item are loaded before any
+// arithmetic, several items at a time (one round trip per batch).
 constexpr int kCombineItems = 2;   // items in flight per thread
 constexpr int kCombineSlices = 8;  // workgroups per query tile
 
@@ -704,7 +704,7 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
   const int na = geo.n_active;
   for (int base = blockIdx.y * 256 + threadIdx.x; base < n_items;
        base += 256 * kCombineSlices * kCombineItems) {
-    float w[kCombineItems][8];
+    float w[kCombineItems][8], lw[kCombineItems][8];
     u32x4 v[kCombineItems][8];
 #pragma unroll
     for (int u = 0; u < kCombineItems; ++u) {
@@ -715,10 +715,13 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         w[u][j] = -INFINITY;
+        lw[u][j] = 0.f;
         v[u][j] = u32x4{0, 0, 0, 0};
         if (ok && j < na) {
           const size_t row = (((size_t)j * a.B + geo.b) * a.H + h) * a.T + t;
-          w[u][j] = part_ml[2 * row];  // m_j for now
+          const float2 ml = *reinterpret_cast<const float2 *>(part_ml + 2 * row);
+          w[u][j] = ml.x;  // m_j
+          lw[u][j] = ml.y; // l_j
           v[u][j] = *reinterpret_cast<const u32x4 *>(part_o + row * D + 8 * c8);
         }
       }
@@ -737,8 +740,7 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j >= na) break;
-        const size_t row = (((size_t)j * a.B + geo.b) * a.H + h) * a.T + t;
-        const float wl = exp2f(w[u][j] - mu) * part_ml[2 * row + 1];
+        const float wl = exp2f(w[u][j] - mu) * lw[u][j];
         den += wl;
         const bf16x8 pv = __builtin_bit_cast(bf16x8, v[u][j]);
 #pragma unroll

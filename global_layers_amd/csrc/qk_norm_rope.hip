@@ -294,11 +294,13 @@ qk_norm_rope_decode(const float *__restrict__ part, int ksplit, const int32_t *_
   ss = wave_sum(ss);
   const float r = rsqrtf(ss / (float)d_h + 1e-6f);
   const double inv_scale = 1.0 / (double)a.scale;
+  // theta^(-2i/d_h) = 2^(-(2i/d_h) log2 theta), in fp64 (as in the prefill kernel)
+  const double l2t = log2((double)a.theta);
 #pragma unroll
   for (int u = 0; u < kMaxPairs; ++u) {
     const int i = lane + 64 * u;
     if (i >= half) continue;
-    const double inv_freq = pow((double)a.theta, -2.0 * (double)i / (double)d_h);
+    const double inv_freq = exp2(-2.0 * (double)i / (double)d_h * l2t);
     float c, s;
     rope_sincos(p, inv_scale, inv_freq, c, s);
     const float y1 = x1[u] * r * (1.f + to_f32(gamma[i])) * mul;
