@@ -227,15 +227,17 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   }
 }
 
-// grid: x = H, y = B; D threads. Chunk weights exp2(m_j - M) are formed once
-// per block in LDS; each thread then sums its channel over the chunks.
+// grid: x = H, y = B; D threads. Each chunk's (m, l) is read once into LDS;
+// the chunk weights exp2(m_j - M) are formed there, then each thread sums its
+// channel over the chunks with kCombineBatch loads in flight per round trip.
 constexpr int kMaxChunks = 128;  // decode_chunk keeps every row at <= 128 chunks
+constexpr int kCombineBatch = 32;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
 decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos,
                     T *__restrict__ o, DecodeArgs a) {
-  __shared__ float wgt[kMaxChunks];
+  __shared__ float m_s[kMaxChunks], l_s[kMaxChunks], wgt[kMaxChunks];
   __shared__ float red[D / 64];
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int lane = c & 63, wave = c >> 6;
@@ -245,7 +247,12 @@ decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ 
   const float *pp = part + ((size_t)b * a.H + h) * a.n_chunks * (D + 2);
 
   float mx = -INFINITY;
-  for (int j = c; j < n; j += D) mx = fmaxf(mx, pp[(size_t)j * (D + 2) + D]);
+  for (int j = c; j < n; j += D) {
+    const float2 ml = *reinterpret_cast<const float2 *>(pp + (size_t)j * (D + 2) + D);
+    m_s[j] = ml.x;
+    l_s[j] = ml.y;
+    mx = fmaxf(mx, ml.x);
+  }
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
@@ -255,10 +262,10 @@ decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ 
   const float mu = M == -INFINITY ? 0.f : M;
   __syncthreads();
   float sl = 0.f;
-  for (int j = c; j < n; j += D) {
-    const float wj = exp2f(pp[(size_t)j * (D + 2) + D] - mu);
+  for (int j = c; j < n; j += D) {  // the entries this thread wrote above
+    const float wj = exp2f(m_s[j] - mu);
     wgt[j] = wj;
-    sl += wj * pp[(size_t)j * (D + 2) + D + 1];
+    sl += wj * l_s[j];
   }
   sl = wave_sum(sl);
   if (lane == 0) red[wave] = sl;
@@ -268,15 +275,15 @@ decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ 
   for (int i = 0; i < D / 64; ++i) L += red[i];
 
   float sa = 0.f;
-  int j = 0;
-  for (; j + 8 <= n; j += 8) {
-    float v[8];
+  for (int j = 0; j < n; j += kCombineBatch) {
+    float v[kCombineBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = pp[(size_t)(j + u) * (D + 2) + c];
+    for (int u = 0; u < kCombineBatch; ++u)
+      v[u] = j + u < n ? pp[(size_t)(j + u) * (D + 2) + c] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sa = fmaf(wgt[j + u], v[u], sa);
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (j + u < n) sa = fmaf(wgt[j + u], v[u], sa);
   }
-  for (; j < n; ++j) sa = fmaf(wgt[j], pp[(size_t)j * (D + 2) + c], sa);
   o[((size_t)b * a.H + h) * D + c] = from_f32<T>(L > 0.f ? sa / L : 0.f);
 }
 
