@@ -98,3 +98,36 @@ def test_cfg5_full_size_sampled_rows(gpu_lib, layer_id):
         assert_bf16_close(f64(vc[b, pos[b]]), v_new[0], f"row {b} v slot")
     del kc, vc, kc0, vc0
     torch.cuda.empty_cache()
+
+
+def test_decode_position_outside_cache_outputs_zero(gpu_lib):
+    """A decode position outside [0, S) makes that row skip its cache write and
+    output 0 (the documented precondition breach); the other rows are
+    unaffected and match the oracle."""
+    d_h, H, Hk, Wn, t = 128, 4, 2, 64, "LOCAL_SLIDING"
+    lengths = np.array([40, 120, 300, 7])
+    base = W.WORKLOADS[5]
+    w = W.scaled(base, B=len(lengths), D=128, H=H, H_kv=Hk, d_h=d_h, window=Wn,
+                 query_scale=d_h ** -0.5, cache_len=300, dtype="bf16",
+                 layers=(W.Layer(t, 1e4, 1.0),))
+    inp = I.decode_inputs(w, 0, lengths)
+    bad = {1: 300, 3: -1}  # S and -1
+    for b, p in bad.items():
+        inp["segment_pos"][b, 0] = p
+    kc, vc = I.decode_cache(w, 0, lengths, device="cuda", poison=True)
+    kc0, vc0 = kc.clone(), vc.clone()
+    kw = layer_kw(w, w.layers[0])
+    d = to_dev(inp)
+    y = gpu_lib.decode(d["x"], d["segment_pos"], weights_of(d), kc, vc, **kw)
+    torch.cuda.synchronize()
+    for b in range(len(lengths)):
+        if b in bad:
+            assert torch.all(y[b] == 0), f"row {b}"
+            same = (kc[b] == kc0[b]) | (torch.isnan(kc[b]) & torch.isnan(kc0[b]))
+            assert bool(same.all()), f"row {b}: k cache written"
+            same = (vc[b] == vc0[b]) | (torch.isnan(vc[b]) & torch.isnan(vc0[b]))
+            assert bool(same.all()), f"row {b}: v cache written"
+        else:
+            yr, k_new, _ = _oracle_row(inp, kw, kc0, vc0, b)
+            assert_bf16_close(f64(y[b:b + 1]), yr, f"row {b} y")
+            assert_bf16_close(f64(kc[b, int(inp["segment_pos"][b, 0])]), k_new[0], f"row {b} k")

@@ -313,6 +313,26 @@ def test_padding_longer_than_window_leaves_rows_without_keys(gpu_lib, d_h):
                       "row 0 tail (unpadded)")
 
 
+@pytest.mark.parametrize("t,Wn", [(G, 0), (L, 64)])
+def test_row_with_every_key_padded_outputs_zero(gpu_lib, t, Wn):
+    """kv_valid_len[b] == 0: no query row of batch row b has an allowed key,
+    so its outputs are 0 (the library's documented choice); the other batch
+    row matches the oracle."""
+    B, T, D, H, Hk, d_h = 2, 300, 512, 4, 1, 256
+    inp = small_prefill_inputs(17, B, T, D, H, Hk, d_h, "bf16", (0, T))
+    kw = _kw(H, Hk, d_h, t, Wn)
+    d = to_dev(inp)
+    desc = gpu_lib.make_desc(B=B, T=T, D=D, dtype=d["x"].dtype, **kw)
+    ws = gpu_lib.new_workspace(desc)
+    ws.fill_(0xFF)
+    y = gpu_lib.prefill(d["x"], d["segment_pos"], weights_of(d), kv_valid_len=d["kv_valid_len"],
+                        workspace=ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.all(gpu_lib.prefill_intermediates(ws, desc)["o"][0] == 0)
+    assert torch.all(y[0] == 0)
+    assert_bf16_close(f64(y)[1], oracle_prefill(inp, kw)[1], "batch row 1")
+
+
 def _attn_core_only(gpu_lib, inp, kw):
     d = to_dev(inp)
     B, T, D = d["x"].shape
