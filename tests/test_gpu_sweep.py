@@ -1,0 +1,126 @@
+"""GPU parity over a seeded sweep of random small shapes: GQA ratios 1..8,
+T not a multiple of any tile size, windows from 1 to past T, random padding,
+both dtypes, every head size with kernels, random RoPE (theta, scale), and
+the query scales the model uses (d_h^-1/2 or (D/H)^-1/2; D >= H d_h as in the
+workloads). Each case is compared element by element with the fp64 oracle
+(bf16: 2e-2 + 1e-2 |ref|, fp32: 1e-4). The shapes are drawn once from a fixed
+seed, so the sweep is the same on every run."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from workloads import inputs as I
+from parity_util import (assert_bf16_close, assert_f32_close, f64, gpu_prefill, log, oracle_kw,
+                         oracle_prefill, small_prefill_inputs, to_dev, weights_of)
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+L, G = "LOCAL_SLIDING", "GLOBAL"
+
+
+def _prefill_cases(n=16, seed=2026):
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = "bf16" if r.random() < 0.75 else "f32"
+        d_h = int(r.choice([64, 128, 256]))
+        Hk = int(r.choice([1, 2, 3, 4]))
+        G_ = int(r.choice([1, 2, 3, 4, 8]))
+        H = Hk * G_
+        if H * d_h > 2048:
+            continue
+        # D >= H d_h as in every workload (the bf16 storage error of y grows
+        # with sqrt(H d_h / D), and the tolerance is stated for those shapes)
+        D = H * d_h + 64 * int(r.integers(0, 3))
+        B = int(r.integers(1, 4))
+        T = int(r.integers(1, 700))
+        t = G if r.random() < 0.4 else L
+        Wn = 0 if t == G else int(r.choice([1, 2, 17, 64, 100, 300, 1000]))
+        lens = None
+        if r.random() < 0.5:
+            lens = tuple(int(x) for x in r.integers(1, T + 1, size=B))
+        theta = float(r.choice([1e4, 1e6]))
+        scale = float(r.choice([1.0, 8.0]))
+        # the query scales Gemma 3 layers use: d_h^-1/2, or (D/H)^-1/2 (27B shapes)
+        alpha = float(d_h ** -0.5 if r.random() < 0.5 else (D / H) ** -0.5)
+        cases.append((B, T, D, H, Hk, d_h, t, Wn, lens, dtype, theta, scale, alpha))
+    return cases
+
+
+PREFILL = _prefill_cases()
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[f"p{i}" for i in range(len(PREFILL))])
+def test_prefill_sweep(gpu_lib, case):
+    B, T, D, H, Hk, d_h, t, Wn, lens, dtype, theta, scale, alpha = case
+    log(f"case {case}")
+    inp = small_prefill_inputs(31, B, T, D, H, Hk, d_h, dtype, lens)
+    kw = dict(H=H, H_kv=Hk, d_h=d_h, attn_type=t, window=Wn, rope_theta=theta,
+              rope_scale=scale, query_scale=alpha)
+    y = gpu_prefill(gpu_lib, inp, kw)
+    ref = oracle_prefill(inp, kw)
+    if lens is not None:
+        # rows with no allowed key output 0 by the library's choice (the fill
+        # value would average V); compare every other row
+        for b in range(B):
+            t_idx = np.arange(T)
+            lo = np.maximum(0, t_idx - Wn + 1) if t == L else np.zeros(T, int)
+            empty = np.minimum(t_idx, lens[b] - 1) < lo
+            if empty.any():
+                assert torch.all(y[b, torch.from_numpy(empty)] == 0)
+                ref[b, empty] = f64(y)[b, empty]
+    (assert_bf16_close if dtype == "bf16" else assert_f32_close)(f64(y), ref, "y")
+
+
+def _decode_cases(n=8, seed=2027):
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = "bf16" if r.random() < 0.75 else "f32"
+        d_h = int(r.choice([64, 128, 256]))
+        Hk = int(r.choice([1, 2, 4]))
+        H = Hk * int(r.choice([1, 2, 4]))
+        B = int(r.integers(1, 5))
+        S = int(r.integers(2, 600))
+        t = G if r.random() < 0.5 else L
+        Wn = 1024 if t == G else int(r.choice([1, 16, 64, 200, 1000]))
+        lengths = tuple(int(x) for x in r.integers(1, S + 1, size=B))
+        cases.append((d_h, H, Hk, Wn, t, lengths, dtype, S))
+    return cases
+
+
+DECODE = _decode_cases()
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[f"d{i}" for i in range(len(DECODE))])
+def test_decode_sweep(gpu_lib, case):
+    d_h, H, Hk, Wn, t, lengths, dtype, S = case
+    log(f"case {case}")
+    w = W.scaled(W.WORKLOADS[5], B=len(lengths), D=H * d_h, H=H, H_kv=Hk, d_h=d_h, window=Wn,
+                 query_scale=d_h ** -0.5, cache_len=S, dtype=dtype,
+                 layers=(W.Layer(t, 1e6 if t == G else 1e4, 8.0 if t == G else 1.0),))
+    lengths = np.array(lengths)
+    inp = I.decode_inputs(w, 0, lengths)
+    kc, vc = I.decode_cache(w, 0, lengths, device="cuda", poison=True)
+    kc0, vc0 = kc.clone(), vc.clone()
+    kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=t, window=w.window,
+              rope_theta=w.layers[0].rope_theta, rope_scale=w.layers[0].rope_scale,
+              query_scale=w.query_scale)
+    d = to_dev(inp)
+    y = gpu_lib.decode(d["x"], d["segment_pos"], weights_of(d), kc, vc, **kw)
+    torch.cuda.synchronize()
+    check = assert_bf16_close if dtype == "bf16" else assert_f32_close
+    for b in range(len(lengths)):
+        p = int(inp["segment_pos"][b, 0])
+        kb = kc0[b:b + 1, :p + 1].float().cpu().numpy()
+        vb = vc0[b:b + 1, :p + 1].float().cpu().numpy()
+        yr, k_new, v_new = O.decode(f64(inp["x"][b:b + 1]), inp["segment_pos"][b:b + 1].numpy(),
+                                    f64(inp["w_q"]), f64(inp["w_kv"]), f64(inp["w_o"]),
+                                    f64(inp["gamma_q"]), f64(inp["gamma_k"]), kb, vb,
+                                    **oracle_kw(kw))
+        check(f64(y[b:b + 1]), yr, f"row {b} y")
+        check(f64(kc[b, p]), k_new[0], f"row {b} k slot")
+        check(f64(vc[b, p]), v_new[0], f"row {b} v slot")
