@@ -25,4 +25,5 @@ from .gemma3_oracle import (  # noqa: F401
     attention_core,
     prefill,
     decode,
+    prefill_cache,
 )

@@ -212,6 +212,40 @@ def prefill(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, *,
                    k_rope=k_rope, q_tilde=q_tilde, o=o)
 
 
+def prefill_cache(x, segment_pos, w_kv, gamma_k, k_cache, v_cache, *,
+                  num_kv_heads: int, head_dim: int, rope_theta: float, rope_scale: float,
+                  kv_valid_len=None):
+    """Caches after a prefill that fills a left-aligned cache.
+
+    "Gemma 3 Attention Block", How it works, Cache: the call's keys (after
+    RMSNorm_K and RoPE) and values are written into a left-aligned buffer of
+    S slots, slot = position. Readings: token t of row b goes to slot
+    segment_pos[b, t]; tokens at or past kv_valid_len[b] (padding) and
+    positions outside [0, S) write nothing; every other slot keeps its
+    contents. Returns fp64 copies of k_cache and v_cache [B,S,H_kv,d_h].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, _ = x.shape
+    Hk, d_h = num_kv_heads, head_dim
+    w_kv = np.asarray(w_kv, dtype=np.float64)
+    k = (x @ w_kv[:Hk * d_h].T).reshape(B, T, Hk, d_h)   # K heads first in w_kv
+    v = (x @ w_kv[Hk * d_h:].T).reshape(B, T, Hk, d_h)
+    pos = np.asarray(segment_pos, dtype=np.int64).reshape(B, T)
+    k_rope = rope(rms_norm(k, gamma_k), pos[:, :, None], rope_theta, rope_scale)
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    S = kc.shape[1]
+    lens = (np.full(B, T, dtype=np.int64) if kv_valid_len is None
+            else np.asarray(kv_valid_len, dtype=np.int64).reshape(B))
+    for b in range(B):
+        for t in range(min(int(lens[b]), T)):
+            p = int(pos[b, t])
+            if 0 <= p < S:
+                kc[b, p] = k_rope[b, t]
+                vc[b, p] = v[b, t]
+    return kc, vc
+
+
 def _prefill_rows(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, rows, H, Hk, d_h,
                   attn_type, window, rope_theta, rope_scale, query_scale, kv_valid_len):
     """Selected query rows of prefill (same steps as the full computation)."""

@@ -472,6 +472,60 @@ def test_local_decode_short_history_equals_global():
     assert np.max(np.abs(y_w - y_g)) > 1e-6
 
 
+# ---------------------------------------------------------------- cache-filling prefill
+@pytest.mark.parametrize("attn_type,W", [(O.GLOBAL, 0), (O.LOCAL_SLIDING, 4)])
+def test_prefill_cache_then_decode_continues_each_row(attn_type, W):
+    # Rows of valid lengths L_b fill a NaN cache from one padded prefill call;
+    # decoding token L_b of a row at position L_b must then give the last row
+    # of a plain prefill over that row's tokens 0..L_b (the cache is what lets
+    # a decode step continue the sequence), and no slot past L_b is touched.
+    B, T, D, H, Hk, d_h, S = 3, 12, 16, 4, 2, 8, 20
+    lens = np.array([12, 7, 1])
+    x = _rand(41, B, T + 1, D)
+    w = _layer(42, D, H, Hk, d_h)
+    kw = dict(num_heads=H, num_kv_heads=Hk, head_dim=d_h, attn_type=attn_type, window=W,
+              rope_theta=1e4, rope_scale=1.0, query_scale=0.4)
+    pos = np.tile(np.arange(T), (B, 1))
+    nan = np.full((B, S, Hk, d_h), np.nan)
+    kc, vc = O.prefill_cache(x[:, :T], pos, w["w_kv"], w["gamma_k"], nan, nan,
+                             num_kv_heads=Hk, head_dim=d_h, rope_theta=1e4, rope_scale=1.0,
+                             kv_valid_len=lens)
+    for b in range(B):
+        L = int(lens[b])
+        assert not np.isnan(kc[b, :L]).any() and not np.isnan(vc[b, :L]).any()
+        assert np.isnan(kc[b, L:]).all() and np.isnan(vc[b, L:]).all()
+        y_ref = _prefill(x[b:b + 1, :L + 1], w, **kw)[0, L]
+        y, _, _ = O.decode(x[b:b + 1, L:L + 1], np.array([[L]]), w["w_q"], w["w_kv"],
+                           w["w_o"], w["gamma_q"], w["gamma_k"], kc[b:b + 1], vc[b:b + 1], **kw)
+        np.testing.assert_allclose(y[0, 0], y_ref, rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_cache_slots_follow_positions():
+    # slot = position: a row whose positions start at 5 fills slots 5.. and
+    # stops at the end of the cache, a negative position writes nothing, and
+    # every other slot keeps its contents
+    B, T, D, H, Hk, d_h, S = 2, 6, 16, 2, 2, 8, 9
+    x = _rand(43, B, T, D)
+    w = _layer(44, D, H, Hk, d_h)
+    pos = np.array([[5, 6, 7, 8, 9, 10], [-1, 0, 1, 2, 3, 4]])
+    old_k, old_v = _rand(45, B, S, Hk, d_h), _rand(46, B, S, Hk, d_h)
+    kc, vc = O.prefill_cache(x, pos, w["w_kv"], w["gamma_k"], old_k, old_v,
+                             num_kv_heads=Hk, head_dim=d_h, rope_theta=1e4, rope_scale=2.0)
+    _, k, v = O.project_qkv(x, w["w_q"], w["w_kv"], H, Hk, d_h)
+    k_rope = O.rope(O.rms_norm(k, w["gamma_k"]), pos[:, :, None], 1e4, 2.0)
+    written = {(0, 5): 0, (0, 6): 1, (0, 7): 2, (0, 8): 3,
+               (1, 0): 1, (1, 1): 2, (1, 2): 3, (1, 3): 4, (1, 4): 5}
+    for b in range(B):
+        for s in range(S):
+            t = written.get((b, s))
+            if t is None:
+                np.testing.assert_array_equal(kc[b, s], old_k[b, s])
+                np.testing.assert_array_equal(vc[b, s], old_v[b, s])
+            else:
+                np.testing.assert_allclose(kc[b, s], k_rope[b, t], rtol=1e-13, atol=1e-15)
+                np.testing.assert_allclose(vc[b, s], v[b, t], rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- sampled rows
 @pytest.mark.parametrize("attn_type,W,lens", [(O.LOCAL_SLIDING, 4, (17, 14)),
                                               (O.GLOBAL, 0, (17, 9))])
