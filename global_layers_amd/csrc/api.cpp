@@ -289,6 +289,38 @@ int gemma3_attn_prefill(const gemma3_attn_desc *desc, const void *x, const int32
                                     workspace_bytes, hip_stream, GEMMA3_STAGE_ALL);
 }
 
+int gemma3_attn_prefill_cache(const gemma3_attn_desc *desc, const void *x,
+                              const int32_t *segment_pos, const int32_t *kv_valid_len,
+                              const gemma3_attn_weights *w, void *k_cache, void *v_cache,
+                              int32_t S, void *y, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+  if (S < 1) return desc ? GEMMA3_ERR_SHAPE : GEMMA3_ERR_NULL;
+  gemma3_ws_layout L;
+  int st = layout(desc, 0, &L);
+  if (st != GEMMA3_OK) return st;
+  if (!k_cache || !v_cache) return GEMMA3_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return GEMMA3_ERR_ALIGN;
+  if ((long)desc->B * S * desc->H_kv * desc->d_h >= (1L << 62)) return GEMMA3_ERR_UNSUPPORTED;
+  // the prefill validates everything else before it enqueues anything
+  st = gemma3_attn_prefill_stages(desc, x, segment_pos, kv_valid_len, w, y, workspace,
+                                  workspace_bytes, hip_stream, GEMMA3_STAGE_ALL);
+  if (st != GEMMA3_OK) return st;
+  char *base = (char *)workspace;
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (desc->dtype == GEMMA3_BF16)
+    RUN(launch_prefill_cache_write<bf16>((const bf16 *)(base + L.k), (const bf16 *)(base + L.vt),
+                                         segment_pos, kv_valid_len, (bf16 *)k_cache,
+                                         (bf16 *)v_cache, desc->B, desc->T, L.T_pad,
+                                         desc->H_kv, desc->d_h, S, s));
+  else
+    RUN(launch_prefill_cache_write<float>((const float *)(base + L.k),
+                                          (const float *)(base + L.vt), segment_pos,
+                                          kv_valid_len, (float *)k_cache, (float *)v_cache,
+                                          desc->B, desc->T, L.T_pad, desc->H_kv, desc->d_h, S,
+                                          s));
+  return GEMMA3_OK;
+}
+
 int gemma3_attn_decode_stages(const gemma3_attn_desc *desc, const void *x,
                               const int32_t *segment_pos, const gemma3_attn_weights *w,
                               void *k_cache, void *v_cache, int32_t S, void *y, void *workspace,

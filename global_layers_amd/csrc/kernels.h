@@ -83,6 +83,15 @@ hipError_t launch_decode_attn(const float *q, const T *k_cache, const T *v_cache
                               hipStream_t s);
 
 // Sum of fp32 split partials [ksplit][M][N] into y [M][N].
+// Copy the valid tokens' rotated keys (k [B,Hk,T_pad,d_h]) and values
+// (vt [B,Hk,d_h,T_pad]) of a prefill into a left-aligned cache [B,S,Hk,d_h]
+// at slot pos[b,t].
+template <typename T>
+hipError_t launch_prefill_cache_write(const T *k, const T *vt, const int32_t *pos,
+                                      const int32_t *kv_len, T *k_cache, T *v_cache, int B,
+                                      int T_len, int T_pad, int Hk, int d_h, int S,
+                                      hipStream_t s);
+
 template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int ksplit, T *y, long MN, hipStream_t s);
 

@@ -81,6 +81,9 @@ _DECODE_ARGS = [ctypes.POINTER(Desc), _P, _P, ctypes.POINTER(Weights), _P, _P, c
                 _P, _P, ctypes.c_size_t, _P]
 for name, args in (("gemma3_attn_prefill", _PREFILL_ARGS),
                    ("gemma3_attn_prefill_stages", _PREFILL_ARGS + [ctypes.c_uint32]),
+                   ("gemma3_attn_prefill_cache",
+                    [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
+                     ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
                    ("gemma3_attn_decode", _DECODE_ARGS),
                    ("gemma3_attn_decode_stages", _DECODE_ARGS + [ctypes.c_uint32])):
     fn = getattr(_lib, name)
@@ -90,7 +93,7 @@ for name, args in (("gemma3_attn_prefill", _PREFILL_ARGS),
 EXPORTED = ("gemma3_attn_workspace_bytes", "gemma3_attn_prefill", "gemma3_attn_decode",
             "gemma3_layer_attn_type", "gemma3_attn_status_string", "gemma3_attn_abi_version",
             "gemma3_attn_workspace_layout", "gemma3_attn_prefill_stages",
-            "gemma3_attn_decode_stages")
+            "gemma3_attn_decode_stages", "gemma3_attn_prefill_cache")
 
 
 class Gemma3AttnError(ValueError):
@@ -166,8 +169,12 @@ def new_workspace(desc: Desc, S: int = 0, device="cuda") -> torch.Tensor:
 
 def prefill(x, segment_pos, weights: dict, *, H, H_kv, d_h, attn_type, window, rope_theta,
             rope_scale, query_scale, kv_valid_len=None, workspace=None, y=None,
-            stages: int = STAGE_ALL):
-    """y [B,T,D] = attention layer over x [B,T,D] (see gemma3_attn_prefill)."""
+            stages: int = STAGE_ALL, k_cache=None, v_cache=None):
+    """y [B,T,D] = attention layer over x [B,T,D] (see gemma3_attn_prefill).
+
+    With k_cache and v_cache ([B,S,H_kv,d_h]) the call also writes every valid
+    token's rotated key and value to slot segment_pos[b,t]
+    (gemma3_attn_prefill_cache; all stages run)."""
     dev = x.device
     B, T, D = x.shape
     desc = make_desc(B=B, T=T, D=D, H=H, H_kv=H_kv, d_h=d_h, attn_type=attn_type,
@@ -186,6 +193,21 @@ def prefill(x, segment_pos, weights: dict, *, H, H_kv, d_h, attn_type, window, r
         workspace = new_workspace(desc, 0, dev)
     if y is None:
         y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    if (k_cache is None) != (v_cache is None):
+        raise ValueError("k_cache and v_cache go together")
+    if k_cache is not None:
+        if stages != STAGE_ALL:
+            raise ValueError("a cache-filling prefill runs every stage")
+        S = k_cache.shape[1]
+        for n, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+            _dev_tensor(c, x.dtype, n, dev)
+            if c.shape != (B, S, H_kv, d_h):
+                raise ValueError(f"{n} must be [B, S, H_kv, d_h]")
+        _check(_lib.gemma3_attn_prefill_cache(
+            ctypes.byref(desc), _ptr(x), _ptr(segment_pos), _ptr(kv_valid_len), ctypes.byref(w),
+            _ptr(k_cache), _ptr(v_cache), S, _ptr(y), _ptr(workspace), workspace.numel(),
+            _stream()))
+        return y
     _check(_lib.gemma3_attn_prefill_stages(
         ctypes.byref(desc), _ptr(x), _ptr(segment_pos), _ptr(kv_valid_len), ctypes.byref(w),
         _ptr(y), _ptr(workspace), workspace.numel(), _stream(), stages))

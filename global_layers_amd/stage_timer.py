@@ -1,6 +1,6 @@
 """Per-stage timing of the prefill path on the seeded synthetic workloads.
 
-    python global_layers_amd/stage_timer.py --workload 4 [--reps 10] [--warmup 3]
+    python global_layers_amd/stage_timer.py --workload 4 [--reps 10] [--warmup 3] [--cache]
 
 Every layer of the workload goes through the C ABI one stage at a time
 (gemma3_attn_prefill_stages): the projection with its QK-norm / RoPE
@@ -8,8 +8,12 @@ epilogue, the attention core, the output projection. Each stage is timed with
 HIP events on the call stream over `reps` back-to-back repetitions after
 `warmup` untimed ones (so the clocks are at their working level, unlike a
 single cold call), and printed in microseconds with its algorithmic TFLOP/s:
-projections 2 M K N, attention 4 d_h H per allowed (query, key) pair. A
-profiling aid (for example under rocprofv3); the benchmark line is bench.py's.
+projections 2 M K N, attention 4 d_h H per allowed (query, key) pair. With
+--cache, the whole layer also runs as gemma3_attn_prefill_cache into a cache
+of T slots; the difference to the plain call is the cache fill, printed with
+its algorithmic GB/s (each valid token's key and value read once and written
+once: 4 H_kv d_h elements). A profiling aid (for example under rocprofv3); the
+benchmark line is bench.py's.
 """
 
 from __future__ import annotations
@@ -46,7 +50,7 @@ def stage_flops(w, layer) -> dict:
             "out": 2 * M * w.H * w.d_h * w.D}
 
 
-def time_layer(w, layer_id: int, reps: int, warmup: int) -> dict:
+def time_layer(w, layer_id: int, reps: int, warmup: int, cache: bool = False) -> dict:
     layer = w.layers[layer_id]
     inp = I.prefill_inputs(w, layer_id)
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
@@ -74,6 +78,24 @@ def time_layer(w, layer_id: int, reps: int, warmup: int) -> dict:
         e1.record(stream)
         torch.cuda.synchronize()
         out[name] = e0.elapsed_time(e1) * 1e3 / reps
+    if cache:
+        S = T
+        kc = torch.zeros((B, S, w.H_kv, w.d_h), dtype=d["x"].dtype, device="cuda")
+        vc = torch.zeros_like(kc)
+        for name, extra in (("plain", {}), ("with_cache", dict(k_cache=kc, v_cache=vc))):
+            run = lambda: lib.prefill(d["x"], d["segment_pos"], weights,  # noqa: E731
+                                      kv_valid_len=d.get("kv_valid_len"), workspace=ws, **extra,
+                                      **kw)
+            for _ in range(warmup):
+                run()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[name] = e0.elapsed_time(e1) * 1e3 / reps
     return out
 
 
@@ -82,6 +104,7 @@ def main() -> None:
     p.add_argument("--workload", default="4", help="workload ids, comma separated (2, 3, 4)")
     p.add_argument("--reps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cache", action="store_true", help="also time the cache-filling prefill")
     args = p.parse_args()
     if not torch.cuda.is_available():
         sys.exit("stage_timer needs a GPU")
@@ -94,10 +117,19 @@ def main() -> None:
         for li, layer in enumerate(w.layers):
             seen.setdefault(layer.attn_type, li)
         for attn_type, li in seen.items():
-            times = time_layer(w, li, args.reps, args.warmup)
+            times = time_layer(w, li, args.reps, args.warmup, args.cache)
             flops = stage_flops(w, w.layers[li])
-            parts = [f"{n} {t:9.1f} us {flops[n] / t / 1e6:7.1f} TFLOP/s" for n, t in times.items()]
+            parts = [f"{n} {times[n]:9.1f} us {flops[n] / times[n] / 1e6:7.1f} TFLOP/s"
+                     for n in ("qkv", "attention", "out")]
             print(f"workload {wid} layer {li} {attn_type:13s} " + " | ".join(parts), flush=True)
+            if args.cache:
+                lens = w.kv_valid_len() or (w.T,) * w.B
+                nbytes = 4 * sum(lens) * w.H_kv * w.d_h * (2 if w.dtype == "bf16" else 4)
+                dt = times["with_cache"] - times["plain"]
+                print(f"workload {wid} layer {li} {attn_type:13s} prefill {times['plain']:9.1f} us"
+                      f" | with cache fill {times['with_cache']:9.1f} us | fill {dt:7.1f} us"
+                      f" {nbytes / max(dt, 1e-3) / 1e3:7.1f} GB/s ({nbytes / 1e6:.1f} MB)",
+                      flush=True)
 
 
 if __name__ == "__main__":

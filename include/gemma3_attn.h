@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define GEMMA3_ATTN_ABI_VERSION 1
+#define GEMMA3_ATTN_ABI_VERSION 2
 
 /* AttentionType ("Global vs Local Layer Routing", How it works). */
 typedef enum { GEMMA3_ATTN_GLOBAL = 0, GEMMA3_ATTN_LOCAL_SLIDING = 1 } gemma3_attn_type;
@@ -135,6 +135,29 @@ int gemma3_attn_prefill(const gemma3_attn_desc *desc, const void *x,
                         const int32_t *segment_pos, const int32_t *kv_valid_len,
                         const gemma3_attn_weights *w, void *y, void *workspace,
                         size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Prefill that also fills a left-aligned cache ("Gemma 3 Attention Block",
+ * How it works, Cache: the call's keys and values are written into a
+ * left-aligned buffer of S slots). Computes y exactly as gemma3_attn_prefill
+ * does (the attention sees the T tokens of this call only), then writes the
+ * rotated key and the value of every valid token t (t < kv_valid_len[b], or
+ * every t when kv_valid_len is NULL) of every KV head to slot
+ * segment_pos[b*T + t] of k_cache and v_cache: device arrays
+ * [B, S, H_kv, d_h] of the descriptor's dtype (the layout gemma3_attn_decode
+ * reads), 16-byte aligned, owned by the caller. Tokens whose position lies
+ * outside [0, S) and every other slot are left untouched. Positions within a
+ * row should be distinct: when two tokens share a slot, either may end up
+ * there. The workspace is the prefill's (gemma3_attn_workspace_bytes(desc, 0)).
+ * Errors: those of gemma3_attn_prefill; S < 1 -> GEMMA3_ERR_SHAPE; a NULL
+ * cache -> GEMMA3_ERR_NULL; a misaligned cache -> GEMMA3_ERR_ALIGN. Nothing
+ * is enqueued when an error is returned before the first launch.
+ */
+int gemma3_attn_prefill_cache(const gemma3_attn_desc *desc, const void *x,
+                              const int32_t *segment_pos, const int32_t *kv_valid_len,
+                              const gemma3_attn_weights *w, void *k_cache, void *v_cache,
+                              int32_t S, void *y, void *workspace, size_t workspace_bytes,
+                              void *hip_stream);
 
 /*
  * Decode: one token per row against a left-aligned cache of S slots

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.abi_version() == 1
+    assert lib.abi_version() == 2
     for st in range(10):
         assert lib._lib.gemma3_attn_status_string(st)
     assert lib._lib.gemma3_attn_status_string(99) == b"unknown status"
@@ -117,6 +117,27 @@ def test_decode_validation_status():
     assert _call_decode(d, kc=None) == 1
     assert _call_decode(d, vc=FAKE + 2) == 9
     assert _call_decode(_desc(T=1, d_h=32, dtype=lib.F32, D=64), S=8, ws_bytes=1 << 30) == 7
+
+
+def _call_prefill_cache(desc, S=512, kc=FAKE, vc=FAKE, x=FAKE, ws_bytes=None):
+    w = lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    n = lib.workspace_bytes(desc) if ws_bytes is None else ws_bytes
+    return lib._lib.gemma3_attn_prefill_cache(ctypes.byref(desc), x, FAKE, None,
+                                              ctypes.byref(w), kc, vc, S, FAKE, FAKE, n, None)
+
+
+def test_prefill_cache_validation_status():
+    d = _desc()
+    assert lib._lib.gemma3_attn_prefill_cache(None, FAKE, FAKE, None, None, FAKE, FAKE, 8,
+                                              FAKE, FAKE, 1, None) == 1
+    assert _call_prefill_cache(d, S=0) == 2
+    assert _call_prefill_cache(_desc(B=0)) == 2
+    assert _call_prefill_cache(d, kc=None) == 1
+    assert _call_prefill_cache(d, vc=None) == 1
+    assert _call_prefill_cache(d, kc=FAKE + 2) == 9
+    assert _call_prefill_cache(d, x=None) == 1      # the prefill's own checks
+    assert _call_prefill_cache(d, ws_bytes=16) == 6
+    assert _call_prefill_cache(_desc(d_h=96), ws_bytes=1 << 40) == 7
 
 
 def test_workspace_layout_prefill_and_decode():
