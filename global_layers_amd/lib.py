@@ -156,6 +156,23 @@ def _weights(w: dict, dtype, device) -> Weights:
     return Weights(*(w[k].data_ptr() for k in ("w_q", "w_kv", "w_o", "gamma_q", "gamma_k")))
 
 
+def fused_qkv_weights(w_qkv, w_o, gamma_q, gamma_k, *, H: int, d_h: int) -> dict:
+    """Weights of a layer with H_kv == H whose projections are one fused matrix.
+
+    "Gemma 3 Attention Block", How it works, projections: with as many KV
+    heads as query heads a single qkv projection yields Q, K and V. w_qkv is
+    [3*H*d_h, D], output-major, Q heads then K heads then V heads; w_q and
+    w_kv become views into it (no copy): the library reads the Q rows and the
+    K/V rows through two pointers that here point into one buffer.
+    """
+    n = H * d_h
+    if w_qkv.dim() != 2 or w_qkv.shape[0] != 3 * n:
+        raise ValueError("w_qkv must be [3 * H * d_h, D]")
+    if not w_qkv.is_contiguous():
+        raise ValueError("w_qkv must be contiguous")
+    return dict(w_q=w_qkv[:n], w_kv=w_qkv[n:], w_o=w_o, gamma_q=gamma_q, gamma_k=gamma_k)
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
