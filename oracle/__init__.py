@@ -26,4 +26,5 @@ from .gemma3_oracle import (  # noqa: F401
     prefill,
     decode,
     prefill_cache,
+    prefill_chunk,
 )

@@ -246,6 +246,51 @@ def prefill_cache(x, segment_pos, w_kv, gamma_k, k_cache, v_cache, *,
     return kc, vc
 
 
+def prefill_chunk(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, k_cache, v_cache,
+                  start: int, *, num_heads: int, num_kv_heads: int, head_dim: int,
+                  attn_type: str, window: int, rope_theta: float, rope_scale: float,
+                  query_scale: float, kv_valid_len=None):
+    """A prefill chunk that continues rows whose first `start` tokens are cached.
+
+    "Gemma 3 Attention Block", How it works, Cache (with the prefill steps of
+    the same section): the chunk's T tokens have indices start .. start+T-1;
+    their rotated keys and values join the cached slots 0..start-1
+    (slot = position) and every query attends under the same masks as a
+    prefill of the whole sequence, in those absolute indices. Readings:
+    segment_pos[b, t] = start + t feeds RoPE and names the slot the token is
+    written to; kv_valid_len[b] counts the chunk's valid tokens (keys past
+    start + kv_valid_len[b] are blocked and not written). Returns y [B,T,D]
+    and the updated fp64 caches.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, _ = x.shape
+    H, Hk, d_h = num_heads, num_kv_heads, head_dim
+    G = H // Hk
+    pos = np.asarray(segment_pos, dtype=np.int64).reshape(B, T)
+    lens = (np.full(B, T, dtype=np.int64) if kv_valid_len is None
+            else np.asarray(kv_valid_len, dtype=np.int64).reshape(B))
+    q, k, v = project_qkv(x, w_q, w_kv, H, Hk, d_h)
+    q_tilde = query_scale * rope(rms_norm(q, gamma_q), pos[:, :, None], rope_theta, rope_scale)
+    k_rope = rope(rms_norm(k, gamma_k), pos[:, :, None], rope_theta, rope_scale)
+    kc, vc = prefill_cache(x, pos, w_kv, gamma_k, k_cache, v_cache, num_kv_heads=Hk,
+                           head_dim=d_h, rope_theta=rope_theta, rope_scale=rope_scale,
+                           kv_valid_len=lens)
+    o = np.empty((B, T, H, d_h), dtype=np.float64)
+    t_idx = start + np.arange(T)
+    s_idx = np.arange(start + T)
+    for b in range(B):
+        ok = allowed_mask(t_idx, s_idx, attn_type, window, start + lens[b])
+        for kh in range(Hk):
+            kb = np.concatenate([np.asarray(k_cache[b, :start, kh], dtype=np.float64),
+                                 k_rope[b, :, kh]])
+            vb = np.concatenate([np.asarray(v_cache[b, :start, kh], dtype=np.float64),
+                                 v[b, :, kh]])
+            o[b, :, kh * G:(kh + 1) * G] = attention_core(q_tilde[b, :, kh * G:(kh + 1) * G],
+                                                          kb, vb, ok)
+    y = o.reshape(B, T, H * d_h) @ np.asarray(w_o, dtype=np.float64).T
+    return y, kc, vc
+
+
 def _prefill_rows(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, rows, H, Hk, d_h,
                   attn_type, window, rope_theta, rope_scale, query_scale, kv_valid_len):
     """Selected query rows of prefill (same steps as the full computation)."""

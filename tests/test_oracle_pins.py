@@ -526,6 +526,50 @@ def test_prefill_cache_slots_follow_positions():
                 np.testing.assert_allclose(vc[b, s], v[b, t], rtol=1e-13, atol=1e-15)
 
 
+@pytest.mark.parametrize("attn_type,W,lens", [(O.GLOBAL, 0, None), (O.LOCAL_SLIDING, 4, None),
+                                              (O.LOCAL_SLIDING, 6, (7, 3)), (O.GLOBAL, 0, (7, 1))])
+def test_prefill_chunk_equals_one_long_prefill(attn_type, W, lens):
+    # a sequence of N = start + T tokens prefilled as a cached first part and a
+    # chunk gives the chunk's rows of one prefill over all N tokens (the chunk's
+    # padding is that prefill's padding), and leaves the cache one prefill of
+    # all N tokens would leave
+    B, start, T, D, H, Hk, d_h, S = 2, 9, 7, 16, 4, 2, 8, 20
+    N = start + T
+    x = _rand(47, B, N, D)
+    w = _layer(48, D, H, Hk, d_h)
+    kw = dict(num_heads=H, num_kv_heads=Hk, head_dim=d_h, attn_type=attn_type, window=W,
+              rope_theta=1e4, rope_scale=1.0, query_scale=0.45)
+    ck = dict(num_kv_heads=Hk, head_dim=d_h, rope_theta=1e4, rope_scale=1.0)
+    pos = np.tile(np.arange(N), (B, 1))
+    nan = np.full((B, S, Hk, d_h), np.nan)
+    kc, vc = O.prefill_cache(x[:, :start], pos[:, :start], w["w_kv"], w["gamma_k"], nan, nan,
+                             **ck)
+    y, kc2, vc2 = O.prefill_chunk(x[:, start:], pos[:, start:], w["w_q"], w["w_kv"], w["w_o"],
+                                  w["gamma_q"], w["gamma_k"], kc, vc, start, **kw,
+                                  kv_valid_len=lens)
+    full_lens = None if lens is None else np.array(lens) + start
+    y_full = _prefill(x, w, kv_valid_len=full_lens, **kw)
+    np.testing.assert_allclose(y, y_full[:, start:], rtol=1e-12, atol=1e-14)
+    kf, vf = O.prefill_cache(x, pos, w["w_kv"], w["gamma_k"], nan, nan, kv_valid_len=full_lens,
+                             **ck)
+    np.testing.assert_array_equal(np.isnan(kc2), np.isnan(kf))
+    np.testing.assert_allclose(np.nan_to_num(kc2), np.nan_to_num(kf), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(np.nan_to_num(vc2), np.nan_to_num(vf), rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_chunk_from_empty_cache_is_plain_prefill():
+    B, T, D, H, Hk, d_h = 2, 8, 16, 2, 1, 8
+    x = _rand(49, B, T, D)
+    w = _layer(50, D, H, Hk, d_h)
+    kw = dict(num_heads=H, num_kv_heads=Hk, head_dim=d_h, attn_type=O.LOCAL_SLIDING, window=3,
+              rope_theta=1e6, rope_scale=8.0, query_scale=0.3)
+    pos = np.tile(np.arange(T), (B, 1))
+    zero = np.zeros((B, T, Hk, d_h))
+    y, _, _ = O.prefill_chunk(x, pos, w["w_q"], w["w_kv"], w["w_o"], w["gamma_q"],
+                              w["gamma_k"], zero, zero, 0, **kw)
+    np.testing.assert_allclose(y, _prefill(x, w, **kw), rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- sampled rows
 @pytest.mark.parametrize("attn_type,W,lens", [(O.LOCAL_SLIDING, 4, (17, 14)),
                                               (O.GLOBAL, 0, (17, 9))])
