@@ -98,7 +98,7 @@ DEVI void qkv_epilogue_impl(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, in
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane & 31, hh = lane >> 5;
 
-  __syncthreads();  // every wave is done with the k-loop stages
+  __syncthreads();  // every wave is done with the k-loop stages (and its loads have landed)
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
 #pragma unroll
@@ -344,6 +344,12 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
       b[j] = *reinterpret_cast<const bf16x8 *>(sb + b_fo[j] + 16 * ((2 * kk + hh) ^ b_sw[j]));
   };
 
+  // The epilogues below stage the C tile in the k-loop's LDS stages. The
+  // last iterations still have (clamped) k-tile loads in flight into those
+  // stages, so every wave waits for all of its loads before the epilogue's
+  // barrier: a load landing after the barrier would overwrite staged rows.
+  auto drain_loads = [&]() { __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm); };
+
   for (int kt = 0; kt < nk; ++kt) {
     // k-tile kt has landed for every wave; the MFMAs of the previous slice's
     // last step are still in the pipe while this slice's first reads go out
@@ -370,6 +376,7 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   }
   static_assert(kKK % 2 == 0, "step 0 of every slice reads into buffer 0");
 
+  drain_loads();
   if constexpr (kQkv) {
     qkv_epilogue<BM, BN, WM, WN, Cfg::kFM, Cfg::kFN>(acc, lds, m0, n0, M, ep);
     return;
