@@ -6,6 +6,7 @@
 // Every check runs before the first enqueue, so a validation error leaves
 // the stream untouched. The library keeps no state between calls.
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "../../include/gemma3_attn.h"
@@ -55,10 +56,18 @@ int check_desc(const gemma3_attn_desc *d, int32_t S) {
   return GEMMA3_OK;
 }
 
-AttnArgs attn_args(const gemma3_attn_desc *d, int T_pad) {
+AttnArgs attn_args(const gemma3_attn_desc *d, int T_pad, int q0 = 0) {
   return AttnArgs{d->B, d->T, d->H, d->H_kv, d->d_h, T_pad,
-                  d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window};
+                  d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window, q0};
 }
+
+// Workspace of a prefill chunk after `start` cached tokens: the prefill's
+// (projections, Q, the chunk's own K / V^T) followed by the attention's key
+// buffers over all start + T keys and their split-KV partials.
+struct ChunkLayout {
+  size_t kc, vtc, part, total;
+  int T_kpad;
+};
 
 int layout(const gemma3_attn_desc *d, int32_t S, gemma3_ws_layout *L) {
   int st = check_desc(d, S);
@@ -106,6 +115,23 @@ int layout(const gemma3_attn_desc *d, int32_t S, gemma3_ws_layout *L) {
     off = align_up(off + (size_t)L->ksplit_out * d->B * d->D * 4);
   }
   L->total_bytes = off;
+  return GEMMA3_OK;
+}
+
+int chunk_layout(const gemma3_attn_desc *d, int32_t start, gemma3_ws_layout *L, ChunkLayout *C) {
+  int st = layout(d, 0, L);
+  if (st != GEMMA3_OK) return st;
+  if (start < 0 || (long)start + d->T > INT32_MAX - kTokPad) return GEMMA3_ERR_SHAPE;
+  const size_t esz = elem_size(d->dtype);
+  C->T_kpad = div_up_h(start + d->T, kTokPad) * kTokPad;
+  size_t off = L->total_bytes;
+  C->kc = off;
+  off = align_up(off + (size_t)d->B * d->H_kv * C->T_kpad * d->d_h * esz);
+  C->vtc = off;
+  off = align_up(off + (size_t)d->B * d->H_kv * d->d_h * C->T_kpad * esz);
+  C->part = off;
+  if (d->dtype == GEMMA3_BF16) off = align_up(off + flash_attn_partial_bytes(attn_args(d, C->T_kpad, start)));
+  C->total = off;
   return GEMMA3_OK;
 }
 
@@ -319,6 +345,70 @@ int gemma3_attn_prefill_cache(const gemma3_attn_desc *desc, const void *x,
                                           desc->B, desc->T, L.T_pad, desc->H_kv, desc->d_h, S,
                                           s));
   return GEMMA3_OK;
+}
+
+size_t gemma3_attn_prefill_chunk_workspace_bytes(const gemma3_attn_desc *desc, int32_t start) {
+  gemma3_ws_layout L;
+  ChunkLayout C;
+  return chunk_layout(desc, start, &L, &C) == GEMMA3_OK ? C.total : 0;
+}
+
+int gemma3_attn_prefill_chunk(const gemma3_attn_desc *desc, const void *x,
+                              const int32_t *segment_pos, const int32_t *kv_valid_len,
+                              const gemma3_attn_weights *w, void *k_cache, void *v_cache,
+                              int32_t S, int32_t start, void *y, void *workspace,
+                              size_t workspace_bytes, void *hip_stream) {
+  gemma3_ws_layout L;
+  ChunkLayout C;
+  int st = chunk_layout(desc, start, &L, &C);
+  if (st != GEMMA3_OK) return st;
+  if (S < 1 || (long)start + desc->T > S) return GEMMA3_ERR_SHAPE;
+  if (!x || !segment_pos || !y || !k_cache || !v_cache) return GEMMA3_ERR_NULL;
+  if ((st = check_weights(w)) != GEMMA3_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache))
+    return GEMMA3_ERR_ALIGN;
+  if ((long)desc->B * S * desc->H_kv * desc->d_h >= (1L << 62)) return GEMMA3_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < C.total) return GEMMA3_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)hip_stream;
+  char *base = (char *)workspace;
+  const AttnArgs a = attn_args(desc, C.T_kpad, start);
+  // projections with QK-norm / RoPE (Q, and the chunk's K / V^T) ...
+  if (desc->dtype == GEMMA3_BF16) {
+    st = prefill_impl<bf16>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
+                            GEMMA3_STAGE_QKV_PROJ | GEMMA3_STAGE_QK_NORM);
+    if (st != GEMMA3_OK) return st;
+    // ... the chunk's keys and values into their slots, all start + T slots
+    // into the attention layouts, attention, output projection
+    RUN(launch_prefill_cache_write<bf16>((const bf16 *)(base + L.k), (const bf16 *)(base + L.vt),
+                                         segment_pos, kv_valid_len, (bf16 *)k_cache,
+                                         (bf16 *)v_cache, desc->B, desc->T, L.T_pad,
+                                         desc->H_kv, desc->d_h, S, s));
+    RUN(launch_cache_gather_keys<bf16>((const bf16 *)k_cache, (const bf16 *)v_cache, kv_valid_len,
+                                       (bf16 *)(base + C.kc), (bf16 *)(base + C.vtc), desc->B,
+                                       start, desc->T, C.T_kpad, desc->H_kv, desc->d_h, S, s));
+    RUN(launch_flash_attn_bf16((const bf16 *)(base + L.q), (const bf16 *)(base + C.kc),
+                               (const bf16 *)(base + C.vtc), kv_valid_len,
+                               (const bf16 *)w->gamma_k, (bf16 *)(base + L.o),
+                               C.part < C.total ? base + C.part : nullptr, a, false, s));
+    return prefill_impl<bf16>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
+                              GEMMA3_STAGE_OUT_PROJ);
+  }
+  st = prefill_impl<float>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
+                           GEMMA3_STAGE_QKV_PROJ | GEMMA3_STAGE_QK_NORM);
+  if (st != GEMMA3_OK) return st;
+  RUN(launch_prefill_cache_write<float>((const float *)(base + L.k), (const float *)(base + L.vt),
+                                        segment_pos, kv_valid_len, (float *)k_cache,
+                                        (float *)v_cache, desc->B, desc->T, L.T_pad, desc->H_kv,
+                                        desc->d_h, S, s));
+  RUN(launch_cache_gather_keys<float>((const float *)k_cache, (const float *)v_cache,
+                                      kv_valid_len, (float *)(base + C.kc),
+                                      (float *)(base + C.vtc), desc->B, start, desc->T, C.T_kpad,
+                                      desc->H_kv, desc->d_h, S, s));
+  RUN(launch_attn_f32((const float *)(base + L.q), (const float *)(base + C.kc),
+                      (const float *)(base + C.vtc), kv_valid_len, (float *)(base + L.o), a, s));
+  return prefill_impl<float>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
+                             GEMMA3_STAGE_OUT_PROJ);
 }
 
 int gemma3_attn_decode_stages(const gemma3_attn_desc *desc, const void *x,

@@ -158,11 +158,11 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
   g.kh = rest % a.Hk;
   g.b = rest / a.Hk;
   const int TQ = rows_per_wave * (4 / gp);
-  g.t_lo = g.qt * TQ;
+  g.t_lo = g.qt * TQ;  // query rows (absolute index: q0 + row)
   g.t_hi = min(a.T, g.t_lo + TQ);
-  g.len = kv_len ? kv_len[g.b] : a.T;
-  g.kv_begin = a.local ? max(0, g.t_lo - a.window + 1) : 0;
-  g.kv_end = min(g.t_hi, g.len);  // exclusive
+  g.len = a.q0 + (kv_len ? kv_len[g.b] : a.T);  // keys below it are valid
+  g.kv_begin = a.local ? max(0, a.q0 + g.t_lo - a.window + 1) : 0;
+  g.kv_end = min(a.q0 + g.t_hi, g.len);  // exclusive
   g.tile_begin = (g.kv_begin / kBN) * kBN;
   g.n_active = g.kv_end > g.kv_begin ? div_up(g.kv_end - g.tile_begin, chunk_keys) : 1;
   return g;
@@ -368,8 +368,9 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // one unsigned compare per element tests lo <= offset <= hi.
   auto mask_bits = [&](int s0, int rb) {
     const int base = s0 + 8 * hh;
-    int hi = min(my_t[rb], len - 1) - base;
-    int lo = (a.local ? my_t[rb] - a.window + 1 : -(1 << 30)) - base;
+    const int ta = a.q0 + my_t[rb];  // absolute index of the query
+    int hi = min(ta, len - 1) - base;
+    int lo = (a.local ? ta - a.window + 1 : -(1 << 30)) - base;
     if (hi < lo) {  // nothing allowed
       lo = 1 << 30;
       hi = lo;
@@ -557,8 +558,8 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // take the masked body.
   int it_lo = 0, it_hi = -1;
   {
-    const int hi_s0 = min(t_lo, len - 1) - (kBN - 1);  // s0 <= hi_s0
-    const int lo_s0 = a.local ? t_hi - a.window : INT_MIN / 2;  // s0 >= lo_s0
+    const int hi_s0 = min(a.q0 + t_lo, len - 1) - (kBN - 1);  // s0 <= hi_s0
+    const int lo_s0 = a.local ? a.q0 + t_hi - a.window : INT_MIN / 2;  // s0 >= lo_s0
     if (hi_s0 >= my_begin) it_hi = (hi_s0 - my_begin) / kBN;
     if (lo_s0 > my_begin) it_lo = div_up(lo_s0 - my_begin, kBN);
   }
@@ -786,8 +787,8 @@ Plan plan(const AttnArgs &a) {
   // Key tiles of query tile qt (data-independent: padding is ignored here).
   auto tiles_of = [&](int qt) {
     const int t_lo = qt * TQ, t_hi = min(a.T, t_lo + TQ);
-    const int kv_begin = a.local ? max(0, t_lo - a.window + 1) : 0;
-    return div_up_h(t_hi - (kv_begin / kBN) * kBN, kBN);
+    const int kv_begin = a.local ? max(0, a.q0 + t_lo - a.window + 1) : 0;
+    return div_up_h(a.q0 + t_hi - (kv_begin / kBN) * kBN, kBN);
   };
   int max_tiles = 0;
   for (int qt = 0; qt < p.n_qtiles; ++qt) max_tiles = max(max_tiles, tiles_of(qt));
@@ -810,7 +811,7 @@ Plan plan(const AttnArgs &a) {
     }
   }
   // one chunk covers every key range when there is no split
-  p.chunk_keys = p.n_split == 1 ? a.T + kBN : div_up_h(max_tiles, p.n_split) * kBN;
+  p.chunk_keys = p.n_split == 1 ? a.q0 + a.T + kBN : div_up_h(max_tiles, p.n_split) * kBN;
   return p;
 }
 

@@ -64,12 +64,13 @@ attn_f32(const float *__restrict__ q, const float *__restrict__ k, const float *
   __shared__ float qs[kMaxD];
   const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int D = a.d_h, G = a.H / a.Hk, kh = h / G;
-  const int len = kv_len ? kv_len[b] : a.T;
+  const int len = a.q0 + (kv_len ? kv_len[b] : a.T);  // keys below it are valid
   for (int c = lane; c < D; c += 64) qs[c] = q[(((size_t)b * a.H + h) * a.T + t) * D + c];
   __syncthreads();
 
-  const int lo = a.local ? max(0, t - a.window + 1) : 0;
-  const int hi = min(t, len - 1);  // inclusive
+  const int ta = a.q0 + t;  // absolute index of the query
+  const int lo = a.local ? max(0, ta - a.window + 1) : 0;
+  const int hi = min(ta, len - 1);  // inclusive
   const float *kb = k + ((size_t)b * a.Hk + kh) * a.T_pad * D;
   const float *vb = vt + ((size_t)b * a.Hk + kh) * D * a.T_pad;
   float m = -INFINITY, l = 0.f, acc[kMaxD / 64] = {};

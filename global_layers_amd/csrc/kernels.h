@@ -55,9 +55,14 @@ hipError_t launch_qk_norm_rope_decode(const float *part, int ksplit, const int32
                                       T *v_cache, int S, const NormRopeArgs &a, hipStream_t s);
 
 // K3 (prefill attention, bf16).
+// Queries are the T rows of q; their absolute index (the one the causal and
+// sliding masks use) is q0 + row. Keys have absolute indices 0 .. T_pad - 1
+// in k / vt; key s is valid below q0 + kv_len[b] (q0 + T without kv_len).
+// A plain prefill has q0 = 0; a chunk after q0 cached tokens has q0 > 0.
 struct AttnArgs {
   int B, T, H, Hk, d_h, T_pad;
   int local, window;
+  int q0;
 };
 // `partial` (flash_attn_partial_bytes(a) bytes, may be NULL when that is 0)
 // holds the split-KV partial outputs.
@@ -91,6 +96,13 @@ hipError_t launch_prefill_cache_write(const T *k, const T *vt, const int32_t *po
                                       const int32_t *kv_len, T *k_cache, T *v_cache, int B,
                                       int T_len, int T_pad, int Hk, int d_h, int S,
                                       hipStream_t s);
+
+// Cache slots 0 .. T_kpad - 1 into the attention layouts k [B,Hk,T_kpad,d_h]
+// and vt [B,Hk,d_h,T_kpad]; slots from q0 + kv_len[b] on become zeros.
+template <typename T>
+hipError_t launch_cache_gather_keys(const T *k_cache, const T *v_cache, const int32_t *kv_len,
+                                    T *k, T *vt, int B, int q0, int T_len, int T_kpad, int Hk,
+                                    int d_h, int S, hipStream_t s);
 
 template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int ksplit, T *y, long MN, hipStream_t s);

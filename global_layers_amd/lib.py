@@ -72,6 +72,8 @@ _lib.gemma3_layer_attn_type.restype = ctypes.c_int
 _lib.gemma3_layer_attn_type.argtypes = [ctypes.c_int32, ctypes.c_int32]
 _lib.gemma3_attn_workspace_bytes.restype = ctypes.c_size_t
 _lib.gemma3_attn_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32]
+_lib.gemma3_attn_prefill_chunk_workspace_bytes.restype = ctypes.c_size_t
+_lib.gemma3_attn_prefill_chunk_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32]
 _lib.gemma3_attn_workspace_layout.restype = ctypes.c_int
 _lib.gemma3_attn_workspace_layout.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
                                               ctypes.POINTER(WsLayout)]
@@ -84,6 +86,9 @@ for name, args in (("gemma3_attn_prefill", _PREFILL_ARGS),
                    ("gemma3_attn_prefill_cache",
                     [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                      ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+                   ("gemma3_attn_prefill_chunk",
+                    [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
+                     ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
                    ("gemma3_attn_decode", _DECODE_ARGS),
                    ("gemma3_attn_decode_stages", _DECODE_ARGS + [ctypes.c_uint32])):
     fn = getattr(_lib, name)
@@ -93,7 +98,8 @@ for name, args in (("gemma3_attn_prefill", _PREFILL_ARGS),
 EXPORTED = ("gemma3_attn_workspace_bytes", "gemma3_attn_prefill", "gemma3_attn_decode",
             "gemma3_layer_attn_type", "gemma3_attn_status_string", "gemma3_attn_abi_version",
             "gemma3_attn_workspace_layout", "gemma3_attn_prefill_stages",
-            "gemma3_attn_decode_stages", "gemma3_attn_prefill_cache")
+            "gemma3_attn_decode_stages", "gemma3_attn_prefill_cache",
+            "gemma3_attn_prefill_chunk", "gemma3_attn_prefill_chunk_workspace_bytes")
 
 
 class Gemma3AttnError(ValueError):
@@ -228,6 +234,43 @@ def prefill(x, segment_pos, weights: dict, *, H, H_kv, d_h, attn_type, window, r
     _check(_lib.gemma3_attn_prefill_stages(
         ctypes.byref(desc), _ptr(x), _ptr(segment_pos), _ptr(kv_valid_len), ctypes.byref(w),
         _ptr(y), _ptr(workspace), workspace.numel(), _stream(), stages))
+    return y
+
+
+def prefill_chunk(x, segment_pos, weights: dict, k_cache, v_cache, start: int, *, H, H_kv, d_h,
+                  attn_type, window, rope_theta, rope_scale, query_scale, kv_valid_len=None,
+                  workspace=None, y=None):
+    """y [B,T,D] for tokens start..start+T-1 of rows whose first `start` tokens
+    are in the caches [B,S,H_kv,d_h]; writes the chunk's slots
+    (see gemma3_attn_prefill_chunk)."""
+    dev = x.device
+    B, T, D = x.shape
+    S = k_cache.shape[1]
+    desc = make_desc(B=B, T=T, D=D, H=H, H_kv=H_kv, d_h=d_h, attn_type=attn_type,
+                     window=window, rope_theta=rope_theta, rope_scale=rope_scale,
+                     query_scale=query_scale, dtype=x.dtype)
+    _dev_tensor(x, x.dtype, "x", dev)
+    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
+    if segment_pos.shape != (B, T):
+        raise ValueError("segment_pos must be [B, T]")
+    if kv_valid_len is not None:
+        _dev_tensor(kv_valid_len, torch.int32, "kv_valid_len", dev)
+        if kv_valid_len.shape != (B,):
+            raise ValueError("kv_valid_len must be [B]")
+    for n, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(c, x.dtype, n, dev)
+        if c.shape != (B, S, H_kv, d_h):
+            raise ValueError(f"{n} must be [B, S, H_kv, d_h]")
+    w = _weights(weights, x.dtype, dev)
+    if workspace is None:
+        n = _lib.gemma3_attn_prefill_chunk_workspace_bytes(ctypes.byref(desc), start)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    _check(_lib.gemma3_attn_prefill_chunk(
+        ctypes.byref(desc), _ptr(x), _ptr(segment_pos), _ptr(kv_valid_len), ctypes.byref(w),
+        _ptr(k_cache), _ptr(v_cache), S, start, _ptr(y), _ptr(workspace), workspace.numel(),
+        _stream()))
     return y
 
 

@@ -160,6 +160,34 @@ int gemma3_attn_prefill_cache(const gemma3_attn_desc *desc, const void *x,
                               void *hip_stream);
 
 /*
+ * Prefill chunk: continues rows whose first `start` tokens are already in
+ * the left-aligned cache ("Gemma 3 Attention Block", How it works: the
+ * prefill steps, with the Cache passage's slot = position). The T tokens of
+ * x have indices start .. start+T-1 and segment_pos[b*T + t] should equal
+ * start + t (it feeds RoPE and names the slot written). Their rotated keys
+ * and values are written to the cache as gemma3_attn_prefill_cache does;
+ * then every query attends to cache slots 0 .. start+T-1 under the causal
+ * and padding masks (and the window on local layers) of one prefill over the
+ * whole sequence: keys at or past start + kv_valid_len[b] are blocked
+ * (start + T without kv_valid_len). Slots 0 .. start-1 must hold the rows'
+ * earlier keys and values (from gemma3_attn_prefill_cache, earlier chunks or
+ * decode steps). With start = 0 this is gemma3_attn_prefill_cache.
+ * Caches: [B, S, H_kv, d_h] device arrays of the descriptor's dtype,
+ * 16-byte aligned, start + T <= S. Workspace:
+ * gemma3_attn_prefill_chunk_workspace_bytes(desc, start) bytes (it grows with
+ * start: the attention reads its keys from a copy in its own layout).
+ * Errors: those of gemma3_attn_prefill; start < 0, S < 1 or start + T > S ->
+ * GEMMA3_ERR_SHAPE; a NULL cache -> GEMMA3_ERR_NULL; misaligned ->
+ * GEMMA3_ERR_ALIGN; a short workspace -> GEMMA3_ERR_WORKSPACE.
+ */
+size_t gemma3_attn_prefill_chunk_workspace_bytes(const gemma3_attn_desc *desc, int32_t start);
+int gemma3_attn_prefill_chunk(const gemma3_attn_desc *desc, const void *x,
+                              const int32_t *segment_pos, const int32_t *kv_valid_len,
+                              const gemma3_attn_weights *w, void *k_cache, void *v_cache,
+                              int32_t S, int32_t start, void *y, void *workspace,
+                              size_t workspace_bytes, void *hip_stream);
+
+/*
  * Decode: one token per row against a left-aligned cache of S slots
  * ("Gemma 3 Attention Block", How it works, Cache). Writes the rotated key
  * and the value of row b into k_cache/v_cache slot segment_pos[b], then

@@ -140,6 +140,30 @@ def test_prefill_cache_validation_status():
     assert _call_prefill_cache(_desc(d_h=96), ws_bytes=1 << 40) == 7
 
 
+def _call_prefill_chunk(desc, S=512, start=100, kc=FAKE, ws_bytes=None):
+    w = lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    n = (lib._lib.gemma3_attn_prefill_chunk_workspace_bytes(ctypes.byref(desc), start)
+         if ws_bytes is None else ws_bytes)
+    return lib._lib.gemma3_attn_prefill_chunk(ctypes.byref(desc), FAKE, FAKE, None,
+                                              ctypes.byref(w), kc, FAKE, S, start, FAKE, FAKE, n,
+                                              None)
+
+
+def test_prefill_chunk_validation_status():
+    d = _desc()  # T = 128
+    ws = lib._lib.gemma3_attn_prefill_chunk_workspace_bytes
+    assert ws(ctypes.byref(d), 0) > lib.workspace_bytes(d)
+    assert ws(ctypes.byref(d), 1000) > ws(ctypes.byref(d), 0)
+    assert ws(ctypes.byref(d), -1) == 0
+    assert _call_prefill_chunk(d, start=-1) == 2
+    assert _call_prefill_chunk(d, S=227, start=100) == 2    # start + T > S
+    assert _call_prefill_chunk(d, S=0, start=0) == 2
+    assert _call_prefill_chunk(d, kc=None) == 1
+    assert _call_prefill_chunk(d, kc=FAKE + 4) == 9
+    assert _call_prefill_chunk(d, ws_bytes=lib.workspace_bytes(d)) == 6
+    assert _call_prefill_chunk(_desc(d_h=96), ws_bytes=1 << 40) == 7
+
+
 def test_workspace_layout_prefill_and_decode():
     d = _desc(B=2, T=100, D=128, H=4, H_kv=2, d_h=64)
     L = lib.workspace_layout(d, 0)

@@ -236,6 +236,32 @@ def test_cfg4_sampled_rows(gpu_lib):
     _sampled(gpu_lib, W.WORKLOADS[4], range(2), rows)
 
 
+def test_repeats_on_dirty_workspaces_are_bitwise_equal(gpu_lib):
+    """The 4B-like local layer (fused QKV projection on 256x256 tiles) on a
+    fresh workspace and on workspaces pre-filled with different bytes: every
+    call must give the same bits. A projection epilogue that staged its tile
+    in LDS while k-tile loads into the same LDS were still in flight changed a
+    few output rows from one call to the next."""
+    w = W.WORKLOADS[3]
+    layer = w.layers[0]
+    inp = I.prefill_inputs(w, 0)
+    kw = layer_kw(w, layer)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    B, T, D = d["x"].shape
+    desc = gpu_lib.make_desc(B=B, T=T, D=D, dtype=d["x"].dtype, **kw)
+    ys = []
+    for fill in (None, 0xFF, 0x3C, 0x00):
+        log(f"workspace fill {fill}")
+        ws = gpu_lib.new_workspace(desc)
+        if fill is not None:
+            ws.fill_(fill)
+        ys.append(gpu_lib.prefill(d["x"], d["segment_pos"], weights_of(d),
+                                  kv_valid_len=d.get("kv_valid_len"), workspace=ws, **kw))
+        torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+
+
 # ---------------------------------------------------------------- structure
 @pytest.mark.parametrize("d_h", [128, 256])
 def test_window_at_least_T_is_bitwise_global(gpu_lib, d_h):
