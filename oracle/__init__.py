@@ -27,4 +27,7 @@ from .gemma3_oracle import (  # noqa: F401
     decode,
     prefill_cache,
     prefill_chunk,
+    gelu_tanh,
+    feed_forward,
+    block_prefill,
 )

@@ -291,6 +291,46 @@ def prefill_chunk(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, k_cache, v_c
     return y, kc, vc
 
 
+def gelu_tanh(u):
+    """The tanh form of GELU (the Flax default the "Full Gemma 3 Block" page
+    names for the MLP): 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))."""
+    u = np.asarray(u, dtype=np.float64)
+    return 0.5 * u * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (u + 0.044715 * u ** 3)))
+
+
+def feed_forward(u, w_gating, w_linear):
+    """GeGLU MLP ("Full Gemma 3 Block", How it works, MLP):
+    FFN(u) = (GELU(u W_g) * (u W_u)) W_d. Layouts (readings): w_gating
+    [2, D_ff, D] as stored with the transposed gating einsum (slice 0 = W_g,
+    slice 1 = W_u, each contracted over D); w_linear [D, D_ff], output-major
+    (W_d of shape (D_ff, D) transposed)."""
+    u = np.asarray(u, dtype=np.float64)
+    wg = np.asarray(w_gating, dtype=np.float64)
+    gate = u @ wg[0].T
+    up = u @ wg[1].T
+    return (gelu_tanh(gate) * up) @ np.asarray(w_linear, dtype=np.float64).T
+
+
+def block_prefill(x, segment_pos, attn_weights: dict, pre_attn_norm, post_attn_norm,
+                  pre_ffw_norm, post_ffw_norm, w_gating, w_linear, *, num_heads: int,
+                  num_kv_heads: int, head_dim: int, attn_type: str, window: int,
+                  rope_theta: float, rope_scale: float, query_scale: float,
+                  kv_valid_len=None):
+    """One Gemma 3 block over the residual stream x [B,T,D] ("Full Gemma 3
+    Block", How it works): a = post-norm(Attn(pre-norm(x))), h = x + a,
+    m = post-norm(FFN(pre-norm(h))), y = h + m. Each norm is RMSNorm over D
+    with (1 + gamma) and eps = 1e-6; Attn is `prefill` above."""
+    x = np.asarray(x, dtype=np.float64)
+    w = attn_weights
+    a = prefill(rms_norm(x, pre_attn_norm), segment_pos, w["w_q"], w["w_kv"], w["w_o"],
+                w["gamma_q"], w["gamma_k"], num_heads=num_heads, num_kv_heads=num_kv_heads,
+                head_dim=head_dim, attn_type=attn_type, window=window, rope_theta=rope_theta,
+                rope_scale=rope_scale, query_scale=query_scale, kv_valid_len=kv_valid_len)
+    h = x + rms_norm(a, post_attn_norm)
+    m = feed_forward(rms_norm(h, pre_ffw_norm), w_gating, w_linear)
+    return h + rms_norm(m, post_ffw_norm)
+
+
 def _prefill_rows(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, rows, H, Hk, d_h,
                   attn_type, window, rope_theta, rope_scale, query_scale, kv_valid_len):
     """Selected query rows of prefill (same steps as the full computation)."""

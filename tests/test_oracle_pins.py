@@ -570,6 +570,66 @@ def test_prefill_chunk_from_empty_cache_is_plain_prefill():
     np.testing.assert_allclose(y, _prefill(x, w, **kw), rtol=1e-13, atol=1e-15)
 
 
+# ---------------------------------------------------------------- full block (GeGLU MLP, norms)
+def test_gelu_tanh_against_torch_and_odd_part():
+    u = np.linspace(-8, 8, 1601)
+    ref = F.gelu(torch.from_numpy(u), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(u), ref, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(O.gelu_tanh(u) - O.gelu_tanh(-u), u, rtol=1e-14, atol=1e-15)
+    assert O.gelu_tanh(0.0) == 0.0
+
+
+def test_feed_forward_against_torch():
+    r = np.random.default_rng(51)
+    D, Dff = 24, 40
+    u = r.standard_normal((3, 5, D))
+    wg = r.standard_normal((2, Dff, D)) * D ** -0.5
+    wl = r.standard_normal((D, Dff)) * Dff ** -0.5
+    t = torch.from_numpy
+    ref = (F.gelu(t(u) @ t(wg[0]).T, approximate="tanh") * (t(u) @ t(wg[1]).T)) @ t(wl).T
+    np.testing.assert_allclose(O.feed_forward(u, wg, wl), ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+def _block_case(seed, zero_o=False, zero_ffn=False):
+    B, T, D, H, Hk, d_h, Dff = 2, 11, 16, 4, 2, 8, 24
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((B, T, D))
+    w = _layer(seed + 1, D, H, Hk, d_h)
+    if zero_o:
+        w["w_o"] = np.zeros_like(w["w_o"])
+    norms = [r.standard_normal(D) * 0.1 for _ in range(4)]
+    wg = r.standard_normal((2, Dff, D)) * D ** -0.5
+    wl = np.zeros((D, Dff)) if zero_ffn else r.standard_normal((D, Dff)) * Dff ** -0.5
+    kw = dict(num_heads=H, num_kv_heads=Hk, head_dim=d_h, attn_type=O.LOCAL_SLIDING, window=4,
+              rope_theta=1e4, rope_scale=1.0, query_scale=0.35)
+    pos = np.tile(np.arange(T), (B, 1))
+    return x, pos, w, norms, wg, wl, kw
+
+
+def test_block_with_silent_sublayers_is_identity():
+    # zero output projection and zero MLP output: both post-norms see zero
+    # vectors and give zero, so both residual adds leave x unchanged
+    x, pos, w, n, wg, wl, kw = _block_case(52, zero_o=True, zero_ffn=True)
+    y = O.block_prefill(x, pos, w, *n, wg, wl, **kw)
+    np.testing.assert_array_equal(y, x)
+
+
+def test_block_post_norm_sits_before_the_residual_add():
+    # with gamma_post = 0 each sublayer adds a vector of RMS ~1 over D to the
+    # stream (the post-norm output), whatever the stream's own scale
+    x, pos, w, n, wg, wl, kw = _block_case(53, zero_ffn=True)
+    n = [n[0], np.zeros_like(n[1]), n[2], n[3]]
+    for c in (1.0, 100.0):
+        y = O.block_prefill(c * x, pos, w, *n, wg, wl, **kw)
+        d = y - c * x
+        rms = np.sqrt(np.mean(d ** 2, axis=-1))
+        np.testing.assert_allclose(rms, 1.0, rtol=1e-4)
+    # and the attention sublayer alone is the pinned prefill of the pre-normed stream
+    a = _prefill(O.rms_norm(x, n[0]), w, **kw)
+    np.testing.assert_allclose(O.block_prefill(x, pos, w, *n, wg, wl, **kw),
+                               x + O.rms_norm(a, n[1]), rtol=1e-13, atol=1e-14)
+
+
 # ---------------------------------------------------------------- sampled rows
 @pytest.mark.parametrize("attn_type,W,lens", [(O.LOCAL_SLIDING, 4, (17, 14)),
                                               (O.GLOBAL, 0, (17, 9))])
