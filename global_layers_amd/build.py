@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgemma3_attn.so")
 SOURCES = ["api.cpp", "gemm_bf16.hip", "qk_norm_rope.hip", "flash_attn.hip",
-           "decode_attn.hip", "fp32_path.hip", "cache_write.hip"]
+           "decode_attn.hip", "fp32_path.hip", "cache_write.hip",
+           "block.hip"]
 ARCH = "gfx950"
 
 

@@ -135,6 +135,35 @@ int chunk_layout(const gemma3_attn_desc *d, int32_t start, gemma3_ws_layout *L, 
   return GEMMA3_OK;
 }
 
+// Block workspace: the attention's, then the normed stream (pre-attention,
+// later pre-MLP), the sublayer output (attention, later MLP), h, the MLP's
+// gate|up projection and its activation.
+struct BlockLayout {
+  size_t hn, a, h, gu, z, total;
+};
+
+int block_layout(const gemma3_attn_desc *d, int32_t D_ff, gemma3_ws_layout *L, BlockLayout *K) {
+  int st = layout(d, 0, L);
+  if (st != GEMMA3_OK) return st;
+  if (D_ff < 1) return GEMMA3_ERR_SHAPE;
+  if (d->D > 6144) return GEMMA3_ERR_UNSUPPORTED;
+  if (d->dtype == GEMMA3_BF16 && D_ff % 64 != 0) return GEMMA3_ERR_UNSUPPORTED;
+  const size_t esz = elem_size(d->dtype), M = (size_t)d->B * d->T;
+  size_t off = L->total_bytes;
+  K->hn = off;
+  off = align_up(off + M * d->D * esz);
+  K->a = off;
+  off = align_up(off + M * d->D * esz);
+  K->h = off;
+  off = align_up(off + M * d->D * esz);
+  K->gu = off;
+  off = align_up(off + M * 2 * (size_t)D_ff * esz);
+  K->z = off;
+  off = align_up(off + M * (size_t)D_ff * esz);
+  K->total = off;
+  return GEMMA3_OK;
+}
+
 int check_weights(const gemma3_attn_weights *w) {
   if (!w || !w->w_q || !w->w_kv || !w->w_o || !w->gamma_q || !w->gamma_k) return GEMMA3_ERR_NULL;
   if (!aligned16(w->w_q) || !aligned16(w->w_kv) || !aligned16(w->w_o)) return GEMMA3_ERR_ALIGN;
@@ -249,6 +278,35 @@ int decode_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
                           ypart, B, d->D, Nq, s));
     RUN(launch_splitk_reduce<T>(ypart, L.ksplit_out, (T *)y, (long)B * d->D, s));
   }
+  return GEMMA3_OK;
+}
+
+template <typename T>
+int block_impl(const gemma3_attn_desc *d, int D_ff, const T *x, const int32_t *pos,
+               const int32_t *kv_len, const gemma3_block_weights *w, T *y, char *base,
+               const gemma3_ws_layout &L, const BlockLayout &K, hipStream_t s) {
+  const int M = d->B * d->T, D = d->D;
+  T *hn = (T *)(base + K.hn), *a = (T *)(base + K.a), *h = (T *)(base + K.h);
+  T *gu = (T *)(base + K.gu), *z = (T *)(base + K.z);
+  RUN(launch_rms_norm_add<T>(nullptr, x, (const T *)w->pre_attn_norm, hn, M, D, s));
+  int st = prefill_impl<T>(d, hn, pos, kv_len, &w->attn, a, base, L, s, GEMMA3_STAGE_ALL);
+  if (st != GEMMA3_OK) return st;
+  RUN(launch_rms_norm_add<T>(x, a, (const T *)w->post_attn_norm, h, M, D, s));
+  RUN(launch_rms_norm_add<T>(nullptr, h, (const T *)w->pre_ffw_norm, hn, M, D, s));
+  if constexpr (sizeof(T) == 2) {
+    RUN(launch_gemm_bf16_nt(hn, (const bf16 *)w->w_gating, (const bf16 *)w->w_gating, 2 * D_ff,
+                            gu, M, 2 * D_ff, D, s));
+    RUN(launch_geglu<T>(gu, z, M, D_ff, s));
+    RUN(launch_gemm_bf16_nt(z, (const bf16 *)w->w_linear, (const bf16 *)w->w_linear, D, a, M, D,
+                            D_ff, s));
+  } else {
+    RUN(launch_gemm_f32_nt(hn, (const float *)w->w_gating, (const float *)w->w_gating, 2 * D_ff,
+                           gu, M, 2 * D_ff, D, s));
+    RUN(launch_geglu<T>(gu, z, M, D_ff, s));
+    RUN(launch_gemm_f32_nt(z, (const float *)w->w_linear, (const float *)w->w_linear, D, a, M,
+                           D, D_ff, s));
+  }
+  RUN(launch_rms_norm_add<T>(h, a, (const T *)w->post_ffw_norm, y, M, D, s));
   return GEMMA3_OK;
 }
 
@@ -409,6 +467,41 @@ int gemma3_attn_prefill_chunk(const gemma3_attn_desc *desc, const void *x,
                       (const float *)(base + C.vtc), kv_valid_len, (float *)(base + L.o), a, s));
   return prefill_impl<float>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
                              GEMMA3_STAGE_OUT_PROJ);
+}
+
+size_t gemma3_block_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff) {
+  gemma3_ws_layout L;
+  BlockLayout K;
+  return block_layout(desc, D_ff, &L, &K) == GEMMA3_OK ? K.total : 0;
+}
+
+
+int gemma3_block_prefill(const gemma3_attn_desc *desc, int32_t D_ff, const void *x,
+                         const int32_t *segment_pos, const int32_t *kv_valid_len,
+                         const gemma3_block_weights *w, void *y, void *workspace,
+                         size_t workspace_bytes, void *hip_stream) {
+  gemma3_ws_layout L;
+  BlockLayout K;
+  int st = block_layout(desc, D_ff, &L, &K);
+  if (st != GEMMA3_OK) return st;
+  if (!x || !segment_pos || !y || !w) return GEMMA3_ERR_NULL;
+  if ((st = check_weights(&w->attn)) != GEMMA3_OK) return st;
+  const void *bw[6] = {w->pre_attn_norm, w->post_attn_norm, w->pre_ffw_norm, w->post_ffw_norm,
+                       w->w_gating, w->w_linear};
+  for (const void *p : bw)
+    if (!p) return GEMMA3_ERR_NULL;
+  for (const void *p : bw)
+    if (!aligned16(p)) return GEMMA3_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(y)) return GEMMA3_ERR_ALIGN;
+  if (x == y) return GEMMA3_ERR_SHAPE;
+  if (!workspace || workspace_bytes < K.total) return GEMMA3_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (desc->dtype == GEMMA3_BF16)
+    return block_impl<bf16>(desc, D_ff, (const bf16 *)x, segment_pos, kv_valid_len, w, (bf16 *)y,
+                            (char *)workspace, L, K, s);
+  return block_impl<float>(desc, D_ff, (const float *)x, segment_pos, kv_valid_len, w,
+                           (float *)y, (char *)workspace, L, K, s);
 }
 
 int gemma3_attn_decode_stages(const gemma3_attn_desc *desc, const void *x,

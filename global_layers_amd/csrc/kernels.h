@@ -104,6 +104,14 @@ hipError_t launch_cache_gather_keys(const T *k_cache, const T *v_cache, const in
                                     T *k, T *vt, int B, int q0, int T_len, int T_kpad, int Hk,
                                     int d_h, int S, hipStream_t s);
 
+// Block pieces: out = (res ? res : 0) + RMSNorm(a) (1 + gamma) per row of D
+// (D <= 6144), and z = GELU_tanh(g) * u with gu rows [g | u] of 2 D_ff.
+template <typename T>
+hipError_t launch_rms_norm_add(const T *res, const T *a, const T *gamma, T *out, int M, int D,
+                               hipStream_t s);
+template <typename T>
+hipError_t launch_geglu(const T *gu, T *z, int M, int Dff, hipStream_t s);
+
 template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int ksplit, T *y, long MN, hipStream_t s);
 

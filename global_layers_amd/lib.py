@@ -77,6 +77,18 @@ _lib.gemma3_attn_prefill_chunk_workspace_bytes.argtypes = [ctypes.POINTER(Desc),
 _lib.gemma3_attn_workspace_layout.restype = ctypes.c_int
 _lib.gemma3_attn_workspace_layout.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
                                               ctypes.POINTER(WsLayout)]
+class BlockWeights(ctypes.Structure):
+    _fields_ = [("attn", Weights), ("pre_attn_norm", ctypes.c_void_p),
+                ("post_attn_norm", ctypes.c_void_p), ("pre_ffw_norm", ctypes.c_void_p),
+                ("post_ffw_norm", ctypes.c_void_p), ("w_gating", ctypes.c_void_p),
+                ("w_linear", ctypes.c_void_p)]
+
+
+_lib.gemma3_block_workspace_bytes.restype = ctypes.c_size_t
+_lib.gemma3_block_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32]
+_lib.gemma3_block_prefill.restype = ctypes.c_int
+_lib.gemma3_block_prefill.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32, _P, _P, _P,
+                                      ctypes.POINTER(BlockWeights), _P, _P, ctypes.c_size_t, _P]
 _PREFILL_ARGS = [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                  ctypes.c_size_t, _P]
 _DECODE_ARGS = [ctypes.POINTER(Desc), _P, _P, ctypes.POINTER(Weights), _P, _P, ctypes.c_int32,
@@ -99,7 +111,8 @@ EXPORTED = ("gemma3_attn_workspace_bytes", "gemma3_attn_prefill", "gemma3_attn_d
             "gemma3_layer_attn_type", "gemma3_attn_status_string", "gemma3_attn_abi_version",
             "gemma3_attn_workspace_layout", "gemma3_attn_prefill_stages",
             "gemma3_attn_decode_stages", "gemma3_attn_prefill_cache",
-            "gemma3_attn_prefill_chunk", "gemma3_attn_prefill_chunk_workspace_bytes")
+            "gemma3_attn_prefill_chunk", "gemma3_attn_prefill_chunk_workspace_bytes",
+            "gemma3_block_prefill", "gemma3_block_workspace_bytes")
 
 
 class Gemma3AttnError(ValueError):
@@ -271,6 +284,46 @@ def prefill_chunk(x, segment_pos, weights: dict, k_cache, v_cache, start: int, *
         ctypes.byref(desc), _ptr(x), _ptr(segment_pos), _ptr(kv_valid_len), ctypes.byref(w),
         _ptr(k_cache), _ptr(v_cache), S, start, _ptr(y), _ptr(workspace), workspace.numel(),
         _stream()))
+    return y
+
+
+BLOCK_KEYS = ("pre_attn_norm", "post_attn_norm", "pre_ffw_norm", "post_ffw_norm", "w_gating",
+              "w_linear")
+
+
+def block_prefill(x, segment_pos, weights: dict, *, H, H_kv, d_h, attn_type, window, rope_theta,
+                  rope_scale, query_scale, kv_valid_len=None, workspace=None, y=None):
+    """y [B,T,D] = one Gemma 3 block over the residual stream x (see
+    gemma3_block_prefill). weights: the attention's five tensors plus
+    BLOCK_KEYS (norms [D], w_gating [2, D_ff, D], w_linear [D, D_ff])."""
+    dev = x.device
+    B, T, D = x.shape
+    D_ff = weights["w_gating"].shape[1]
+    desc = make_desc(B=B, T=T, D=D, H=H, H_kv=H_kv, d_h=d_h, attn_type=attn_type,
+                     window=window, rope_theta=rope_theta, rope_scale=rope_scale,
+                     query_scale=query_scale, dtype=x.dtype)
+    _dev_tensor(x, x.dtype, "x", dev)
+    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
+    if segment_pos.shape != (B, T):
+        raise ValueError("segment_pos must be [B, T]")
+    if kv_valid_len is not None:
+        _dev_tensor(kv_valid_len, torch.int32, "kv_valid_len", dev)
+        if kv_valid_len.shape != (B,):
+            raise ValueError("kv_valid_len must be [B]")
+    for k in BLOCK_KEYS:
+        _dev_tensor(weights[k], x.dtype, k, dev)
+    if weights["w_gating"].shape != (2, D_ff, D) or weights["w_linear"].shape != (D, D_ff):
+        raise ValueError("w_gating must be [2, D_ff, D] and w_linear [D, D_ff]")
+    bw = BlockWeights(_weights(weights, x.dtype, dev),
+                      *(weights[k].data_ptr() for k in BLOCK_KEYS))
+    if workspace is None:
+        n = _lib.gemma3_block_workspace_bytes(ctypes.byref(desc), D_ff)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    _check(_lib.gemma3_block_prefill(ctypes.byref(desc), D_ff, _ptr(x), _ptr(segment_pos),
+                                     _ptr(kv_valid_len), ctypes.byref(bw), _ptr(y),
+                                     _ptr(workspace), workspace.numel(), _stream()))
     return y
 
 

@@ -1,6 +1,6 @@
 """Per-stage timing of the prefill path on the seeded synthetic workloads.
 
-    python global_layers_amd/stage_timer.py --workload 4 [--reps 10] [--warmup 3] [--cache]
+    python global_layers_amd/stage_timer.py --workload 4 [--reps 10] [--warmup 3] [--cache] [--block]
 
 Every layer of the workload goes through the C ABI one stage at a time
 (gemma3_attn_prefill_stages): the projection with its QK-norm / RoPE
@@ -12,13 +12,18 @@ projections 2 M K N, attention 4 d_h H per allowed (query, key) pair. With
 --cache, the whole layer also runs as gemma3_attn_prefill_cache into a cache
 of T slots; the difference to the plain call is the cache fill, printed with
 its algorithmic GB/s (each valid token's key and value read once and written
-once: 4 H_kv d_h elements). A profiling aid (for example under rocprofv3); the
-benchmark line is bench.py's.
+once: 4 H_kv d_h elements). With --block, the layer also runs as a whole
+Gemma 3 block (gemma3_block_prefill: norms, attention, GeGLU MLP with
+D_ff = 6 D on the 1B shape and 4 D otherwise, seeded synthetic weights), printed
+with its algorithmic TFLOP/s (the attention layer's plus 6 M D D_ff for the
+MLP). A profiling aid (for example under rocprofv3); the benchmark line is
+bench.py's.
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import os
 import sys
 
@@ -99,12 +104,48 @@ def time_layer(w, layer_id: int, reps: int, warmup: int, cache: bool = False) ->
     return out
 
 
+def time_block(w, layer_id: int, reps: int, warmup: int):
+    layer = w.layers[layer_id]
+    inp = I.prefill_inputs(w, layer_id)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    D = w.D
+    D_ff = 6 * D if w.D == 1152 else 4 * D
+    g = torch.Generator(device="cuda").manual_seed(1000 + layer_id)
+    dt = d["x"].dtype
+    for k in ("pre_attn_norm", "post_attn_norm", "pre_ffw_norm", "post_ffw_norm"):
+        d[k] = (torch.randn(D, generator=g, device="cuda") * 0.1).to(dt)
+    d["w_gating"] = (torch.randn((2, D_ff, D), generator=g, device="cuda") * D ** -0.5).to(dt)
+    d["w_linear"] = (torch.randn((D, D_ff), generator=g, device="cuda") * D_ff ** -0.5).to(dt)
+    kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
+              rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
+              query_scale=w.query_scale)
+    B, T, _ = d["x"].shape
+    desc = lib.make_desc(B=B, T=T, D=D, dtype=dt, **kw)
+    ws = torch.empty(lib._lib.gemma3_block_workspace_bytes(ctypes.byref(desc), D_ff),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(d["x"])
+    run = lambda: lib.block_prefill(d["x"], d["segment_pos"], d,  # noqa: E731
+                                    kv_valid_len=d.get("kv_valid_len"), workspace=ws, y=y, **kw)
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps, 6 * B * T * D * D_ff, D_ff
+
+
 def main() -> None:
     p = argparse.ArgumentParser()
     p.add_argument("--workload", default="4", help="workload ids, comma separated (2, 3, 4)")
     p.add_argument("--reps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--cache", action="store_true", help="also time the cache-filling prefill")
+    p.add_argument("--block", action="store_true", help="also time the whole Gemma 3 block")
     args = p.parse_args()
     if not torch.cuda.is_available():
         sys.exit("stage_timer needs a GPU")
@@ -122,6 +163,11 @@ def main() -> None:
             parts = [f"{n} {times[n]:9.1f} us {flops[n] / times[n] / 1e6:7.1f} TFLOP/s"
                      for n in ("qkv", "attention", "out")]
             print(f"workload {wid} layer {li} {attn_type:13s} " + " | ".join(parts), flush=True)
+            if args.block:
+                us, mlp_flops, D_ff = time_block(w, li, args.reps, args.warmup)
+                tot = sum(flops.values()) + mlp_flops
+                print(f"workload {wid} layer {li} {attn_type:13s} block (D_ff {D_ff}) {us:9.1f} us"
+                      f" {tot / us / 1e6:7.1f} TFLOP/s", flush=True)
             if args.cache:
                 lens = w.kv_valid_len() or (w.T,) * w.B
                 nbytes = 4 * sum(lens) * w.H_kv * w.d_h * (2 if w.dtype == "bf16" else 4)

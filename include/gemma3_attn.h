@@ -199,6 +199,40 @@ int gemma3_attn_decode(const gemma3_attn_desc *desc, const void *x,
                        void *k_cache, void *v_cache, int32_t S, void *y,
                        void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * One Gemma 3 block over the residual stream ("Full Gemma 3 Block", How it
+ * works): a = RMSNorm_post_attn(Attn(RMSNorm_pre_attn(x))), h = x + a,
+ * m = RMSNorm_post_ffw(FFN(RMSNorm_pre_ffw(h))), y = h + m, where Attn is
+ * gemma3_attn_prefill with `attn` and the descriptor, each RMSNorm runs over
+ * D with (1 + gamma) and eps = 1e-6, and
+ * FFN(u) = (GELU_tanh(u W_g) * (u W_u)) W_d.
+ * Weights (device, the descriptor's dtype, 16-byte aligned, caller-owned):
+ *   the four norm vectors [D];
+ *   w_gating [2, D_ff, D]: W_g rows then W_u rows, output-major (the
+ *            module's transposed gating einsum layout);
+ *   w_linear [D, D_ff]: output-major, i.e. W_d (D_ff x D) transposed.
+ * x and y are [B, T, D] and may not alias. Workspace:
+ * gemma3_block_workspace_bytes(desc, D_ff). Errors: those of
+ * gemma3_attn_prefill; D_ff < 1 -> GEMMA3_ERR_SHAPE; a NULL weight ->
+ * GEMMA3_ERR_NULL; misaligned -> GEMMA3_ERR_ALIGN; bf16 with D_ff not a
+ * multiple of 64, or D > 6144 -> GEMMA3_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  gemma3_attn_weights attn;
+  const void *pre_attn_norm;
+  const void *post_attn_norm;
+  const void *pre_ffw_norm;
+  const void *post_ffw_norm;
+  const void *w_gating;
+  const void *w_linear;
+} gemma3_block_weights;
+
+size_t gemma3_block_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff);
+int gemma3_block_prefill(const gemma3_attn_desc *desc, int32_t D_ff, const void *x,
+                         const int32_t *segment_pos, const int32_t *kv_valid_len,
+                         const gemma3_block_weights *w, void *y, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
+
 /* Host-only routing helper ("Global vs Local Layer Routing", How it works):
  * type of layer `layer` in a stack of `num_layers`: P[layer mod 6] with
  * P = (L, L, L, L, L, G). Returns -1 when layer is outside [0, num_layers). */

@@ -164,6 +164,29 @@ def test_prefill_chunk_validation_status():
     assert _call_prefill_chunk(_desc(d_h=96), ws_bytes=1 << 40) == 7
 
 
+def test_block_validation_status():
+    d = _desc()  # bf16, D = 256
+    f = lib._lib.gemma3_block_workspace_bytes
+    assert f(ctypes.byref(d), 512) > lib.workspace_bytes(d)
+    assert f(ctypes.byref(d), 0) == 0
+    assert f(ctypes.byref(d), 100) == 0                      # bf16 needs D_ff % 64 == 0
+    assert f(ctypes.byref(_desc(dtype=lib.F32)), 100) > 0
+    aw = lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+
+    def call(D_ff=512, x=FAKE, y=FAKE + 4096, bw=None, n=None):
+        bw = bw or lib.BlockWeights(aw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+        n = f(ctypes.byref(d), D_ff) if n is None else n
+        return lib._lib.gemma3_block_prefill(ctypes.byref(d), D_ff, x, FAKE, None,
+                                             ctypes.byref(bw), y, FAKE, n, None)
+    assert call(D_ff=0, n=1 << 40) == 2
+    assert call(D_ff=96, n=1 << 40) == 7
+    assert call(x=None) == 1
+    assert call(bw=lib.BlockWeights(aw, FAKE, None, FAKE, FAKE, FAKE, FAKE)) == 1
+    assert call(bw=lib.BlockWeights(aw, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE)) == 9
+    assert call(y=FAKE) == 2                                   # y may not alias x
+    assert call(n=16) == 6
+
+
 def test_workspace_layout_prefill_and_decode():
     d = _desc(B=2, T=100, D=128, H=4, H_kv=2, d_h=64)
     L = lib.workspace_layout(d, 0)
