@@ -30,4 +30,6 @@ from .gemma3_oracle import (  # noqa: F401
     gelu_tanh,
     feed_forward,
     block_prefill,
+    stack_prefill,
+    kv_cache_bytes,
 )

@@ -331,6 +331,43 @@ def block_prefill(x, segment_pos, attn_weights: dict, pre_attn_norm, post_attn_n
     return h + rms_norm(m, post_ffw_norm)
 
 
+def stack_prefill(x, segment_pos, layers: list, *, num_heads: int, num_kv_heads: int,
+                  head_dim: int, window: int, local_rope=(1e4, 1.0), global_rope=(1e6, 8.0),
+                  query_scale: float, kv_valid_len=None):
+    """A stack of Gemma 3 blocks ("Global vs Local Layer Routing", How it
+    works; "Full Gemma 3 Block"): layer l is a block of type
+    layer_attn_type(l, len(layers)) with that type's (theta, scale) and, when
+    local, the window; each layer's output is the next layer's input. layers:
+    one dict per layer with the attention weights and the block weights
+    (pre_attn_norm, post_attn_norm, pre_ffw_norm, post_ffw_norm, w_gating,
+    w_linear)."""
+    n = len(layers)
+    h = np.asarray(x, dtype=np.float64)
+    for l, w in enumerate(layers):
+        t = layer_attn_type(l, n)
+        theta, scale = local_rope if t == LOCAL_SLIDING else global_rope
+        h = block_prefill(h, segment_pos, w, w["pre_attn_norm"], w["post_attn_norm"],
+                          w["pre_ffw_norm"], w["post_ffw_norm"], w["w_gating"], w["w_linear"],
+                          num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                          attn_type=t, window=window, rope_theta=theta, rope_scale=scale,
+                          query_scale=query_scale, kv_valid_len=kv_valid_len)
+    return h
+
+
+def kv_cache_bytes(num_layers: int, batch: int, slots: int, num_kv_heads: int, head_dim: int,
+                   window: int, elem_bytes: int, local_window_only: bool) -> int:
+    """K and V cache bytes of a stack ("Gemma 3 Attention Block", Overview, and
+    "Global vs Local Layer Routing": local layers only ever read their last W
+    positions). Every layer holds K and V of [batch, S, H_kv, d_h]; with
+    local_window_only a local layer holds min(W, S) slots instead."""
+    per_slot = 2 * batch * num_kv_heads * head_dim * elem_bytes
+    total = 0
+    for l in range(num_layers):
+        local = layer_attn_type(l, num_layers) == LOCAL_SLIDING
+        total += per_slot * (min(window, slots) if local and local_window_only else slots)
+    return total
+
+
 def _prefill_rows(x, segment_pos, w_q, w_kv, w_o, gamma_q, gamma_k, rows, H, Hk, d_h,
                   attn_type, window, rope_theta, rope_scale, query_scale, kv_valid_len):
     """Selected query rows of prefill (same steps as the full computation)."""

@@ -630,6 +630,40 @@ def test_block_post_norm_sits_before_the_residual_add():
                                x + O.rms_norm(a, n[1]), rtol=1e-13, atol=1e-14)
 
 
+def test_stack_routes_layers_and_chains_blocks():
+    # two-layer stack = block(block(x)) with the routed types: layer 0 local,
+    # layer 1 local (no global slot in a stack of two); a stack of six ends
+    # with a global layer whose (theta, scale) is the global pair
+    x, pos, w, n, wg, wl, kw = _block_case(54)
+    lay = dict(w, pre_attn_norm=n[0], post_attn_norm=n[1], pre_ffw_norm=n[2], post_ffw_norm=n[3],
+               w_gating=wg, w_linear=wl)
+    common = dict(num_heads=kw["num_heads"], num_kv_heads=kw["num_kv_heads"],
+                  head_dim=kw["head_dim"], window=kw["window"], query_scale=kw["query_scale"])
+    bk = dict(kw, rope_theta=1e4, rope_scale=1.0)
+    y1 = O.block_prefill(x, pos, w, *n, wg, wl, **bk)
+    y2 = O.block_prefill(y1, pos, w, *n, wg, wl, **bk)
+    np.testing.assert_array_equal(O.stack_prefill(x, pos, [lay, lay], **common), y2)
+    h = x
+    for l in range(6):
+        t = O.GLOBAL if l == 5 else O.LOCAL_SLIDING
+        th, sc = (1e6, 8.0) if t == O.GLOBAL else (1e4, 1.0)
+        h = O.block_prefill(h, pos, w, *n, wg, wl, **dict(kw, attn_type=t, rope_theta=th,
+                                                        rope_scale=sc))
+    np.testing.assert_array_equal(O.stack_prefill(x, pos, [lay] * 6, **common), h)
+
+
+def test_kv_cache_footprint_closed_form():
+    # 26 layers (the 1B depth: 4 full six-slot tiles + 2 local): 4 global and
+    # 22 local layers; 128K slots, one KV head of 256, bf16, batch 1
+    per_slot = 2 * 1 * 1 * 256 * 2
+    S, W = 131072, 512
+    full = O.kv_cache_bytes(26, 1, S, 1, 256, W, 2, False)
+    win = O.kv_cache_bytes(26, 1, S, 1, 256, W, 2, True)
+    assert full == 26 * S * per_slot
+    assert win == (4 * S + 22 * W) * per_slot
+    assert O.kv_cache_bytes(5, 1, 100, 1, 256, 512, 2, True) == 5 * 100 * per_slot  # W > S
+
+
 # ---------------------------------------------------------------- sampled rows
 @pytest.mark.parametrize("attn_type,W,lens", [(O.LOCAL_SLIDING, 4, (17, 14)),
                                               (O.GLOBAL, 0, (17, 9))])
