@@ -504,6 +504,96 @@ int gemma3_block_prefill(const gemma3_attn_desc *desc, int32_t D_ff, const void 
                            (float *)y, (char *)workspace, L, K, s);
 }
 
+namespace {
+gemma3_attn_desc layer_desc(const gemma3_attn_desc *d, const gemma3_stack_config *c, int l) {
+  gemma3_attn_desc e = *d;
+  const bool global = gemma3_layer_attn_type(l, c->num_layers) == GEMMA3_ATTN_GLOBAL;
+  e.attn_type = global ? GEMMA3_ATTN_GLOBAL : GEMMA3_ATTN_LOCAL_SLIDING;
+  e.window = c->window;
+  e.rope_theta = global ? c->global_theta : c->local_theta;
+  e.rope_scale = global ? c->global_scale : c->local_scale;
+  return e;
+}
+
+// Every layer's block workspace (the largest), then two residual buffers the
+// layers alternate between.
+int stack_layout(const gemma3_attn_desc *d, int32_t D_ff, const gemma3_stack_config *c,
+                 size_t *res0, size_t *total) {
+  if (!d || !c) return GEMMA3_ERR_NULL;
+  if (c->num_layers < 1) return GEMMA3_ERR_SHAPE;
+  size_t mx = 0;
+  for (int l = 0; l < c->num_layers; ++l) {
+    const gemma3_attn_desc e = layer_desc(d, c, l);
+    gemma3_ws_layout L;
+    BlockLayout K;
+    const int st = block_layout(&e, D_ff, &L, &K);
+    if (st != GEMMA3_OK) return st;
+    mx = K.total > mx ? K.total : mx;
+  }
+  const size_t res = (size_t)d->B * d->T * d->D * elem_size(d->dtype);
+  *res0 = mx;
+  *total = align_up(mx + res) + align_up(res);
+  return GEMMA3_OK;
+}
+}  // namespace
+
+size_t gemma3_stack_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff,
+                                    const gemma3_stack_config *cfg) {
+  size_t r0, tot;
+  return stack_layout(desc, D_ff, cfg, &r0, &tot) == GEMMA3_OK ? tot : 0;
+}
+
+int gemma3_stack_prefill(const gemma3_attn_desc *desc, int32_t D_ff,
+                         const gemma3_stack_config *cfg, const void *x,
+                         const int32_t *segment_pos, const int32_t *kv_valid_len,
+                         const gemma3_block_weights *layers, void *y, void *workspace,
+                         size_t workspace_bytes, void *hip_stream) {
+  size_t r0, total;
+  int st = stack_layout(desc, D_ff, cfg, &r0, &total);
+  if (st != GEMMA3_OK) return st;
+  if (!x || !segment_pos || !y || !layers) return GEMMA3_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return GEMMA3_ERR_ALIGN;
+  if (x == y) return GEMMA3_ERR_SHAPE;
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    const gemma3_block_weights *w = &layers[l];
+    if ((st = check_weights(&w->attn)) != GEMMA3_OK) return st;
+    const void *bw[6] = {w->pre_attn_norm, w->post_attn_norm, w->pre_ffw_norm,
+                         w->post_ffw_norm, w->w_gating, w->w_linear};
+    for (const void *p : bw)
+      if (!p) return GEMMA3_ERR_NULL;
+    for (const void *p : bw)
+      if (!aligned16(p)) return GEMMA3_ERR_ALIGN;
+  }
+  if (!workspace || workspace_bytes < total) return GEMMA3_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
+  char *base = (char *)workspace;
+  const size_t res = (size_t)desc->B * desc->T * desc->D * elem_size(desc->dtype);
+  void *buf[2] = {base + r0, base + align_up(r0 + res)};
+  const void *in = x;
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    void *out = l == cfg->num_layers - 1 ? y : buf[l & 1];
+    const gemma3_attn_desc e = layer_desc(desc, cfg, l);
+    st = gemma3_block_prefill(&e, D_ff, in, segment_pos, kv_valid_len, &layers[l], out,
+                              workspace, r0, hip_stream);
+    if (st != GEMMA3_OK) return st;
+    in = out;
+  }
+  return GEMMA3_OK;
+}
+
+size_t gemma3_kv_cache_bytes(int32_t num_layers, int32_t B, int32_t S, int32_t H_kv, int32_t d_h,
+                             int32_t window, int32_t dtype, int32_t local_window_only) {
+  if (num_layers < 1 || B < 1 || S < 1 || H_kv < 1 || d_h < 1 || window < 1) return 0;
+  if (dtype != GEMMA3_F32 && dtype != GEMMA3_BF16) return 0;
+  const size_t per_slot = 2 * (size_t)B * H_kv * d_h * elem_size(dtype);
+  size_t total = 0;
+  for (int l = 0; l < num_layers; ++l) {
+    const bool local = gemma3_layer_attn_type(l, num_layers) == GEMMA3_ATTN_LOCAL_SLIDING;
+    total += per_slot * (size_t)(local && local_window_only && window < S ? window : S);
+  }
+  return total;
+}
+
 int gemma3_attn_decode_stages(const gemma3_attn_desc *desc, const void *x,
                               const int32_t *segment_pos, const gemma3_attn_weights *w,
                               void *k_cache, void *v_cache, int32_t S, void *y, void *workspace,

@@ -89,6 +89,21 @@ _lib.gemma3_block_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int
 _lib.gemma3_block_prefill.restype = ctypes.c_int
 _lib.gemma3_block_prefill.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32, _P, _P, _P,
                                       ctypes.POINTER(BlockWeights), _P, _P, ctypes.c_size_t, _P]
+class StackConfig(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("local_theta", ctypes.c_float), ("local_scale", ctypes.c_float),
+                ("global_theta", ctypes.c_float), ("global_scale", ctypes.c_float)]
+
+
+_lib.gemma3_stack_workspace_bytes.restype = ctypes.c_size_t
+_lib.gemma3_stack_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                              ctypes.POINTER(StackConfig)]
+_lib.gemma3_stack_prefill.restype = ctypes.c_int
+_lib.gemma3_stack_prefill.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                      ctypes.POINTER(StackConfig), _P, _P, _P,
+                                      ctypes.POINTER(BlockWeights), _P, _P, ctypes.c_size_t, _P]
+_lib.gemma3_kv_cache_bytes.restype = ctypes.c_size_t
+_lib.gemma3_kv_cache_bytes.argtypes = [ctypes.c_int32] * 8
 _PREFILL_ARGS = [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                  ctypes.c_size_t, _P]
 _DECODE_ARGS = [ctypes.POINTER(Desc), _P, _P, ctypes.POINTER(Weights), _P, _P, ctypes.c_int32,
@@ -112,7 +127,8 @@ EXPORTED = ("gemma3_attn_workspace_bytes", "gemma3_attn_prefill", "gemma3_attn_d
             "gemma3_attn_workspace_layout", "gemma3_attn_prefill_stages",
             "gemma3_attn_decode_stages", "gemma3_attn_prefill_cache",
             "gemma3_attn_prefill_chunk", "gemma3_attn_prefill_chunk_workspace_bytes",
-            "gemma3_block_prefill", "gemma3_block_workspace_bytes")
+            "gemma3_block_prefill", "gemma3_block_workspace_bytes", "gemma3_stack_prefill",
+            "gemma3_stack_workspace_bytes", "gemma3_kv_cache_bytes")
 
 
 class Gemma3AttnError(ValueError):
@@ -325,6 +341,51 @@ def block_prefill(x, segment_pos, weights: dict, *, H, H_kv, d_h, attn_type, win
                                      _ptr(kv_valid_len), ctypes.byref(bw), _ptr(y),
                                      _ptr(workspace), workspace.numel(), _stream()))
     return y
+
+
+def stack_prefill(x, segment_pos, layers: list, *, H, H_kv, d_h, window, query_scale,
+                  local_rope=(1e4, 1.0), global_rope=(1e6, 8.0), kv_valid_len=None,
+                  workspace=None, y=None):
+    """y [B,T,D] of a routed stack of blocks, one weights dict per layer (as
+    block_prefill takes); layer l's type is layer_attn_type(l, len(layers))
+    (see gemma3_stack_prefill)."""
+    dev = x.device
+    B, T, D = x.shape
+    n = len(layers)
+    D_ff = layers[0]["w_gating"].shape[1]
+    desc = make_desc(B=B, T=T, D=D, H=H, H_kv=H_kv, d_h=d_h, attn_type="GLOBAL", window=window,
+                     rope_theta=global_rope[0], rope_scale=global_rope[1],
+                     query_scale=query_scale, dtype=x.dtype)
+    cfg = StackConfig(n, window, local_rope[0], local_rope[1], global_rope[0], global_rope[1])
+    _dev_tensor(x, x.dtype, "x", dev)
+    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
+    if segment_pos.shape != (B, T):
+        raise ValueError("segment_pos must be [B, T]")
+    if kv_valid_len is not None:
+        _dev_tensor(kv_valid_len, torch.int32, "kv_valid_len", dev)
+    arr = (BlockWeights * n)()
+    for l, w in enumerate(layers):
+        for k in BLOCK_KEYS:
+            _dev_tensor(w[k], x.dtype, k, dev)
+        if w["w_gating"].shape != (2, D_ff, D) or w["w_linear"].shape != (D, D_ff):
+            raise ValueError("every layer needs w_gating [2, D_ff, D] and w_linear [D, D_ff]")
+        arr[l] = BlockWeights(_weights(w, x.dtype, dev), *(w[k].data_ptr() for k in BLOCK_KEYS))
+    if workspace is None:
+        nb = _lib.gemma3_stack_workspace_bytes(ctypes.byref(desc), D_ff, ctypes.byref(cfg))
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    _check(_lib.gemma3_stack_prefill(ctypes.byref(desc), D_ff, ctypes.byref(cfg), _ptr(x),
+                                     _ptr(segment_pos), _ptr(kv_valid_len), arr, _ptr(y),
+                                     _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def kv_cache_bytes(num_layers, B, S, H_kv, d_h, window, dtype, local_window_only) -> int:
+    """K and V cache bytes of a stack (see gemma3_kv_cache_bytes)."""
+    dt = _DTYPES.get(dtype, dtype)
+    return _lib.gemma3_kv_cache_bytes(num_layers, B, S, H_kv, d_h, window, dt,
+                                      1 if local_window_only else 0)
 
 
 def decode(x, segment_pos, weights: dict, k_cache, v_cache, *, H, H_kv, d_h, attn_type, window,

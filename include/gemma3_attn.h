@@ -233,6 +233,47 @@ int gemma3_block_prefill(const gemma3_attn_desc *desc, int32_t D_ff, const void 
                          const gemma3_block_weights *w, void *y, void *workspace,
                          size_t workspace_bytes, void *hip_stream);
 
+/*
+ * A routed stack of Gemma 3 blocks ("Global vs Local Layer Routing", How it
+ * works; "Full Gemma 3 Block"): layer l is gemma3_block_prefill with type
+ * gemma3_layer_attn_type(l, num_layers), that type's (theta, scale) and, on
+ * local layers, `window`; each layer's output is the next layer's input, the
+ * last layer's is y. The descriptor gives B, T, D, H, H_kv, d_h, query_scale
+ * and dtype (its attn_type, window, rope_theta and rope_scale are replaced per
+ * layer). `layers` is a host array of num_layers block weights (device
+ * tensors as in gemma3_block_prefill). Workspace:
+ * gemma3_stack_workspace_bytes(desc, D_ff, cfg). Errors: those of
+ * gemma3_block_prefill for any layer, checked for every layer before anything
+ * is enqueued; num_layers < 1 -> GEMMA3_ERR_SHAPE; NULL cfg or layers ->
+ * GEMMA3_ERR_NULL.
+ */
+typedef struct {
+  int32_t num_layers;
+  int32_t window;          /* W of the local layers */
+  float local_theta;       /* 1e4 */
+  float local_scale;       /* 1 */
+  float global_theta;      /* 1e6 */
+  float global_scale;      /* 8 on 4B/12B/27B shapes, 1 otherwise */
+} gemma3_stack_config;
+
+size_t gemma3_stack_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff,
+                                    const gemma3_stack_config *cfg);
+int gemma3_stack_prefill(const gemma3_attn_desc *desc, int32_t D_ff,
+                         const gemma3_stack_config *cfg, const void *x,
+                         const int32_t *segment_pos, const int32_t *kv_valid_len,
+                         const gemma3_block_weights *layers, void *y, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Host-only KV-cache footprint of a stack (bytes of K and V): every layer
+ * holds [B, S, H_kv, d_h] of `dtype` (the left-aligned caches
+ * gemma3_attn_decode reads); with local_window_only != 0 a local layer counts
+ * min(window, S) slots, what it needs when only its window is kept (local
+ * layers never read older positions). 0 for invalid arguments.
+ */
+size_t gemma3_kv_cache_bytes(int32_t num_layers, int32_t B, int32_t S, int32_t H_kv, int32_t d_h,
+                             int32_t window, int32_t dtype, int32_t local_window_only);
+
 /* Host-only routing helper ("Global vs Local Layer Routing", How it works):
  * type of layer `layer` in a stack of `num_layers`: P[layer mod 6] with
  * P = (L, L, L, L, L, G). Returns -1 when layer is outside [0, num_layers). */

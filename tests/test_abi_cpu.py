@@ -187,6 +187,35 @@ def test_block_validation_status():
     assert call(n=16) == 6
 
 
+def test_kv_cache_footprint_matches_oracle():
+    import oracle as O
+    for args in ((26, 1, 131072, 1, 256, 512), (34, 16, 131072, 8, 256, 1024),
+                 (62, 2, 32768, 16, 128, 1024), (5, 1, 100, 1, 256, 512), (1, 3, 10, 2, 64, 4)):
+        for dt, esz in ((lib.BF16, 2), (lib.F32, 4)):
+            for only in (False, True):
+                assert lib.kv_cache_bytes(*args, dt, only) == O.kv_cache_bytes(*args, esz, only)
+    assert lib.kv_cache_bytes(0, 1, 10, 1, 64, 4, lib.BF16, True) == 0
+
+
+def test_stack_validation_status():
+    d = _desc()
+    cfg = lib.StackConfig(7, 64, 1e4, 1.0, 1e6, 8.0)
+    f = lib._lib.gemma3_stack_workspace_bytes
+    n = f(ctypes.byref(d), 512, ctypes.byref(cfg))
+    assert n > lib._lib.gemma3_block_workspace_bytes(ctypes.byref(d), 512)
+    assert f(ctypes.byref(d), 512, ctypes.byref(lib.StackConfig(0, 64, 1e4, 1.0, 1e6, 8.0))) == 0
+    assert f(ctypes.byref(d), 512, ctypes.byref(lib.StackConfig(6, 0, 1e4, 1.0, 1e6, 8.0))) == 0
+    aw = lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    good = lib.BlockWeights(aw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    arr = (lib.BlockWeights * 7)(*([good] * 7))
+    call = lambda a, ws=n: lib._lib.gemma3_stack_prefill(  # noqa: E731
+        ctypes.byref(d), 512, ctypes.byref(cfg), FAKE, FAKE, None, a, FAKE + 4096, FAKE, ws, None)
+    bad = (lib.BlockWeights * 7)(*([good] * 6 + [lib.BlockWeights(aw, FAKE, FAKE, FAKE, FAKE,
+                                                                    FAKE, None)]))
+    assert call(bad) == 1                                       # the last layer is checked too
+    assert call(arr, ws=16) == 6
+
+
 def test_workspace_layout_prefill_and_decode():
     d = _desc(B=2, T=100, D=128, H=4, H_kv=2, d_h=64)
     L = lib.workspace_layout(d, 0)
