@@ -30,6 +30,7 @@ from .gemma3_oracle import (  # noqa: F401
     gelu_tanh,
     feed_forward,
     block_prefill,
+    block_decode,
     stack_prefill,
     kv_cache_bytes,
 )

@@ -331,6 +331,27 @@ def block_prefill(x, segment_pos, attn_weights: dict, pre_attn_norm, post_attn_n
     return h + rms_norm(m, post_ffw_norm)
 
 
+def block_decode(x, segment_pos, attn_weights: dict, pre_attn_norm, post_attn_norm,
+                 pre_ffw_norm, post_ffw_norm, w_gating, w_linear, k_cache, v_cache, *,
+                 num_heads: int, num_kv_heads: int, head_dim: int, attn_type: str, window: int,
+                 rope_theta: float, rope_scale: float, query_scale: float):
+    """One decode step of a whole block ("Full Gemma 3 Block" around the
+    decode step of "Gemma 3 Attention Block", Cache): the attention sublayer
+    is `decode` on the pre-normed token (the cache holds keys and values of
+    the pre-normed stream), the rest as in block_prefill. Returns y [B,1,D]
+    and the (k, v) written at slot segment_pos[b]."""
+    x = np.asarray(x, dtype=np.float64)
+    w = attn_weights
+    a, k_new, v_new = decode(rms_norm(x, pre_attn_norm), segment_pos, w["w_q"], w["w_kv"],
+                             w["w_o"], w["gamma_q"], w["gamma_k"], k_cache, v_cache,
+                             num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                             attn_type=attn_type, window=window, rope_theta=rope_theta,
+                             rope_scale=rope_scale, query_scale=query_scale)
+    h = x + rms_norm(a, post_attn_norm)
+    m = feed_forward(rms_norm(h, pre_ffw_norm), w_gating, w_linear)
+    return h + rms_norm(m, post_ffw_norm), k_new, v_new
+
+
 def stack_prefill(x, segment_pos, layers: list, *, num_heads: int, num_kv_heads: int,
                   head_dim: int, window: int, local_rope=(1e4, 1.0), global_rope=(1e6, 8.0),
                   query_scale: float, kv_valid_len=None):

@@ -652,6 +652,25 @@ def test_stack_routes_layers_and_chains_blocks():
     np.testing.assert_array_equal(O.stack_prefill(x, pos, [lay] * 6, **common), h)
 
 
+@pytest.mark.parametrize("attn_type,W", [(O.GLOBAL, 0), (O.LOCAL_SLIDING, 4)])
+def test_block_decode_continues_block_prefill(attn_type, W):
+    # the cache of a block holds the keys and values of its pre-normed stream:
+    # filled from tokens 0..t-1, a block decode step of token t gives the last
+    # row of a block prefill over tokens 0..t
+    x, pos, w, n, wg, wl, kw = _block_case(55)
+    kw = dict(kw, attn_type=attn_type, window=W)
+    t, S = 8, 12
+    B, _, D = x.shape
+    Hk, d_h = kw["num_kv_heads"], kw["head_dim"]
+    nan = np.full((B, S, Hk, d_h), np.nan)
+    kc, vc = O.prefill_cache(O.rms_norm(x[:, :t], n[0]), pos[:, :t], w["w_kv"], w["gamma_k"],
+                             nan, nan, num_kv_heads=Hk, head_dim=d_h,
+                             rope_theta=kw["rope_theta"], rope_scale=kw["rope_scale"])
+    y, _, _ = O.block_decode(x[:, t:t + 1], np.full((B, 1), t), w, *n, wg, wl, kc, vc, **kw)
+    y_ref = O.block_prefill(x[:, :t + 1], pos[:, :t + 1], w, *n, wg, wl, **kw)[:, t]
+    np.testing.assert_allclose(y[:, 0], y_ref, rtol=1e-12, atol=1e-13)
+
+
 def test_kv_cache_footprint_closed_form():
     # 26 layers (the 1B depth: 4 full six-slot tiles + 2 local): 4 global and
     # 22 local layers; 128K slots, one KV head of 256, bf16, batch 1
