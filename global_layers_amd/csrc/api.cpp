@@ -164,6 +164,44 @@ int block_layout(const gemma3_attn_desc *d, int32_t D_ff, gemma3_ws_layout *L, B
   return GEMMA3_OK;
 }
 
+// Block decode workspace: the attention decode's, then the normed token, the
+// sublayer output, h, gate|up, the activation and the fp32 split-K partials
+// of the MLP's two projections.
+struct BlockDecodeLayout {
+  size_t hn, a, h, gu, z, part, total;
+  int ks_gu, ks_dn;
+};
+
+int block_decode_layout(const gemma3_attn_desc *d, int32_t D_ff, int32_t S, gemma3_ws_layout *L,
+                        BlockDecodeLayout *K) {
+  if (S < 1) return d ? GEMMA3_ERR_SHAPE : GEMMA3_ERR_NULL;
+  int st = layout(d, S, L);
+  if (st != GEMMA3_OK) return st;
+  if (D_ff < 1) return GEMMA3_ERR_SHAPE;
+  if (d->D > 6144) return GEMMA3_ERR_UNSUPPORTED;
+  const bool bf = d->dtype == GEMMA3_BF16;
+  if (bf && D_ff % 64 != 0) return GEMMA3_ERR_UNSUPPORTED;
+  const size_t esz = elem_size(d->dtype), B = d->B;
+  size_t off = L->total_bytes;
+  K->hn = off;
+  off = align_up(off + B * d->D * esz);
+  K->a = off;
+  off = align_up(off + B * d->D * esz);
+  K->h = off;
+  off = align_up(off + B * d->D * esz);
+  K->gu = off;
+  off = align_up(off + B * 2 * (size_t)D_ff * esz);
+  K->z = off;
+  off = align_up(off + B * (size_t)D_ff * esz);
+  K->ks_gu = bf ? gemv_ksplit(2 * D_ff, d->D) : 1;
+  K->ks_dn = bf ? gemv_ksplit(d->D, D_ff) : 1;
+  K->part = off;
+  const size_t p1 = (size_t)K->ks_gu * B * 2 * D_ff, p2 = (size_t)K->ks_dn * B * d->D;
+  off = align_up(off + (p1 > p2 ? p1 : p2) * 4);
+  K->total = off;
+  return GEMMA3_OK;
+}
+
 int check_weights(const gemma3_attn_weights *w) {
   if (!w || !w->w_q || !w->w_kv || !w->w_o || !w->gamma_q || !w->gamma_k) return GEMMA3_ERR_NULL;
   if (!aligned16(w->w_q) || !aligned16(w->w_kv) || !aligned16(w->w_o)) return GEMMA3_ERR_ALIGN;
@@ -307,6 +345,41 @@ int block_impl(const gemma3_attn_desc *d, int D_ff, const T *x, const int32_t *p
                            D, D_ff, s));
   }
   RUN(launch_rms_norm_add<T>(h, a, (const T *)w->post_ffw_norm, y, M, D, s));
+  return GEMMA3_OK;
+}
+
+template <typename T>
+int block_decode_impl(const gemma3_attn_desc *d, int D_ff, const T *x, const int32_t *pos,
+                      const gemma3_block_weights *w, void *kc, void *vc, int32_t S, T *y,
+                      char *base, const gemma3_ws_layout &L, const BlockDecodeLayout &K,
+                      hipStream_t s) {
+  const int B = d->B, D = d->D;
+  T *hn = (T *)(base + K.hn), *a = (T *)(base + K.a), *h = (T *)(base + K.h);
+  T *gu = (T *)(base + K.gu), *z = (T *)(base + K.z);
+  float *part = (float *)(base + K.part);
+  RUN(launch_rms_norm_add<T>(nullptr, x, (const T *)w->pre_attn_norm, hn, B, D, s));
+  int st = decode_impl<T>(d, hn, pos, &w->attn, kc, vc, S, a, base, L, s, GEMMA3_DSTAGE_ALL);
+  if (st != GEMMA3_OK) return st;
+  RUN(launch_rms_norm_add<T>(x, a, (const T *)w->post_attn_norm, h, B, D, s));
+  RUN(launch_rms_norm_add<T>(nullptr, h, (const T *)w->pre_ffw_norm, hn, B, D, s));
+  if constexpr (sizeof(T) == 2) {
+    RUN(launch_gemv16_bf16(hn, (const bf16 *)w->w_gating, (const bf16 *)w->w_gating, 2 * D_ff,
+                           part, B, 2 * D_ff, D, K.ks_gu, s));
+  } else {
+    RUN(launch_gemv_f32(hn, (const float *)w->w_gating, (const float *)w->w_gating, 2 * D_ff,
+                        part, B, 2 * D_ff, D, s));
+  }
+  RUN(launch_splitk_reduce<T>(part, K.ks_gu, gu, (long)B * 2 * D_ff, s));
+  RUN(launch_geglu<T>(gu, z, B, D_ff, s));
+  if constexpr (sizeof(T) == 2) {
+    RUN(launch_gemv16_bf16(z, (const bf16 *)w->w_linear, (const bf16 *)w->w_linear, D, part, B,
+                           D, D_ff, K.ks_dn, s));
+  } else {
+    RUN(launch_gemv_f32(z, (const float *)w->w_linear, (const float *)w->w_linear, D, part, B, D,
+                        D_ff, s));
+  }
+  RUN(launch_splitk_reduce<T>(part, K.ks_dn, a, (long)B * D, s));
+  RUN(launch_rms_norm_add<T>(h, a, (const T *)w->post_ffw_norm, y, B, D, s));
   return GEMMA3_OK;
 }
 
@@ -579,6 +652,43 @@ int gemma3_stack_prefill(const gemma3_attn_desc *desc, int32_t D_ff,
     in = out;
   }
   return GEMMA3_OK;
+}
+
+size_t gemma3_block_decode_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff,
+                                           int32_t S) {
+  gemma3_ws_layout L;
+  BlockDecodeLayout K;
+  return block_decode_layout(desc, D_ff, S, &L, &K) == GEMMA3_OK ? K.total : 0;
+}
+
+int gemma3_block_decode(const gemma3_attn_desc *desc, int32_t D_ff, const void *x,
+                        const int32_t *segment_pos, const gemma3_block_weights *w,
+                        void *k_cache, void *v_cache, int32_t S, void *y, void *workspace,
+                        size_t workspace_bytes, void *hip_stream) {
+  gemma3_ws_layout L;
+  BlockDecodeLayout K;
+  int st = block_decode_layout(desc, D_ff, S, &L, &K);
+  if (st != GEMMA3_OK) return st;
+  if (!x || !segment_pos || !y || !w || !k_cache || !v_cache) return GEMMA3_ERR_NULL;
+  if ((st = check_weights(&w->attn)) != GEMMA3_OK) return st;
+  const void *bw[6] = {w->pre_attn_norm, w->post_attn_norm, w->pre_ffw_norm, w->post_ffw_norm,
+                       w->w_gating, w->w_linear};
+  for (const void *p : bw)
+    if (!p) return GEMMA3_ERR_NULL;
+  for (const void *p : bw)
+    if (!aligned16(p)) return GEMMA3_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache))
+    return GEMMA3_ERR_ALIGN;
+  if (x == y) return GEMMA3_ERR_SHAPE;
+  if ((long)desc->B * S * desc->H_kv * desc->d_h >= (1L << 62)) return GEMMA3_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < K.total) return GEMMA3_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (desc->dtype == GEMMA3_BF16)
+    return block_decode_impl<bf16>(desc, D_ff, (const bf16 *)x, segment_pos, w, k_cache, v_cache,
+                                   S, (bf16 *)y, (char *)workspace, L, K, s);
+  return block_decode_impl<float>(desc, D_ff, (const float *)x, segment_pos, w, k_cache, v_cache,
+                                  S, (float *)y, (char *)workspace, L, K, s);
 }
 
 size_t gemma3_kv_cache_bytes(int32_t num_layers, int32_t B, int32_t S, int32_t H_kv, int32_t d_h,

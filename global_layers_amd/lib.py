@@ -102,6 +102,13 @@ _lib.gemma3_stack_prefill.restype = ctypes.c_int
 _lib.gemma3_stack_prefill.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
                                       ctypes.POINTER(StackConfig), _P, _P, _P,
                                       ctypes.POINTER(BlockWeights), _P, _P, ctypes.c_size_t, _P]
+_lib.gemma3_block_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.gemma3_block_decode_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                                     ctypes.c_int32]
+_lib.gemma3_block_decode.restype = ctypes.c_int
+_lib.gemma3_block_decode.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32, _P, _P,
+                                     ctypes.POINTER(BlockWeights), _P, _P, ctypes.c_int32, _P,
+                                     _P, ctypes.c_size_t, _P]
 _lib.gemma3_kv_cache_bytes.restype = ctypes.c_size_t
 _lib.gemma3_kv_cache_bytes.argtypes = [ctypes.c_int32] * 8
 _PREFILL_ARGS = [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
@@ -128,7 +135,8 @@ EXPORTED = ("gemma3_attn_workspace_bytes", "gemma3_attn_prefill", "gemma3_attn_d
             "gemma3_attn_decode_stages", "gemma3_attn_prefill_cache",
             "gemma3_attn_prefill_chunk", "gemma3_attn_prefill_chunk_workspace_bytes",
             "gemma3_block_prefill", "gemma3_block_workspace_bytes", "gemma3_stack_prefill",
-            "gemma3_stack_workspace_bytes", "gemma3_kv_cache_bytes")
+            "gemma3_stack_workspace_bytes", "gemma3_kv_cache_bytes", "gemma3_block_decode",
+            "gemma3_block_decode_workspace_bytes")
 
 
 class Gemma3AttnError(ValueError):
@@ -378,6 +386,42 @@ def stack_prefill(x, segment_pos, layers: list, *, H, H_kv, d_h, window, query_s
     _check(_lib.gemma3_stack_prefill(ctypes.byref(desc), D_ff, ctypes.byref(cfg), _ptr(x),
                                      _ptr(segment_pos), _ptr(kv_valid_len), arr, _ptr(y),
                                      _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def block_decode(x, segment_pos, weights: dict, k_cache, v_cache, *, H, H_kv, d_h, attn_type,
+                 window, rope_theta, rope_scale, query_scale, workspace=None, y=None):
+    """y [B,1,D]: one decode step of a whole block (see gemma3_block_decode);
+    the caches hold this layer's pre-normed keys and values."""
+    dev = x.device
+    B, T, D = x.shape
+    S = k_cache.shape[1]
+    D_ff = weights["w_gating"].shape[1]
+    desc = make_desc(B=B, T=T, D=D, H=H, H_kv=H_kv, d_h=d_h, attn_type=attn_type,
+                     window=window, rope_theta=rope_theta, rope_scale=rope_scale,
+                     query_scale=query_scale, dtype=x.dtype)
+    _dev_tensor(x, x.dtype, "x", dev)
+    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
+    if segment_pos.numel() != B:
+        raise ValueError("segment_pos must hold one position per row")
+    for n, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(c, x.dtype, n, dev)
+        if c.shape != (B, S, H_kv, d_h):
+            raise ValueError(f"{n} must be [B, S, H_kv, d_h]")
+    for k in BLOCK_KEYS:
+        _dev_tensor(weights[k], x.dtype, k, dev)
+    if weights["w_gating"].shape != (2, D_ff, D) or weights["w_linear"].shape != (D, D_ff):
+        raise ValueError("w_gating must be [2, D_ff, D] and w_linear [D, D_ff]")
+    bw = BlockWeights(_weights(weights, x.dtype, dev),
+                      *(weights[k].data_ptr() for k in BLOCK_KEYS))
+    if workspace is None:
+        n = _lib.gemma3_block_decode_workspace_bytes(ctypes.byref(desc), D_ff, S)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    _check(_lib.gemma3_block_decode(ctypes.byref(desc), D_ff, _ptr(x), _ptr(segment_pos),
+                                    ctypes.byref(bw), _ptr(k_cache), _ptr(v_cache), S, _ptr(y),
+                                    _ptr(workspace), workspace.numel(), _stream()))
     return y
 
 

@@ -247,6 +247,20 @@ int gemma3_block_prefill(const gemma3_attn_desc *desc, int32_t D_ff, const void 
  * is enqueued; num_layers < 1 -> GEMMA3_ERR_SHAPE; NULL cfg or layers ->
  * GEMMA3_ERR_NULL.
  */
+/*
+ * One decode step of a whole block: x [B, 1, D], one token per row at
+ * position segment_pos[b]; the attention sublayer is gemma3_attn_decode on
+ * the pre-normed token (so k_cache / v_cache, [B, S, H_kv, d_h], hold the
+ * keys and values of this layer's pre-normed stream), the rest as in
+ * gemma3_block_prefill. Workspace: gemma3_block_decode_workspace_bytes(desc,
+ * D_ff, S). Errors: those of gemma3_attn_decode and gemma3_block_prefill.
+ */
+size_t gemma3_block_decode_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff, int32_t S);
+int gemma3_block_decode(const gemma3_attn_desc *desc, int32_t D_ff, const void *x,
+                        const int32_t *segment_pos, const gemma3_block_weights *w,
+                        void *k_cache, void *v_cache, int32_t S, void *y, void *workspace,
+                        size_t workspace_bytes, void *hip_stream);
+
 typedef struct {
   int32_t num_layers;
   int32_t window;          /* W of the local layers */

@@ -99,3 +99,48 @@ def test_block_1b_shape(gpu_lib, layer_id):
               rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
               query_scale=w.query_scale)
     _check(gpu_lib, inp, _block_weights(63 + layer_id, w.D, 6 * w.D, "bf16"), kw, "bf16")
+
+
+@pytest.mark.parametrize("dtype,d_h,D,D_ff", [("bf16", 128, 512, 1024), ("bf16", 256, 1024, 2048),
+                                              ("f32", 64, 256, 320)])
+@pytest.mark.parametrize("attn_type,window", [(L, 100), (G, 0)])
+def test_block_decode(gpu_lib, dtype, d_h, D, D_ff, attn_type, window):
+    # one token per row against caches of this layer's (pre-normed) keys and
+    # values: y and the written slot against the oracle's block_decode
+    B, H, Hk, S = 3, 4, 2, 300
+    lengths = (200, 37, 300)
+    log(f"block decode {dtype} d_h={d_h} {attn_type}")
+    r = np.random.default_rng([64, d_h, D])
+    x = I.to_dtype(r.standard_normal((B, 1, D)), dtype)
+    pos = torch.tensor([n - 1 for n in lengths], dtype=torch.int32)[:, None].contiguous()
+    inp = small_prefill_inputs(65, 1, 1, D, H, Hk, d_h, dtype)
+    attn = {k: inp[k] for k in ("w_q", "w_kv", "w_o", "gamma_q", "gamma_k")}
+    bw = _block_weights(66, D, D_ff, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.full((B, S, Hk, d_h), float("nan"), dtype=tdt)
+    vc = torch.full_like(kc, float("nan"))
+    for b, n in enumerate(lengths):
+        kc[b, :n - 1] = torch.from_numpy(r.standard_normal((n - 1, Hk, d_h))).to(tdt)
+        vc[b, :n - 1] = torch.from_numpy(r.standard_normal((n - 1, Hk, d_h))).to(tdt)
+    kw = dict(H=H, H_kv=Hk, d_h=d_h, attn_type=attn_type, window=window,
+              rope_theta=1e4 if attn_type == L else 1e6,
+              rope_scale=1.0 if attn_type == L else 8.0, query_scale=d_h ** -0.5)
+    w = {k: v.cuda() for k, v in dict(attn, **bw).items()}
+    kcd, vcd = kc.cuda(), vc.cuda()
+    y = gpu_lib.block_decode(x.cuda(), pos.cuda(), w, kcd, vcd, **kw)
+    torch.cuda.synchronize()
+    check = assert_block_close if dtype == "bf16" else assert_f32_close
+    for b, n in enumerate(lengths):
+        p = n - 1
+        yr, k_new, v_new = O.block_decode(
+            f64(x[b:b + 1]), np.array([[p]]), {k: f64(v) for k, v in attn.items()},
+            *(f64(bw[k]) for k in ("pre_attn_norm", "post_attn_norm", "pre_ffw_norm",
+                                   "post_ffw_norm")),
+            f64(bw["w_gating"]), f64(bw["w_linear"]), f64(kc[b:b + 1, :p + 1]),
+            f64(vc[b:b + 1, :p + 1]), num_heads=H, num_kv_heads=Hk, head_dim=d_h,
+            attn_type=attn_type, window=window, rope_theta=kw["rope_theta"],
+            rope_scale=kw["rope_scale"], query_scale=kw["query_scale"])
+        check(f64(y[b:b + 1]), yr, f"row {b} y")
+        (assert_block_close if dtype == "bf16" else assert_f32_close)(
+            f64(kcd[b, p]), k_new[0], f"row {b} k slot")
+        assert torch.isnan(kcd[b, p + 1:].float()).all(), "slots past the position were written"
