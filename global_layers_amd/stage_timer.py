@@ -1,6 +1,7 @@
 """Per-stage timing of the prefill path on the seeded synthetic workloads.
 
     python global_layers_amd/stage_timer.py --workload 4 [--reps 10] [--warmup 3] [--cache] [--block]
+    python global_layers_amd/stage_timer.py --workload 5 --block   (decode: whole-block steps)
 
 Every layer of the workload goes through the C ABI one stage at a time
 (gemma3_attn_prefill_stages): the projection with its QK-norm / RoPE
@@ -139,6 +140,45 @@ def time_block(w, layer_id: int, reps: int, warmup: int):
     return e0.elapsed_time(e1) * 1e3 / reps, 6 * B * T * D * D_ff, D_ff
 
 
+def time_block_decode(w, layer_id: int, reps: int, warmup: int):
+    """A whole-block decode step of the decode workload (D_ff = 4 D): event
+    time and the algorithmic bytes (allowed K/V slots, attention and MLP
+    weights, each read once)."""
+    layer = w.layers[layer_id]
+    inp = I.decode_inputs(w, layer_id)
+    kc, vc = I.decode_cache(w, layer_id, inp["lengths"], device="cuda", poison=False)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    D = w.D
+    D_ff = 4 * D
+    g = torch.Generator(device="cuda").manual_seed(2000 + layer_id)
+    dt = d["x"].dtype
+    for k in ("pre_attn_norm", "post_attn_norm", "pre_ffw_norm", "post_ffw_norm"):
+        d[k] = (torch.randn(D, generator=g, device="cuda") * 0.1).to(dt)
+    d["w_gating"] = (torch.randn((2, D_ff, D), generator=g, device="cuda") * D ** -0.5).to(dt)
+    d["w_linear"] = (torch.randn((D, D_ff), generator=g, device="cuda") * D_ff ** -0.5).to(dt)
+    kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
+              rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
+              query_scale=w.query_scale)
+    y = torch.empty_like(d["x"])
+    run = lambda: lib.block_decode(d["x"], d["segment_pos"], d, kc, vc, y=y, **kw)  # noqa: E731
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    esz = 2 if dt == torch.bfloat16 else 4
+    lens = np.asarray(inp["lengths"])
+    slots = np.minimum(lens, w.window) if layer.attn_type == W.LOCAL_SLIDING else lens
+    kv = int(slots.sum()) * w.H_kv * w.d_h * 2 * esz
+    weights = sum(d[k].numel() for k in ("w_q", "w_kv", "w_o", "w_gating", "w_linear")) * esz
+    return e0.elapsed_time(e1) * 1e3 / reps, kv + weights
+
+
 def main() -> None:
     p = argparse.ArgumentParser()
     p.add_argument("--workload", default="4", help="workload ids, comma separated (2, 3, 4)")
@@ -152,7 +192,15 @@ def main() -> None:
     for wid in (int(x) for x in args.workload.split(",")):
         w = W.WORKLOADS[wid]
         if w.T == 1:
-            sys.exit(f"workload {wid} is a decode workload")
+            if not args.block:
+                sys.exit(f"workload {wid} is a decode workload (time it with --block)")
+            for li, layer in enumerate(w.layers):
+                us, nbytes = time_block_decode(w, li, args.reps, args.warmup)
+                print(f"workload {wid} layer {li} {layer.attn_type:13s} block decode step "
+                      f"{us:9.1f} us {nbytes / us / 1e3:8.1f} GB/s "
+                      f"({nbytes / 1e6:.0f} MB, {nbytes / us / 1e3 / 8000:.1%} of 8 TB/s)",
+                      flush=True)
+            continue
         # one layer of each attention type (the others repeat its shapes)
         seen = {}
         for li, layer in enumerate(w.layers):
