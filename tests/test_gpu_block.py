@@ -17,8 +17,8 @@ import torch
 
 import workloads as W
 from workloads import inputs as I
-from parity_util import (REL_RMS_BF16, assert_f32_close, err_stats, f64, log,
-                         small_prefill_inputs, to_dev)
+from parity_util import (REL_RMS_BF16, assert_bf16_close, assert_f32_close, err_stats, f64,
+                         log, small_prefill_inputs, to_dev)
 import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -141,6 +141,10 @@ def test_block_decode(gpu_lib, dtype, d_h, D, D_ff, attn_type, window):
             attn_type=attn_type, window=window, rope_theta=kw["rope_theta"],
             rope_scale=kw["rope_scale"], query_scale=kw["query_scale"])
         check(f64(y[b:b + 1]), yr, f"row {b} y")
-        (assert_block_close if dtype == "bf16" else assert_f32_close)(
-            f64(kcd[b, p]), k_new[0], f"row {b} k slot")
-        assert torch.isnan(kcd[b, p + 1:].float()).all(), "slots past the position were written"
+        # the written slot holds the rotated key and the value of the
+        # pre-normed token: attention-path quantities, so the attention bar
+        slot = assert_bf16_close if dtype == "bf16" else assert_f32_close
+        slot(f64(kcd[b, p]), k_new[0], f"row {b} k slot")
+        slot(f64(vcd[b, p]), v_new[0], f"row {b} v slot")
+        assert torch.isnan(kcd[b, p + 1:].float()).all(), "k slots past the position were written"
+        assert torch.isnan(vcd[b, p + 1:].float()).all(), "v slots past the position were written"

@@ -671,6 +671,91 @@ def test_block_decode_continues_block_prefill(attn_type, W):
     np.testing.assert_allclose(y[:, 0], y_ref, rtol=1e-12, atol=1e-13)
 
 
+def _torch_rms(v, gamma):
+    t = torch.from_numpy(np.asarray(v, dtype=np.float64))
+    return F.rms_norm(t, (t.shape[-1],), weight=torch.from_numpy(1 + gamma), eps=1e-6)
+
+
+def _torch_ffn(u, wg, wl):
+    t = torch.from_numpy
+    return (F.gelu(u @ t(wg[0]).T, approximate="tanh") * (u @ t(wg[1]).T)) @ t(wl).T
+
+
+def _mlp_branch(h, n, wg, wl):
+    """post-FFW RMSNorm of the GeGLU FFN of the pre-FFW-normed stream, all in
+    torch float64 (F.rms_norm, F.gelu with the tanh approximation)."""
+    return _torch_rms(_torch_ffn(_torch_rms(h, n[2]), wg, wl).numpy(), n[3]).numpy()
+
+
+def test_block_with_silent_attention_is_residual_plus_mlp_branch():
+    # zero output projection: the attention sublayer adds nothing (h = x), so
+    # the block is x + RMSNorm_post_ffw(FFN(RMSNorm_pre_ffw(x))), with the
+    # four norms' gammas all different (a swapped norm vector fails)
+    x, pos, w, n, wg, wl, kw = _block_case(56, zero_o=True)
+    y = O.block_prefill(x, pos, w, *n, wg, wl, **kw)
+    np.testing.assert_allclose(y, x + _mlp_branch(x, n, wg, wl), rtol=1e-12, atol=1e-13)
+
+
+def test_block_mlp_branch_has_unit_rms_after_its_post_norm():
+    # with gamma_post_ffw = 0 the MLP branch is a unit-RMS vector over D,
+    # whatever the scale of the FFN weights or of the stream
+    x, pos, w, n, wg, wl, kw = _block_case(57, zero_o=True)
+    n = [n[0], n[1], n[2], np.zeros_like(n[3])]
+    for c, s in ((1.0, 1.0), (1.0, 1e3), (100.0, 1.0), (100.0, 1e3)):
+        y = O.block_prefill(c * x, pos, w, *n, wg, s * wl, **kw)
+        rms = np.sqrt(np.mean((y - c * x) ** 2, axis=-1))
+        np.testing.assert_allclose(rms, 1.0, rtol=1e-4)
+
+
+@pytest.mark.parametrize("attn_type,W", [(O.GLOBAL, 0), (O.LOCAL_SLIDING, 3)])
+def test_block_mlp_reads_the_stream_after_attention(attn_type, W):
+    # With the MLP's output weights zeroed the block returns h = x + a (its
+    # post-norm sees zeros); the MLP branch added with real weights must then
+    # be exactly the branch evaluated on that h, not on x.
+    x, pos, w, n, wg, wl, kw = _block_case(58)
+    kw = dict(kw, attn_type=attn_type, window=W)
+    h = O.block_prefill(x, pos, w, *n, wg, np.zeros_like(wl), **kw)
+    assert np.max(np.abs(h - x)) > 0.1          # the attention does move the stream
+    y = O.block_prefill(x, pos, w, *n, wg, wl, **kw)
+    np.testing.assert_allclose(y - h, _mlp_branch(h, n, wg, wl), rtol=1e-10, atol=1e-12)
+    # invariant form: change token 0 only. Rows t > 0 see it through the
+    # attention and no other way, so their MLP branch changes as well when
+    # (and only when) some row t > 0 may attend to key 0.
+    x2 = x.copy()
+    x2[:, 0] += 3.0
+    h2 = O.block_prefill(x2, pos, w, *n, wg, np.zeros_like(wl), **kw)
+    y2 = O.block_prefill(x2, pos, w, *n, wg, wl, **kw)
+    d_branch = np.abs((y2 - h2) - (y - h))[:, 1:]
+    reach = np.arange(1, x.shape[1]) < (W if attn_type == O.LOCAL_SLIDING else 10 ** 9)
+    assert np.all(d_branch[:, reach].max(axis=-1) > 1e-3)
+    assert np.all(d_branch[:, ~reach] == 0)
+
+
+@pytest.mark.parametrize("attn_type,W", [(O.GLOBAL, 0), (O.LOCAL_SLIDING, 4)])
+def test_block_decode_mlp_reads_the_stream_after_attention(attn_type, W):
+    # the decode step's MLP branch, likewise, is the branch of h (the step's
+    # output with the MLP's output weights zeroed) and the post-norm scales it
+    # to unit RMS when its gamma is 0
+    x, pos, w, n, wg, wl, kw = _block_case(59)
+    kw = dict(kw, attn_type=attn_type, window=W)
+    t, S = 7, 10
+    B, _, D = x.shape
+    Hk, d_h = kw["num_kv_heads"], kw["head_dim"]
+    r = np.random.default_rng(60)
+    kc = r.standard_normal((B, S, Hk, d_h))
+    vc = r.standard_normal((B, S, Hk, d_h))
+    xt, pt = x[:, t:t + 1], np.full((B, 1), t)
+    h, _, _ = O.block_decode(xt, pt, w, *n, wg, np.zeros_like(wl), kc, vc, **kw)
+    assert np.max(np.abs(h - xt)) > 0.1
+    y, _, _ = O.block_decode(xt, pt, w, *n, wg, wl, kc, vc, **kw)
+    np.testing.assert_allclose(y - h, _mlp_branch(h, n, wg, wl), rtol=1e-10, atol=1e-12)
+    n0 = [n[0], n[1], n[2], np.zeros_like(n[3])]
+    for s in (1.0, 1e3):
+        y, _, _ = O.block_decode(xt, pt, w, *n0, wg, s * wl, kc, vc, **kw)
+        h0, _, _ = O.block_decode(xt, pt, w, *n0, wg, np.zeros_like(wl), kc, vc, **kw)
+        np.testing.assert_allclose(np.sqrt(np.mean((y - h0) ** 2, axis=-1)), 1.0, rtol=1e-4)
+
+
 def test_kv_cache_footprint_closed_form():
     # 26 layers (the 1B depth: 4 full six-slot tiles + 2 local): 4 global and
     # 22 local layers; 128K slots, one KV head of 256, bf16, batch 1
