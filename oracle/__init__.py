@@ -32,5 +32,7 @@ from .gemma3_oracle import (  # noqa: F401
     block_prefill,
     block_decode,
     stack_prefill,
+    stack_prefill_cache,
+    stack_decode,
     kv_cache_bytes,
 )

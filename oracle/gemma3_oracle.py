@@ -375,6 +375,61 @@ def stack_prefill(x, segment_pos, layers: list, *, num_heads: int, num_kv_heads:
     return h
 
 
+def _layer_rope(l, n, local_rope, global_rope):
+    t = layer_attn_type(l, n)
+    theta, scale = local_rope if t == LOCAL_SLIDING else global_rope
+    return t, theta, scale
+
+
+def stack_prefill_cache(x, segment_pos, layers: list, k_caches: list, v_caches: list, *,
+                        num_heads: int, num_kv_heads: int, head_dim: int, window: int,
+                        local_rope=(1e4, 1.0), global_rope=(1e6, 8.0), query_scale: float,
+                        kv_valid_len=None):
+    """stack_prefill that also fills one left-aligned cache per layer ("Global
+    vs Local Layer Routing", How it works: each layer attends with its own
+    type; "Gemma 3 Attention Block", How it works, Cache). Layer l's cache
+    receives the rotated keys and the values of that layer's own attention
+    input, the pre-attention-normed stream, as prefill_cache writes them (with
+    layer l's theta and scale). Returns y and the list of fp64 (k, v) caches."""
+    n = len(layers)
+    h = np.asarray(x, dtype=np.float64)
+    caches = []
+    for l, w in enumerate(layers):
+        t, theta, scale = _layer_rope(l, n, local_rope, global_rope)
+        caches.append(prefill_cache(rms_norm(h, w["pre_attn_norm"]), segment_pos, w["w_kv"],
+                                    w["gamma_k"], k_caches[l], v_caches[l],
+                                    num_kv_heads=num_kv_heads, head_dim=head_dim,
+                                    rope_theta=theta, rope_scale=scale,
+                                    kv_valid_len=kv_valid_len))
+        h = block_prefill(h, segment_pos, w, w["pre_attn_norm"], w["post_attn_norm"],
+                          w["pre_ffw_norm"], w["post_ffw_norm"], w["w_gating"], w["w_linear"],
+                          num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                          attn_type=t, window=window, rope_theta=theta, rope_scale=scale,
+                          query_scale=query_scale, kv_valid_len=kv_valid_len)
+    return h, caches
+
+
+def stack_decode(x, segment_pos, layers: list, k_caches: list, v_caches: list, *,
+                 num_heads: int, num_kv_heads: int, head_dim: int, window: int,
+                 local_rope=(1e4, 1.0), global_rope=(1e6, 8.0), query_scale: float):
+    """One decode step of a routed stack: layer l is block_decode with the
+    routed type, that type's (theta, scale) and, when local, the window,
+    against layer l's own cache; each layer's output feeds the next. Returns
+    y [B,1,D] and, per layer, the (k, v) written at slot segment_pos[b]."""
+    n = len(layers)
+    h = np.asarray(x, dtype=np.float64)
+    written = []
+    for l, w in enumerate(layers):
+        t, theta, scale = _layer_rope(l, n, local_rope, global_rope)
+        h, k_new, v_new = block_decode(
+            h, segment_pos, w, w["pre_attn_norm"], w["post_attn_norm"], w["pre_ffw_norm"],
+            w["post_ffw_norm"], w["w_gating"], w["w_linear"], k_caches[l], v_caches[l],
+            num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim, attn_type=t,
+            window=window, rope_theta=theta, rope_scale=scale, query_scale=query_scale)
+        written.append((k_new, v_new))
+    return h, written
+
+
 def kv_cache_bytes(num_layers: int, batch: int, slots: int, num_kv_heads: int, head_dim: int,
                    window: int, elem_bytes: int, local_window_only: bool) -> int:
     """K and V cache bytes of a stack ("Gemma 3 Attention Block", Overview, and

@@ -756,6 +756,79 @@ def test_block_decode_mlp_reads_the_stream_after_attention(attn_type, W):
         np.testing.assert_allclose(np.sqrt(np.mean((y - h0) ** 2, axis=-1)), 1.0, rtol=1e-4)
 
 
+def _stack_case(seed, n_layers):
+    B, T, D, H, Hk, d_h, Dff = 2, 10, 16, 4, 2, 8, 24
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((B, T, D))
+    layers = []
+    for l in range(n_layers):
+        w = _layer(seed + 10 + l, D, H, Hk, d_h)
+        w.update(pre_attn_norm=r.standard_normal(D) * 0.1,
+                 post_attn_norm=r.standard_normal(D) * 0.1,
+                 pre_ffw_norm=r.standard_normal(D) * 0.1,
+                 post_ffw_norm=r.standard_normal(D) * 0.1,
+                 w_gating=r.standard_normal((2, Dff, D)) * D ** -0.5,
+                 w_linear=r.standard_normal((D, Dff)) * Dff ** -0.5)
+        layers.append(w)
+    kw = dict(num_heads=H, num_kv_heads=Hk, head_dim=d_h, window=3, query_scale=0.35)
+    pos = np.tile(np.arange(T), (B, 1))
+    return x, pos, layers, kw
+
+
+def test_stack_decode_continues_stack_prefill():
+    # seven layers (five local, one global, one local remainder), window 3:
+    # caches filled by a stack prefill of tokens 0..t-1, then a stack decode
+    # step of token t, give row t of a stack prefill over tokens 0..t, and
+    # every layer's written slot is the slot a longer cache-filling prefill
+    # writes
+    x, pos, layers, kw = _stack_case(70, 7)
+    t, S = 7, 9
+    B, _, D = x.shape
+    Hk, d_h = kw["num_kv_heads"], kw["head_dim"]
+    nan = [np.full((B, S, Hk, d_h), np.nan) for _ in layers]
+    _, caches = O.stack_prefill_cache(x[:, :t], pos[:, :t], layers, nan, nan, **kw)
+    y, written = O.stack_decode(x[:, t:t + 1], np.full((B, 1), t), layers,
+                                [c[0] for c in caches], [c[1] for c in caches], **kw)
+    y_ref = O.stack_prefill(x[:, :t + 1], pos[:, :t + 1], layers, **kw)
+    np.testing.assert_allclose(y[:, 0], y_ref[:, t], rtol=1e-11, atol=1e-12)
+    y_long, long_caches = O.stack_prefill_cache(x[:, :t + 1], pos[:, :t + 1], layers, nan, nan,
+                                                **kw)
+    np.testing.assert_array_equal(y_long, y_ref)
+    for l, ((k_new, v_new), (kc, vc)) in enumerate(zip(written, long_caches)):
+        np.testing.assert_allclose(k_new, kc[:, t], rtol=1e-11, atol=1e-12, err_msg=f"layer {l}")
+        np.testing.assert_allclose(v_new, vc[:, t], rtol=1e-11, atol=1e-12, err_msg=f"layer {l}")
+        assert np.all(np.isnan(kc[:, t + 1:])) and np.all(np.isnan(vc[:, t + 1:]))
+        assert not np.any(np.isnan(kc[:, :t + 1]))
+
+
+def test_stack_caches_hold_each_layers_own_keys():
+    # the caches of different layers differ (each holds its own layer's
+    # pre-normed stream with its own rotation); a one-layer stack's cache is
+    # the cache-filling prefill of that layer's pre-normed input
+    x, pos, layers, kw = _stack_case(71, 6)
+    B, T, D = x.shape
+    Hk, d_h = kw["num_kv_heads"], kw["head_dim"]
+    z = [np.zeros((B, T, Hk, d_h)) for _ in layers]
+    _, caches = O.stack_prefill_cache(x, pos, layers, z, z, **kw)
+    assert np.max(np.abs(caches[0][0] - caches[1][0])) > 0.1
+    w = layers[0]
+    kc, vc = O.prefill_cache(O.rms_norm(x, w["pre_attn_norm"]), pos, w["w_kv"], w["gamma_k"],
+                             z[0], z[0], num_kv_heads=Hk, head_dim=d_h, rope_theta=1e4,
+                             rope_scale=1.0)
+    _, c1 = O.stack_prefill_cache(x, pos, layers[:1], z, z, **kw)
+    np.testing.assert_array_equal(c1[0][0], kc)
+    np.testing.assert_array_equal(c1[0][1], vc)
+    # the global layer of the six (layer 5) caches the normed keys of its own
+    # input (the output of layers 0-4), rotated with the global pair (1e6, 8):
+    # unrotated at position 0, the complex-form rotation at position 3
+    k0 = O.rms_norm(np.einsum("btd,nd->btn", O.rms_norm(
+        O.stack_prefill(x, pos, layers[:5], **kw), layers[5]["pre_attn_norm"]),
+        layers[5]["w_kv"][:Hk * d_h]).reshape(B, T, Hk, d_h), layers[5]["gamma_k"])
+    np.testing.assert_allclose(caches[5][0][:, 0], k0[:, 0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(caches[5][0][:, 3], _rope_complex(k0[:, 3], 3, 1e6, 8.0),
+                               rtol=1e-12, atol=1e-13)
+
+
 def test_kv_cache_footprint_closed_form():
     # 26 layers (the 1B depth: 4 full six-slot tiles + 2 local): 4 global and
     # 22 local layers; 128K slots, one KV head of 256, bf16, batch 1
