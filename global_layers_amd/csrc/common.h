@@ -87,3 +87,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 and leaves the
 // expcnt and lgkmcnt counters unconstrained.
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+
+// One direct global -> LDS load (gfx950 global_load_lds_dwordx4): lane l
+// moves the 16 bytes at sbase + lane_off (sbase wave-uniform) to LDS byte
+// lds_wave_off + 16 l (lds_wave_off wave-uniform). The LDS destination goes
+// in M0, bound as an input operand so the compiler sets M0 itself and knows
+// it is taken. Inline assembly rather than the builtin: the compiler would
+// count an LDS-writing load as a memory access of unknown order and make
+// every later LDS fragment read wait for all LDS reads in flight; hidden from
+// it, those reads keep their partial waits (which stay correct whether or not
+// the load also counts in lgkmcnt: waiting for <= k outstanding still retires
+// the oldest reads). Callers therefore wait for completion explicitly (vmcnt)
+// before the barrier that hands the data to other waves, and only ever target
+// a buffer that no wave reads before that barrier.
+DEVI void load_lds16(const void *sbase, uint32_t lane_off, uint32_t lds_wave_off) {
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"(sbase), "{m0}"(lds_wave_off)
+               : "memory");
+}

@@ -69,23 +69,6 @@ template <int D> struct AttnCfg {
 template <int D> DEVI int swz_k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
 DEVI int swz_v(int r) { return (r >> 1) & 7; }
 
-// One direct global -> LDS load: lane l moves the 16 bytes at
-// sbase + lane_off (sbase wave-uniform) to LDS byte lds_wave_off + 16 l
-// (lds_wave_off wave-uniform). Written as inline assembly: the compiler counts an
-// LDS-writing load as a memory access of unknown order and would then make
-// every later LDS fragment read wait for all LDS reads in flight; hidden from
-// it, those reads keep their partial waits (which stay correct whether or
-// not the load also counts in lgkmcnt: waiting for <= k outstanding still
-// retires the oldest reads). Callers wait for completion explicitly
-// (publish_tiles) before the barrier that hands the data to other waves, and
-// only ever target a buffer that no wave reads before that barrier.
-DEVI void load_lds16(const void *sbase, uint32_t lane_off, uint32_t lds_wave_off) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(lane_off), "s"(sbase), "s"(lds_wave_off)
-               : "memory", "m0");
-}
-
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0) and lgkmcnt(0), expcnt free.
 constexpr int kWaitVmLgkm0 = 0x7 << 4;
 
@@ -335,12 +318,19 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   __syncthreads();
   gmax = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
   float m_ref[kRB];
-  f32x16 negm[kRB];
-  auto neg_ref = [&](int rb) {
-    const float v = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
+  float negu[kRB];  // -U_t (0 for a row without keys), the S accumulators' start
+  auto neg_ref = [&](int rb) { return m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb]; };
+  // The 16-register start vector of an S accumulator, formed next to the
+  // MFMA that takes it: the empty asm makes the value opaque, so the compiler
+  // writes the 16 copies where they are used instead of keeping them live
+  // through the loop (16 registers per row block freed, which keeps the loop
+  // of the two-block variant free of register spills).
+  auto splat_ref = [&](int rb) {
+    float u = negu[rb];
+    asm volatile("" : "+v"(u));
     f32x16 r;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) r[e] = v;
+    for (int e = 0; e < 16; ++e) r[e] = u;
     return r;
   };
   bool bound_ok = true;
@@ -358,7 +348,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // 1% margin covers the bf16 rounding of the stored keys
     m_ref[rb] = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f;
     bound_ok = bound_ok && 2.f * m_ref[rb] <= 100.f;
-    negm[rb] = neg_ref(rb);
+    negu[rb] = neg_ref(rb);
   }
 
   // Which logits of a 32-key half starting at key s0 are allowed (bit e of
@@ -483,7 +473,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int rb = 0; rb < kRB; ++rb)
             s_nxt[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                fr[j], qf[rb][g * kG + j], (g == 0 && j == 0) ? negm[rb] : s_nxt[rb], 0, 0, 0);
+                fr[j], qf[rb][g * kG + j], (g == 0 && j == 0) ? splat_ref(rb) : s_nxt[rb], 0, 0, 0);
       } else if constexpr (!kS) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -598,7 +588,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // write to slot 0
   f32x16 s0_first[kRB];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) s0_first[rb] = n_tiles > 0 ? qk_half(0, negm[rb], rb) : f32x16{};
+  for (int rb = 0; rb < kRB; ++rb) s0_first[rb] = n_tiles > 0 ? qk_half(0, splat_ref(rb), rb) : f32x16{};
   if (!__syncthreads_and(bound_ok) || force_exact_max) {
     // Exact row maxima (log2 units) over the allowed keys: each tile's two K
     // halves go to slots 0 and 1, S MFMAs only. Rare; kept simple.
@@ -625,13 +615,13 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       m_ref[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32, kWave));
-      negm[rb] = neg_ref(rb);
+      negu[rb] = neg_ref(rb);
     }
     issue_prologue();
     publish_tiles();
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
-      s0_first[rb] = n_tiles > 0 ? qk_half(0, negm[rb], rb) : f32x16{};
+      s0_first[rb] = n_tiles > 0 ? qk_half(0, splat_ref(rb), rb) : f32x16{};
     __syncthreads();
   }
   run(s0_first);

@@ -24,20 +24,6 @@ template <int N> struct VmWait {
   static constexpr int kImm = (N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 };
 
-// One direct global -> LDS load: lane l moves the 16 bytes at sbase + lane_off
-// (sbase wave-uniform) to LDS byte lds_wave_off + 16 l (wave-uniform offset).
-// Inline assembly: the compiler would count an LDS-writing load as a memory
-// access of unknown order and make every later fragment read wait for all
-// LDS reads in flight; hidden from it, the reads keep their partial waits. The
-// k loop waits for these loads explicitly (vmcnt) before the barrier that
-// publishes a stage.
-DEVI void load_lds16(const void *sbase, uint32_t lane_off, uint32_t lds_wave_off) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(lane_off), "s"(sbase), "s"(lds_wave_off)
-               : "memory", "m0");
-}
-
 // Tile of BM x BN outputs, K sliced by BK, NST LDS stages. Waves WM x WN.
 // Each stage holds A [BM][BK] and B [BN][BK] bf16, rows of BK*2 bytes, 16-byte
 // chunks XOR-swizzled by row so fragment reads by 16 consecutive rows hit all banks.
