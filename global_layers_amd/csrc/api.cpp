@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+
 #include "../../include/gemma3_attn.h"
 #include "../../include/gemma3_attn_stages.h"
 #include "kernels.h"
@@ -319,16 +320,24 @@ int decode_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
   return GEMMA3_OK;
 }
 
+// kc / vc (optional, [B, S, H_kv, d_h]): the attention sublayer also writes
+// its rotated keys and values (those of the pre-normed stream) into them, as
+// gemma3_attn_prefill_cache does.
 template <typename T>
 int block_impl(const gemma3_attn_desc *d, int D_ff, const T *x, const int32_t *pos,
                const int32_t *kv_len, const gemma3_block_weights *w, T *y, char *base,
-               const gemma3_ws_layout &L, const BlockLayout &K, hipStream_t s) {
+               const gemma3_ws_layout &L, const BlockLayout &K, hipStream_t s,
+               T *kc = nullptr, T *vc = nullptr, int32_t S = 0) {
   const int M = d->B * d->T, D = d->D;
   T *hn = (T *)(base + K.hn), *a = (T *)(base + K.a), *h = (T *)(base + K.h);
   T *gu = (T *)(base + K.gu), *z = (T *)(base + K.z);
   RUN(launch_rms_norm_add<T>(nullptr, x, (const T *)w->pre_attn_norm, hn, M, D, s));
   int st = prefill_impl<T>(d, hn, pos, kv_len, &w->attn, a, base, L, s, GEMMA3_STAGE_ALL);
   if (st != GEMMA3_OK) return st;
+  if (kc)
+    RUN(launch_prefill_cache_write<T>((const T *)(base + L.k), (const T *)(base + L.vt), pos,
+                                      kv_len, kc, vc, d->B, d->T, L.T_pad, d->H_kv, d->d_h, S,
+                                      s));
   RUN(launch_rms_norm_add<T>(x, a, (const T *)w->post_attn_norm, h, M, D, s));
   RUN(launch_rms_norm_add<T>(nullptr, h, (const T *)w->pre_ffw_norm, hn, M, D, s));
   if constexpr (sizeof(T) == 2) {
@@ -589,23 +598,102 @@ gemma3_attn_desc layer_desc(const gemma3_attn_desc *d, const gemma3_stack_config
 }
 
 // Every layer's block workspace (the largest), then two residual buffers the
-// layers alternate between.
+// layers alternate between. S > 0: the decode step's block workspaces, with
+// one-token residual buffers.
 int stack_layout(const gemma3_attn_desc *d, int32_t D_ff, const gemma3_stack_config *c,
-                 size_t *res0, size_t *total) {
+                 int32_t S, size_t *res0, size_t *total) {
   if (!d || !c) return GEMMA3_ERR_NULL;
   if (c->num_layers < 1) return GEMMA3_ERR_SHAPE;
   size_t mx = 0;
   for (int l = 0; l < c->num_layers; ++l) {
     const gemma3_attn_desc e = layer_desc(d, c, l);
     gemma3_ws_layout L;
-    BlockLayout K;
-    const int st = block_layout(&e, D_ff, &L, &K);
-    if (st != GEMMA3_OK) return st;
-    mx = K.total > mx ? K.total : mx;
+    size_t tot = 0;
+    if (S == 0) {
+      BlockLayout K;
+      const int st = block_layout(&e, D_ff, &L, &K);
+      if (st != GEMMA3_OK) return st;
+      tot = K.total;
+    } else {
+      BlockDecodeLayout K;
+      const int st = block_decode_layout(&e, D_ff, S, &L, &K);
+      if (st != GEMMA3_OK) return st;
+      tot = K.total;
+    }
+    mx = tot > mx ? tot : mx;
   }
   const size_t res = (size_t)d->B * d->T * d->D * elem_size(d->dtype);
   *res0 = mx;
   *total = align_up(mx + res) + align_up(res);
+  return GEMMA3_OK;
+}
+
+int check_block_weights(const gemma3_block_weights *w) {
+  if (!w) return GEMMA3_ERR_NULL;
+  int st = check_weights(&w->attn);
+  if (st != GEMMA3_OK) return st;
+  const void *bw[6] = {w->pre_attn_norm, w->post_attn_norm, w->pre_ffw_norm, w->post_ffw_norm,
+                       w->w_gating, w->w_linear};
+  for (const void *p : bw)
+    if (!p) return GEMMA3_ERR_NULL;
+  for (const void *p : bw)
+    if (!aligned16(p)) return GEMMA3_ERR_ALIGN;
+  return GEMMA3_OK;
+}
+
+// Per-layer caches of a stack: both host arrays present, every entry a
+// non-NULL, 16-byte aligned device pointer.
+int check_stack_caches(const gemma3_attn_desc *d, int n, void *const *kc, void *const *vc,
+                       int32_t S) {
+  if (!kc || !vc) return GEMMA3_ERR_NULL;
+  if (S < 1) return GEMMA3_ERR_SHAPE;
+  for (int l = 0; l < n; ++l) {
+    if (!kc[l] || !vc[l]) return GEMMA3_ERR_NULL;
+    if (!aligned16(kc[l]) || !aligned16(vc[l])) return GEMMA3_ERR_ALIGN;
+  }
+  if ((long)d->B * S * d->H_kv * d->d_h >= (1L << 62)) return GEMMA3_ERR_UNSUPPORTED;
+  return GEMMA3_OK;
+}
+
+// The routed stack of blocks over T tokens (caches optional: kc == NULL).
+int stack_prefill_run(const gemma3_attn_desc *desc, int32_t D_ff, const gemma3_stack_config *cfg,
+                      const void *x, const int32_t *segment_pos, const int32_t *kv_valid_len,
+                      const gemma3_block_weights *layers, void *const *kc, void *const *vc,
+                      int32_t S, void *y, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
+  size_t r0, total;
+  int st = stack_layout(desc, D_ff, cfg, 0, &r0, &total);
+  if (st != GEMMA3_OK) return st;
+  if (!x || !segment_pos || !y || !layers) return GEMMA3_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return GEMMA3_ERR_ALIGN;
+  if (x == y) return GEMMA3_ERR_SHAPE;
+  for (int l = 0; l < cfg->num_layers; ++l)
+    if ((st = check_block_weights(&layers[l])) != GEMMA3_OK) return st;
+  if (kc && (st = check_stack_caches(desc, cfg->num_layers, kc, vc, S)) != GEMMA3_OK) return st;
+  if (!workspace || workspace_bytes < total) return GEMMA3_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
+  char *base = (char *)workspace;
+  const size_t res = (size_t)desc->B * desc->T * desc->D * elem_size(desc->dtype);
+  void *buf[2] = {base + r0, base + align_up(r0 + res)};
+  hipStream_t s = (hipStream_t)hip_stream;
+  const void *in = x;
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    void *out = l == cfg->num_layers - 1 ? y : buf[l & 1];
+    const gemma3_attn_desc e = layer_desc(desc, cfg, l);
+    gemma3_ws_layout L;
+    BlockLayout K;
+    if ((st = block_layout(&e, D_ff, &L, &K)) != GEMMA3_OK) return st;
+    if (e.dtype == GEMMA3_BF16)
+      st = block_impl<bf16>(&e, D_ff, (const bf16 *)in, segment_pos, kv_valid_len, &layers[l],
+                            (bf16 *)out, base, L, K, s, kc ? (bf16 *)kc[l] : nullptr,
+                            kc ? (bf16 *)vc[l] : nullptr, S);
+    else
+      st = block_impl<float>(&e, D_ff, (const float *)in, segment_pos, kv_valid_len, &layers[l],
+                             (float *)out, base, L, K, s, kc ? (float *)kc[l] : nullptr,
+                             kc ? (float *)vc[l] : nullptr, S);
+    if (st != GEMMA3_OK) return st;
+    in = out;
+  }
   return GEMMA3_OK;
 }
 }  // namespace
@@ -613,7 +701,7 @@ int stack_layout(const gemma3_attn_desc *d, int32_t D_ff, const gemma3_stack_con
 size_t gemma3_stack_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff,
                                     const gemma3_stack_config *cfg) {
   size_t r0, tot;
-  return stack_layout(desc, D_ff, cfg, &r0, &tot) == GEMMA3_OK ? tot : 0;
+  return stack_layout(desc, D_ff, cfg, 0, &r0, &tot) == GEMMA3_OK ? tot : 0;
 }
 
 int gemma3_stack_prefill(const gemma3_attn_desc *desc, int32_t D_ff,
@@ -621,33 +709,63 @@ int gemma3_stack_prefill(const gemma3_attn_desc *desc, int32_t D_ff,
                          const int32_t *segment_pos, const int32_t *kv_valid_len,
                          const gemma3_block_weights *layers, void *y, void *workspace,
                          size_t workspace_bytes, void *hip_stream) {
+  return stack_prefill_run(desc, D_ff, cfg, x, segment_pos, kv_valid_len, layers, nullptr,
+                           nullptr, 0, y, workspace, workspace_bytes, hip_stream);
+}
+
+int gemma3_stack_prefill_cache(const gemma3_attn_desc *desc, int32_t D_ff,
+                               const gemma3_stack_config *cfg, const void *x,
+                               const int32_t *segment_pos, const int32_t *kv_valid_len,
+                               const gemma3_block_weights *layers, void *const *k_caches,
+                               void *const *v_caches, int32_t S, void *y, void *workspace,
+                               size_t workspace_bytes, void *hip_stream) {
+  if (!k_caches || !v_caches) return GEMMA3_ERR_NULL;
+  return stack_prefill_run(desc, D_ff, cfg, x, segment_pos, kv_valid_len, layers, k_caches,
+                           v_caches, S, y, workspace, workspace_bytes, hip_stream);
+}
+
+size_t gemma3_stack_decode_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff,
+                                           const gemma3_stack_config *cfg, int32_t S) {
+  if (S < 1) return 0;
+  size_t r0, tot;
+  return stack_layout(desc, D_ff, cfg, S, &r0, &tot) == GEMMA3_OK ? tot : 0;
+}
+
+int gemma3_stack_decode(const gemma3_attn_desc *desc, int32_t D_ff,
+                        const gemma3_stack_config *cfg, const void *x,
+                        const int32_t *segment_pos, const gemma3_block_weights *layers,
+                        void *const *k_caches, void *const *v_caches, int32_t S, void *y,
+                        void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (S < 1) return desc && cfg ? GEMMA3_ERR_SHAPE : GEMMA3_ERR_NULL;
   size_t r0, total;
-  int st = stack_layout(desc, D_ff, cfg, &r0, &total);
+  int st = stack_layout(desc, D_ff, cfg, S, &r0, &total);
   if (st != GEMMA3_OK) return st;
   if (!x || !segment_pos || !y || !layers) return GEMMA3_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return GEMMA3_ERR_ALIGN;
   if (x == y) return GEMMA3_ERR_SHAPE;
-  for (int l = 0; l < cfg->num_layers; ++l) {
-    const gemma3_block_weights *w = &layers[l];
-    if ((st = check_weights(&w->attn)) != GEMMA3_OK) return st;
-    const void *bw[6] = {w->pre_attn_norm, w->post_attn_norm, w->pre_ffw_norm,
-                         w->post_ffw_norm, w->w_gating, w->w_linear};
-    for (const void *p : bw)
-      if (!p) return GEMMA3_ERR_NULL;
-    for (const void *p : bw)
-      if (!aligned16(p)) return GEMMA3_ERR_ALIGN;
-  }
+  for (int l = 0; l < cfg->num_layers; ++l)
+    if ((st = check_block_weights(&layers[l])) != GEMMA3_OK) return st;
+  if ((st = check_stack_caches(desc, cfg->num_layers, k_caches, v_caches, S)) != GEMMA3_OK)
+    return st;
   if (!workspace || workspace_bytes < total) return GEMMA3_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
   char *base = (char *)workspace;
-  const size_t res = (size_t)desc->B * desc->T * desc->D * elem_size(desc->dtype);
+  const size_t res = (size_t)desc->B * desc->D * elem_size(desc->dtype);
   void *buf[2] = {base + r0, base + align_up(r0 + res)};
+  hipStream_t s = (hipStream_t)hip_stream;
   const void *in = x;
   for (int l = 0; l < cfg->num_layers; ++l) {
     void *out = l == cfg->num_layers - 1 ? y : buf[l & 1];
     const gemma3_attn_desc e = layer_desc(desc, cfg, l);
-    st = gemma3_block_prefill(&e, D_ff, in, segment_pos, kv_valid_len, &layers[l], out,
-                              workspace, r0, hip_stream);
+    gemma3_ws_layout L;
+    BlockDecodeLayout K;
+    if ((st = block_decode_layout(&e, D_ff, S, &L, &K)) != GEMMA3_OK) return st;
+    if (e.dtype == GEMMA3_BF16)
+      st = block_decode_impl<bf16>(&e, D_ff, (const bf16 *)in, segment_pos, &layers[l],
+                                   k_caches[l], v_caches[l], S, (bf16 *)out, base, L, K, s);
+    else
+      st = block_decode_impl<float>(&e, D_ff, (const float *)in, segment_pos, &layers[l],
+                                    k_caches[l], v_caches[l], S, (float *)out, base, L, K, s);
     if (st != GEMMA3_OK) return st;
     in = out;
   }
@@ -693,15 +811,33 @@ int gemma3_block_decode(const gemma3_attn_desc *desc, int32_t D_ff, const void *
 
 size_t gemma3_kv_cache_bytes(int32_t num_layers, int32_t B, int32_t S, int32_t H_kv, int32_t d_h,
                              int32_t window, int32_t dtype, int32_t local_window_only) {
-  if (num_layers < 1 || B < 1 || S < 1 || H_kv < 1 || d_h < 1 || window < 1) return 0;
-  if (dtype != GEMMA3_F32 && dtype != GEMMA3_BF16) return 0;
+  gemma3_kv_footprint f;
+  if (gemma3_kv_cache_footprint(num_layers, B, S, H_kv, d_h, window, dtype, &f) != GEMMA3_OK)
+    return 0;
+  return f.global_bytes + (local_window_only ? f.local_window_bytes : f.local_bytes);
+}
+
+int gemma3_kv_cache_footprint(int32_t num_layers, int32_t B, int32_t S, int32_t H_kv,
+                              int32_t d_h, int32_t window, int32_t dtype,
+                              gemma3_kv_footprint *out) {
+  if (!out) return GEMMA3_ERR_NULL;
+  memset(out, 0, sizeof(*out));
+  if (num_layers < 1 || B < 1 || S < 1 || H_kv < 1 || d_h < 1) return GEMMA3_ERR_SHAPE;
+  if (window < 1) return GEMMA3_ERR_WINDOW;
+  if (dtype != GEMMA3_F32 && dtype != GEMMA3_BF16) return GEMMA3_ERR_DTYPE;
   const size_t per_slot = 2 * (size_t)B * H_kv * d_h * elem_size(dtype);
-  size_t total = 0;
+  const size_t win = (size_t)(window < S ? window : S);
   for (int l = 0; l < num_layers; ++l) {
-    const bool local = gemma3_layer_attn_type(l, num_layers) == GEMMA3_ATTN_LOCAL_SLIDING;
-    total += per_slot * (size_t)(local && local_window_only && window < S ? window : S);
+    if (gemma3_layer_attn_type(l, num_layers) == GEMMA3_ATTN_LOCAL_SLIDING) {
+      ++out->n_local;
+      out->local_bytes += per_slot * (size_t)S;
+      out->local_window_bytes += per_slot * win;
+    } else {
+      ++out->n_global;
+      out->global_bytes += per_slot * (size_t)S;
+    }
   }
-  return total;
+  return GEMMA3_OK;
 }
 
 int gemma3_attn_decode_stages(const gemma3_attn_desc *desc, const void *x,

@@ -109,8 +109,32 @@ _lib.gemma3_block_decode.restype = ctypes.c_int
 _lib.gemma3_block_decode.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32, _P, _P,
                                      ctypes.POINTER(BlockWeights), _P, _P, ctypes.c_int32, _P,
                                      _P, ctypes.c_size_t, _P]
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_lib.gemma3_stack_prefill_cache.restype = ctypes.c_int
+_lib.gemma3_stack_prefill_cache.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                            ctypes.POINTER(StackConfig), _P, _P, _P,
+                                            ctypes.POINTER(BlockWeights), _PP, _PP,
+                                            ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+_lib.gemma3_stack_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.gemma3_stack_decode_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                                     ctypes.POINTER(StackConfig), ctypes.c_int32]
+_lib.gemma3_stack_decode.restype = ctypes.c_int
+_lib.gemma3_stack_decode.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                     ctypes.POINTER(StackConfig), _P, _P,
+                                     ctypes.POINTER(BlockWeights), _PP, _PP, ctypes.c_int32, _P,
+                                     _P, ctypes.c_size_t, _P]
 _lib.gemma3_kv_cache_bytes.restype = ctypes.c_size_t
 _lib.gemma3_kv_cache_bytes.argtypes = [ctypes.c_int32] * 8
+
+
+class KvFootprint(ctypes.Structure):
+    _fields_ = [("n_local", ctypes.c_int32), ("n_global", ctypes.c_int32),
+                ("local_bytes", ctypes.c_size_t), ("global_bytes", ctypes.c_size_t),
+                ("local_window_bytes", ctypes.c_size_t)]
+
+
+_lib.gemma3_kv_cache_footprint.restype = ctypes.c_int
+_lib.gemma3_kv_cache_footprint.argtypes = [ctypes.c_int32] * 7 + [ctypes.POINTER(KvFootprint)]
 _PREFILL_ARGS = [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                  ctypes.c_size_t, _P]
 _DECODE_ARGS = [ctypes.POINTER(Desc), _P, _P, ctypes.POINTER(Weights), _P, _P, ctypes.c_int32,
@@ -136,7 +160,9 @@ EXPORTED = ("gemma3_attn_workspace_bytes", "gemma3_attn_prefill", "gemma3_attn_d
             "gemma3_attn_prefill_chunk", "gemma3_attn_prefill_chunk_workspace_bytes",
             "gemma3_block_prefill", "gemma3_block_workspace_bytes", "gemma3_stack_prefill",
             "gemma3_stack_workspace_bytes", "gemma3_kv_cache_bytes", "gemma3_block_decode",
-            "gemma3_block_decode_workspace_bytes")
+            "gemma3_block_decode_workspace_bytes", "gemma3_stack_prefill_cache",
+            "gemma3_stack_decode", "gemma3_stack_decode_workspace_bytes",
+            "gemma3_kv_cache_footprint")
 
 
 class Gemma3AttnError(ValueError):
@@ -351,12 +377,7 @@ def block_prefill(x, segment_pos, weights: dict, *, H, H_kv, d_h, attn_type, win
     return y
 
 
-def stack_prefill(x, segment_pos, layers: list, *, H, H_kv, d_h, window, query_scale,
-                  local_rope=(1e4, 1.0), global_rope=(1e6, 8.0), kv_valid_len=None,
-                  workspace=None, y=None):
-    """y [B,T,D] of a routed stack of blocks, one weights dict per layer (as
-    block_prefill takes); layer l's type is layer_attn_type(l, len(layers))
-    (see gemma3_stack_prefill)."""
+def _stack_args(x, layers, H, H_kv, d_h, window, query_scale, local_rope, global_rope):
     dev = x.device
     B, T, D = x.shape
     n = len(layers)
@@ -366,11 +387,6 @@ def stack_prefill(x, segment_pos, layers: list, *, H, H_kv, d_h, window, query_s
                      query_scale=query_scale, dtype=x.dtype)
     cfg = StackConfig(n, window, local_rope[0], local_rope[1], global_rope[0], global_rope[1])
     _dev_tensor(x, x.dtype, "x", dev)
-    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
-    if segment_pos.shape != (B, T):
-        raise ValueError("segment_pos must be [B, T]")
-    if kv_valid_len is not None:
-        _dev_tensor(kv_valid_len, torch.int32, "kv_valid_len", dev)
     arr = (BlockWeights * n)()
     for l, w in enumerate(layers):
         for k in BLOCK_KEYS:
@@ -378,14 +394,83 @@ def stack_prefill(x, segment_pos, layers: list, *, H, H_kv, d_h, window, query_s
         if w["w_gating"].shape != (2, D_ff, D) or w["w_linear"].shape != (D, D_ff):
             raise ValueError("every layer needs w_gating [2, D_ff, D] and w_linear [D, D_ff]")
         arr[l] = BlockWeights(_weights(w, x.dtype, dev), *(w[k].data_ptr() for k in BLOCK_KEYS))
+    return desc, cfg, arr, D_ff
+
+
+def _cache_arrays(k_caches, v_caches, n, B, H_kv, d_h, dtype, dev):
+    """Host arrays of the per-layer cache device pointers (all [B, S, H_kv, d_h])."""
+    if len(k_caches) != n or len(v_caches) != n:
+        raise ValueError("one k and one v cache per layer")
+    S = k_caches[0].shape[1]
+    ka, va = (ctypes.c_void_p * n)(), (ctypes.c_void_p * n)()
+    for l in range(n):
+        for nm, c in (("k_cache", k_caches[l]), ("v_cache", v_caches[l])):
+            _dev_tensor(c, dtype, nm, dev)
+            if c.shape != (B, S, H_kv, d_h):
+                raise ValueError(f"{nm} of layer {l} must be [B, S, H_kv, d_h]")
+        ka[l], va[l] = k_caches[l].data_ptr(), v_caches[l].data_ptr()
+    return ka, va, S
+
+
+def stack_prefill(x, segment_pos, layers: list, *, H, H_kv, d_h, window, query_scale,
+                  local_rope=(1e4, 1.0), global_rope=(1e6, 8.0), kv_valid_len=None,
+                  workspace=None, y=None, k_caches=None, v_caches=None):
+    """y [B,T,D] of a routed stack of blocks, one weights dict per layer (as
+    block_prefill takes); layer l's type is layer_attn_type(l, len(layers))
+    (see gemma3_stack_prefill). With k_caches / v_caches (one [B,S,H_kv,d_h]
+    tensor per layer) every layer also fills its own cache
+    (gemma3_stack_prefill_cache)."""
+    dev = x.device
+    B, T, D = x.shape
+    desc, cfg, arr, D_ff = _stack_args(x, layers, H, H_kv, d_h, window, query_scale, local_rope,
+                                       global_rope)
+    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
+    if segment_pos.shape != (B, T):
+        raise ValueError("segment_pos must be [B, T]")
+    if kv_valid_len is not None:
+        _dev_tensor(kv_valid_len, torch.int32, "kv_valid_len", dev)
     if workspace is None:
         nb = _lib.gemma3_stack_workspace_bytes(ctypes.byref(desc), D_ff, ctypes.byref(cfg))
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     if y is None:
         y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
-    _check(_lib.gemma3_stack_prefill(ctypes.byref(desc), D_ff, ctypes.byref(cfg), _ptr(x),
-                                     _ptr(segment_pos), _ptr(kv_valid_len), arr, _ptr(y),
-                                     _ptr(workspace), workspace.numel(), _stream()))
+    if (k_caches is None) != (v_caches is None):
+        raise ValueError("k_caches and v_caches go together")
+    if k_caches is None:
+        _check(_lib.gemma3_stack_prefill(ctypes.byref(desc), D_ff, ctypes.byref(cfg), _ptr(x),
+                                         _ptr(segment_pos), _ptr(kv_valid_len), arr, _ptr(y),
+                                         _ptr(workspace), workspace.numel(), _stream()))
+        return y
+    ka, va, S = _cache_arrays(k_caches, v_caches, len(layers), B, H_kv, d_h, x.dtype, dev)
+    _check(_lib.gemma3_stack_prefill_cache(ctypes.byref(desc), D_ff, ctypes.byref(cfg), _ptr(x),
+                                           _ptr(segment_pos), _ptr(kv_valid_len), arr, ka, va,
+                                           S, _ptr(y), _ptr(workspace), workspace.numel(),
+                                           _stream()))
+    return y
+
+
+def stack_decode(x, segment_pos, layers: list, k_caches, v_caches, *, H, H_kv, d_h, window,
+                 query_scale, local_rope=(1e4, 1.0), global_rope=(1e6, 8.0), workspace=None,
+                 y=None):
+    """y [B,1,D]: one decode step of a routed stack, layer l against its own
+    caches k_caches[l] / v_caches[l] (see gemma3_stack_decode)."""
+    dev = x.device
+    B, T, D = x.shape
+    desc, cfg, arr, D_ff = _stack_args(x, layers, H, H_kv, d_h, window, query_scale, local_rope,
+                                       global_rope)
+    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
+    if segment_pos.numel() != B:
+        raise ValueError("segment_pos must hold one position per row")
+    ka, va, S = _cache_arrays(k_caches, v_caches, len(layers), B, H_kv, d_h, x.dtype, dev)
+    if workspace is None:
+        nb = _lib.gemma3_stack_decode_workspace_bytes(ctypes.byref(desc), D_ff,
+                                                      ctypes.byref(cfg), S)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    _check(_lib.gemma3_stack_decode(ctypes.byref(desc), D_ff, ctypes.byref(cfg), _ptr(x),
+                                    _ptr(segment_pos), arr, ka, va, S, _ptr(y), _ptr(workspace),
+                                    workspace.numel(), _stream()))
     return y
 
 
@@ -430,6 +515,15 @@ def kv_cache_bytes(num_layers, B, S, H_kv, d_h, window, dtype, local_window_only
     dt = _DTYPES.get(dtype, dtype)
     return _lib.gemma3_kv_cache_bytes(num_layers, B, S, H_kv, d_h, window, dt,
                                       1 if local_window_only else 0)
+
+
+def kv_cache_footprint(num_layers, B, S, H_kv, d_h, window, dtype) -> dict:
+    """Per-type K/V cache bytes of a routed stack (see gemma3_kv_cache_footprint)."""
+    dt = _DTYPES.get(dtype, dtype)
+    f = KvFootprint()
+    _check(_lib.gemma3_kv_cache_footprint(num_layers, B, S, H_kv, d_h, window, dt,
+                                          ctypes.byref(f)))
+    return {k: getattr(f, k) for k, _ in KvFootprint._fields_}
 
 
 def decode(x, segment_pos, weights: dict, k_cache, v_cache, *, H, H_kv, d_h, attn_type, window,

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define GEMMA3_ATTN_ABI_VERSION 2
+#define GEMMA3_ATTN_ABI_VERSION 3
 
 /* AttentionType ("Global vs Local Layer Routing", How it works). */
 typedef enum { GEMMA3_ATTN_GLOBAL = 0, GEMMA3_ATTN_LOCAL_SLIDING = 1 } gemma3_attn_type;
@@ -234,20 +234,6 @@ int gemma3_block_prefill(const gemma3_attn_desc *desc, int32_t D_ff, const void 
                          size_t workspace_bytes, void *hip_stream);
 
 /*
- * A routed stack of Gemma 3 blocks ("Global vs Local Layer Routing", How it
- * works; "Full Gemma 3 Block"): layer l is gemma3_block_prefill with type
- * gemma3_layer_attn_type(l, num_layers), that type's (theta, scale) and, on
- * local layers, `window`; each layer's output is the next layer's input, the
- * last layer's is y. The descriptor gives B, T, D, H, H_kv, d_h, query_scale
- * and dtype (its attn_type, window, rope_theta and rope_scale are replaced per
- * layer). `layers` is a host array of num_layers block weights (device
- * tensors as in gemma3_block_prefill). Workspace:
- * gemma3_stack_workspace_bytes(desc, D_ff, cfg). Errors: those of
- * gemma3_block_prefill for any layer, checked for every layer before anything
- * is enqueued; num_layers < 1 -> GEMMA3_ERR_SHAPE; NULL cfg or layers ->
- * GEMMA3_ERR_NULL.
- */
-/*
  * One decode step of a whole block: x [B, 1, D], one token per row at
  * position segment_pos[b]; the attention sublayer is gemma3_attn_decode on
  * the pre-normed token (so k_cache / v_cache, [B, S, H_kv, d_h], hold the
@@ -270,6 +256,20 @@ typedef struct {
   float global_scale;      /* 8 on 4B/12B/27B shapes, 1 otherwise */
 } gemma3_stack_config;
 
+/*
+ * A routed stack of Gemma 3 blocks ("Global vs Local Layer Routing", How it
+ * works; "Full Gemma 3 Block"): layer l is gemma3_block_prefill with type
+ * gemma3_layer_attn_type(l, num_layers), that type's (theta, scale) and, on
+ * local layers, `window`; each layer's output is the next layer's input, the
+ * last layer's is y. The descriptor gives B, T, D, H, H_kv, d_h, query_scale
+ * and dtype (its attn_type, window, rope_theta and rope_scale are replaced per
+ * layer). `layers` is a host array of num_layers block weights (device
+ * tensors as in gemma3_block_prefill). Workspace:
+ * gemma3_stack_workspace_bytes(desc, D_ff, cfg). Errors: those of
+ * gemma3_block_prefill for any layer, checked for every layer before anything
+ * is enqueued; num_layers < 1 -> GEMMA3_ERR_SHAPE; NULL cfg or layers ->
+ * GEMMA3_ERR_NULL.
+ */
 size_t gemma3_stack_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff,
                                     const gemma3_stack_config *cfg);
 int gemma3_stack_prefill(const gemma3_attn_desc *desc, int32_t D_ff,
@@ -279,12 +279,75 @@ int gemma3_stack_prefill(const gemma3_attn_desc *desc, int32_t D_ff,
                          size_t workspace_bytes, void *hip_stream);
 
 /*
- * Host-only KV-cache footprint of a stack (bytes of K and V): every layer
- * holds [B, S, H_kv, d_h] of `dtype` (the left-aligned caches
- * gemma3_attn_decode reads); with local_window_only != 0 a local layer counts
- * min(window, S) slots, what it needs when only its window is kept (local
- * layers never read older positions). 0 for invalid arguments.
+ * The same routed stack, also filling one left-aligned cache per layer
+ * ("Global vs Local Layer Routing", How it works: every layer attends with
+ * its own type; "Gemma 3 Attention Block", How it works, Cache): layer l's
+ * attention sublayer writes the rotated keys and the values of its own input
+ * (the pre-attention-normed stream of layer l, rotated with layer l's theta
+ * and scale) into k_caches[l] / v_caches[l] as gemma3_attn_prefill_cache
+ * does (valid tokens only, slot = segment_pos, positions outside [0, S)
+ * skipped). k_caches and v_caches are HOST arrays of num_layers DEVICE
+ * pointers, each cache [B, S, H_kv, d_h] of the descriptor's dtype, 16-byte
+ * aligned, caller-owned; they are what gemma3_stack_decode reads. Workspace
+ * and y as in gemma3_stack_prefill. Errors: those of gemma3_stack_prefill;
+ * NULL arrays or entries -> GEMMA3_ERR_NULL; S < 1 -> GEMMA3_ERR_SHAPE;
+ * a misaligned cache -> GEMMA3_ERR_ALIGN; all checked before any enqueue.
  */
+int gemma3_stack_prefill_cache(const gemma3_attn_desc *desc, int32_t D_ff,
+                               const gemma3_stack_config *cfg, const void *x,
+                               const int32_t *segment_pos, const int32_t *kv_valid_len,
+                               const gemma3_block_weights *layers, void *const *k_caches,
+                               void *const *v_caches, int32_t S, void *y, void *workspace,
+                               size_t workspace_bytes, void *hip_stream);
+
+/*
+ * One decode step of the routed stack: x [B, 1, D], one token per row at
+ * position segment_pos[b]; layer l is gemma3_block_decode with the routed
+ * type, that type's (theta, scale) and (local) window, against its own
+ * caches k_caches[l] / v_caches[l] (host arrays of device pointers as in
+ * gemma3_stack_prefill_cache; each [B, S, H_kv, d_h]); each layer's output
+ * is the next one's input, the last one's is y [B, 1, D]. Slot
+ * segment_pos[b] of every layer's caches is written. Workspace:
+ * gemma3_stack_decode_workspace_bytes(desc, D_ff, cfg, S) (desc.T = 1).
+ * Errors: those of gemma3_block_decode for any layer and of
+ * gemma3_stack_prefill_cache for the cache arrays, all checked before any
+ * enqueue.
+ */
+size_t gemma3_stack_decode_workspace_bytes(const gemma3_attn_desc *desc, int32_t D_ff,
+                                           const gemma3_stack_config *cfg, int32_t S);
+int gemma3_stack_decode(const gemma3_attn_desc *desc, int32_t D_ff,
+                        const gemma3_stack_config *cfg, const void *x,
+                        const int32_t *segment_pos, const gemma3_block_weights *layers,
+                        void *const *k_caches, void *const *v_caches, int32_t S, void *y,
+                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Host-only KV-cache footprint of a routed stack ("Gemma 3 Attention Block",
+ * Overview: the cache is what grows at long context; "Global vs Local Layer
+ * Routing", How it works: local layers only read their last W positions).
+ * Per layer K and V of [B, S, H_kv, d_h] elements of `dtype`, the caches the
+ * decode entry points of this library read, split by the routed type of each
+ * layer (gemma3_layer_attn_type). local_window_bytes is an analytic figure:
+ * what the local layers would hold if each kept only min(W, S) slots. No
+ * entry point of this library reads a cache of that size (every cache here
+ * is indexed by slot = position, so it needs S slots).
+ * Errors: NULL out -> GEMMA3_ERR_NULL; a size < 1 -> GEMMA3_ERR_SHAPE;
+ * window < 1 -> GEMMA3_ERR_WINDOW; unknown dtype -> GEMMA3_ERR_DTYPE.
+ */
+typedef struct {
+  int32_t n_local, n_global;   /* layers of each type */
+  size_t local_bytes;          /* K and V of the local layers, S slots each */
+  size_t global_bytes;         /* K and V of the global layers, S slots each */
+  size_t local_window_bytes;   /* the local layers at min(W, S) slots each (analytic) */
+} gemma3_kv_footprint;
+
+int gemma3_kv_cache_footprint(int32_t num_layers, int32_t B, int32_t S, int32_t H_kv,
+                              int32_t d_h, int32_t window, int32_t dtype,
+                              gemma3_kv_footprint *out);
+
+/* Total of gemma3_kv_cache_footprint: global_bytes + local_bytes, or with
+ * local_window_only != 0 global_bytes + local_window_bytes (the analytic
+ * window-only figure). 0 for invalid arguments. */
 size_t gemma3_kv_cache_bytes(int32_t num_layers, int32_t B, int32_t S, int32_t H_kv, int32_t d_h,
                              int32_t window, int32_t dtype, int32_t local_window_only);
 

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.abi_version() == 2
+    assert lib.abi_version() == 3
     for st in range(10):
         assert lib._lib.gemma3_attn_status_string(st)
     assert lib._lib.gemma3_attn_status_string(99) == b"unknown status"
@@ -195,6 +195,62 @@ def test_kv_cache_footprint_matches_oracle():
             for only in (False, True):
                 assert lib.kv_cache_bytes(*args, dt, only) == O.kv_cache_bytes(*args, esz, only)
     assert lib.kv_cache_bytes(0, 1, 10, 1, 64, 4, lib.BF16, True) == 0
+
+
+def test_kv_cache_footprint_splits_by_routed_type():
+    # local and global bytes each against the oracle's routing and its
+    # whole-stack formula (a stack of only its local, or only its global, layers)
+    import oracle as O
+    for args in ((26, 1, 131072, 1, 256, 512), (62, 2, 32768, 16, 128, 1024), (7, 1, 100, 1, 64, 4)):
+        n, B, S, Hk, d_h, Wn = args
+        f = lib.kv_cache_footprint(*args, lib.BF16)
+        types = O.layer_attn_types(n)
+        assert (f["n_local"], f["n_global"]) == (types.count(O.LOCAL_SLIDING), types.count(O.GLOBAL))
+        per_layer = O.kv_cache_bytes(1, B, S, Hk, d_h, Wn, 2, False)
+        per_local_window = O.kv_cache_bytes(1, B, S, Hk, d_h, Wn, 2, True)
+        assert f["global_bytes"] == f["n_global"] * per_layer
+        assert f["local_bytes"] == f["n_local"] * per_layer
+        assert f["local_window_bytes"] == f["n_local"] * per_local_window
+        assert f["local_bytes"] + f["global_bytes"] == O.kv_cache_bytes(*args, 2, False)
+        assert f["local_window_bytes"] + f["global_bytes"] == O.kv_cache_bytes(*args, 2, True)
+    bad = lib.KvFootprint()
+    assert lib._lib.gemma3_kv_cache_footprint(0, 1, 10, 1, 64, 4, lib.BF16, ctypes.byref(bad)) == 2
+    assert lib._lib.gemma3_kv_cache_footprint(6, 1, 10, 1, 64, 0, lib.BF16, ctypes.byref(bad)) == 3
+    assert lib._lib.gemma3_kv_cache_footprint(6, 1, 10, 1, 64, 4, 7, ctypes.byref(bad)) == 4
+    assert lib._lib.gemma3_kv_cache_footprint(6, 1, 10, 1, 64, 4, lib.BF16, None) == 1
+
+
+def test_stack_cache_and_decode_validation_status():
+    d = _desc()
+    cfg = lib.StackConfig(7, 64, 1e4, 1.0, 1e6, 8.0)
+    aw = lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    good = lib.BlockWeights(aw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    arr = (lib.BlockWeights * 7)(*([good] * 7))
+    n = lib._lib.gemma3_stack_workspace_bytes(ctypes.byref(d), 512, ctypes.byref(cfg))
+    caches = (ctypes.c_void_p * 7)(*([FAKE] * 7))
+    holed = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [None]))
+    skew = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [FAKE + 8]))
+    pf = lambda kc, vc, S=64, ws=n: lib._lib.gemma3_stack_prefill_cache(  # noqa: E731
+        ctypes.byref(d), 512, ctypes.byref(cfg), FAKE, FAKE, None, arr, kc, vc, S, FAKE + 4096,
+        FAKE, ws, None)
+    assert pf(None, caches) == 1
+    assert pf(caches, holed) == 1
+    assert pf(caches, skew) == 9
+    assert pf(caches, caches, S=0) == 2
+    assert pf(caches, caches, ws=16) == 6
+    dd = _desc(T=1)
+    nd = lib._lib.gemma3_stack_decode_workspace_bytes(ctypes.byref(dd), 512, ctypes.byref(cfg), 64)
+    assert nd > 0
+    assert lib._lib.gemma3_stack_decode_workspace_bytes(ctypes.byref(dd), 512, ctypes.byref(cfg),
+                                                        0) == 0
+    dc = lambda kc, vc, S=64, ws=nd, desc=dd: lib._lib.gemma3_stack_decode(  # noqa: E731
+        ctypes.byref(desc), 512, ctypes.byref(cfg), FAKE, FAKE, arr, kc, vc, S, FAKE + 4096,
+        FAKE, ws, None)
+    assert dc(caches, holed) == 1
+    assert dc(caches, skew) == 9
+    assert dc(caches, caches, S=0) == 2
+    assert dc(caches, caches, ws=16) == 6
+    assert dc(caches, caches, desc=d) == 2                  # T != 1
 
 
 def test_stack_validation_status():
