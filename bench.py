@@ -1,20 +1,23 @@
 """Benchmark of the Gemma 3 attention-block forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-extra]
 
-A step is one prefill pass of the Gemma-3-1B-shaped pair of layers (one local,
-one global; B=1, T=4096, D=1152, H=4, H_kv=1, d_h=256, W=512, bf16) through
-the C ABI, inputs resident in HBM. `value` is the whole-call algorithmic
-TFLOP/s of that step: 2*M*N*K for the three projections plus 4*d_h*H per
-allowed (query, key) pair, never the masked or skipped pairs.
+A step is one prefill pass of the 27B-shaped pair of layers (one local, one
+global; B=1, T=32768, D=5376, H=32, H_kv=16, d_h=128, W=1024, alpha =
+168^-1/2, bf16), the largest prefill workload on one GPU, through the C ABI
+with inputs resident in HBM. `value` is the whole-call algorithmic TFLOP/s of
+that step: 2*M*N*K for the three projections plus 4*d_h*H per allowed
+(query, key) pair, never the masked or skipped pairs.
 
-The same run also times the decode step of the 12B-like shape (B=16,
-D=3840, H=16, H_kv=8, d_h=256, bf16 cache of 131072 slots, seeded lengths),
-as a global and as a local (W=1024) layer, reporting algorithmic GB/s
-(allowed KV slots, weights, x, y, cache write) with the 256 MB Infinity Cache
-flushed between repetitions; per-stage kernel times from HIP events on the
-launch stream; the roofline entry of the dominant kernel; and the fp64 oracle
-timed on the host cores as a reported CPU baseline.
+The same run also reports (extra keys, not the headline): the 1B-shaped
+pair (B=1, T=4096) and the 4B-like six-layer tile (B=4, T=8192, padded rows)
+the same way; the decode step of the 12B-like shape (B=16, D=3840, H=16,
+H_kv=8, d_h=256, bf16 cache of 131072 slots, seeded lengths) as a global and
+as a local (W=1024) layer in algorithmic GB/s (allowed KV slots, weights, x,
+y, cache write) with the 256 MB Infinity Cache flushed between repetitions;
+per-kernel times from HIP events on the launch stream; the roofline entry of
+the dominant kernel; and the fp64 oracle timed on the host cores on a
+bounded sample of the headline workload, as a reported CPU baseline.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -32,6 +35,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEADLINE = 4                # 27B-shaped local + global pair
+EXTRA = (2, 3)              # 1B-shaped pair, 4B-like six-layer tile
+CPU_SAMPLE_T = 2048         # oracle sample: the first tokens of the headline workload
 
 
 def log(*a):
@@ -41,18 +47,19 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--decode-reps", type=int, default=20)
-    p.add_argument("--stage-reps", type=int, default=20)
+    p.add_argument("--stage-reps", type=int, default=10)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run a plain 512 MiB device copy first (scales the HBM byte counters)")
     return p.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def source_hash(path):
@@ -60,16 +67,19 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel_src):
-    """HBM bytes per launch of the attention stage from the committed counter
-    summary, only while the kernel source still matches the one profiled."""
+def measured_traffic(key):
+    """HBM bytes per launch of one kernel from the committed counter summary,
+    only while every kernel source still matches the one profiled."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash(kernel_src):
-        return None
-    return rec.get("bytes_per_launch")
+    for src, h in rec.get("source_sha256_16", {}).items():
+        path = os.path.join(ROOT, src)
+        if not os.path.exists(path) or source_hash(path) != h:
+            return None
+    ent = rec.get("kernels", {}).get(key)
+    return None if ent is None else ent.get("bytes_per_launch")
 
 
 # ------------------------------------------------------------------ work counts
@@ -81,14 +91,14 @@ def allowed_pairs(T, attn_type, window, kv_len):
     return int(np.maximum(0, hi - lo + 1).sum())
 
 
-def prefill_flops(w, layer):
+def stage_flops(w, layer):
+    """Algorithmic FLOPs of one layer's three stages."""
     M = w.B * w.T
-    n_qkv = (w.H + 2 * w.H_kv) * w.d_h
-    proj = 2 * M * w.D * n_qkv + 2 * M * (w.H * w.d_h) * w.D
     lens = w.kv_valid_len() or (w.T,) * w.B
     pairs = sum(allowed_pairs(w.T, layer.attn_type, w.window, L) for L in lens)
-    attn = 4 * w.d_h * w.H * pairs
-    return proj, attn
+    return {"qkv": 2 * M * w.D * (w.H + 2 * w.H_kv) * w.d_h,
+            "attention": 4 * w.d_h * w.H * pairs,
+            "out": 2 * M * (w.H * w.d_h) * w.D}
 
 
 def decode_bytes(w, layer, lengths):
@@ -104,6 +114,106 @@ def decode_bytes(w, layer, lengths):
 # ------------------------------------------------------------------ helpers
 def stream_events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+STAGES = (("qkv", "STAGE_QKV_PROJ|STAGE_QK_NORM"), ("attention", "STAGE_ATTN"),
+          ("out", "STAGE_OUT_PROJ"))
+KERNEL_OF_STAGE = {"qkv": "gemm_bf16_nt (QKV projection, QK-norm/RoPE/alpha epilogue)",
+                   "attention": "flash_attn_fwd_bf16 (+ flash_combine when split)",
+                   "out": "gemm_bf16_nt (output projection)"}
+
+
+def bench_prefill(args, torch, W, I, lib, dev, wid, cpu_copy=False):
+    """Whole steps (every layer of the workload, in order) and, per layer,
+    each stage repeated alone. Returns the summary and, with cpu_copy, the
+    CPU tensors of the inputs (for the oracle sample)."""
+    w = W.WORKLOADS[wid]
+    x_cpu = I.prefill_x(w)
+    x = x_cpu.to(dev)
+    pos = I.prefill_positions(w).to(dev)
+    kvl = I.prefill_kv_valid_len(w)
+    kvl = None if kvl is None else kvl.to(dev)
+    layers, cpu_w, ws_bytes = [], [], 0
+    for li, layer in enumerate(w.layers):
+        wc = I.layer_weights(w, li)
+        if cpu_copy:
+            cpu_w.append(wc)
+        kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
+                  rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
+                  query_scale=w.query_scale)
+        desc = lib.make_desc(B=w.B, T=w.T, D=w.D, dtype=torch.bfloat16, **kw)
+        ws_bytes = max(ws_bytes, lib.workspace_bytes(desc, 0))
+        layers.append(dict(layer=layer, wts={k: v.to(dev) for k, v in wc.items()}, kw=kw,
+                           flops=stage_flops(w, layer)))
+    # the layers run one after another on one stream and share a workspace
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    y = torch.empty((w.B, w.T, w.D), dtype=torch.bfloat16, device=dev)
+    step_flops = sum(sum(L["flops"].values()) for L in layers)
+
+    def step():
+        for L in layers:
+            lib.prefill(x, pos, L["wts"], kv_valid_len=kvl, workspace=ws, y=y, **L["kw"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = stream_events(torch)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[{w.name}] step {ms_per_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall) "
+        f"-> {value:.1f} TFLOP/s ({value / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
+
+    # per-stage kernel times: events on the launch stream around `stage_reps`
+    # back-to-back calls of that stage alone (the workspace holds the earlier
+    # stages' results from the full call before). On the bf16 shapes here the
+    # projection and QK-norm/RoPE are one kernel (epilogue fusion).
+    kernels, seen = [], set()
+    for li, L in enumerate(layers):
+        key = (L["layer"].attn_type, L["layer"].rope_theta, L["layer"].rope_scale)
+        if key in seen:   # repeated layers of a tile have the same shapes and plan
+            continue
+        seen.add(key)
+        lib.prefill(x, pos, L["wts"], kv_valid_len=kvl, workspace=ws, y=y, **L["kw"])
+        row = {}
+        for name, bits in STAGES:
+            st = 0
+            for b in bits.split("|"):
+                st |= getattr(lib, b)
+            a, b_ = stream_events(torch)
+            a.record()
+            for _ in range(args.stage_reps):
+                lib.prefill(x, pos, L["wts"], kv_valid_len=kvl, workspace=ws, y=y, stages=st,
+                            **L["kw"])
+            b_.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b_) * 1e3 / args.stage_reps
+            tf = L["flops"][name] / (us * 1e-6) / 1e12
+            row[name] = us
+            kernels.append({"layer": li, "type": L["layer"].attn_type, "stage": name,
+                            "kernel": KERNEL_OF_STAGE[name], "us": round(us, 2),
+                            "flops": L["flops"][name], "tflops": round(tf, 2),
+                            "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        log(f"  layer {li} {L['layer'].attn_type:13s} " +
+            " ".join(f"{k}={v:.1f}us" for k, v in row.items()))
+    out = {"workload": w.name, "value": round(value, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(ms_per_step, 5), "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+           "step_flops": step_flops, "kernels": kernels,
+           "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "H": w.H,
+                      "H_kv": w.H_kv, "d_h": w.d_h, "window": w.window,
+                      "kv_valid_len": w.kv_valid_len(),
+                      "layers": [f"{L['layer'].attn_type}(theta={L['layer'].rope_theta:g},"
+                                 f"scale={L['layer'].rope_scale:g})" for L in layers],
+                      "step_flops": step_flops, "parallelism": "none (1 GPU)"}}
+    del ws, y, x, layers
+    torch.cuda.empty_cache()
+    return out, (x_cpu, cpu_w)
 
 
 def main():
@@ -133,122 +243,60 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---------------------------------------------------------------- prefill
-    w = W.WORKLOADS[2]
-    layers = []
-    x = I.prefill_x(w).to(dev)
-    pos = I.prefill_positions(w).to(dev)
-    for li, layer in enumerate(w.layers):
-        wts = {k: v.to(dev) for k, v in I.layer_weights(w, li).items()}
-        kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
-                  rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
-                  query_scale=w.query_scale)
-        desc = lib.make_desc(B=w.B, T=w.T, D=w.D, dtype=torch.bfloat16, **kw)
-        ws = lib.new_workspace(desc, 0, dev)
-        y = torch.empty((w.B, w.T, w.D), dtype=torch.bfloat16, device=dev)
-        proj, attn = prefill_flops(w, layer)
-        layers.append(dict(layer=layer, wts=wts, kw=kw, ws=ws, y=y, proj=proj, attn=attn))
-    step_flops = sum(L["proj"] + L["attn"] for L in layers)
-
-    def step():
-        for L in layers:
-            lib.prefill(x, pos, L["wts"], workspace=L["ws"], y=L["y"], **L["kw"])
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = stream_events(torch)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
-    log(f"prefill step {ms_per_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall) "
-        f"-> {value:.1f} TFLOP/s ({value / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
-
-    # per-stage kernel times (events on the launch stream, each stage repeated
-    # alone). The projection and QK-norm/RoPE run as one stage: on this shape
-    # they are one kernel (norm, RoPE and V transpose in the GEMM epilogue).
-    stage_names = {lib.STAGE_QKV_PROJ | lib.STAGE_QK_NORM: "qkv_proj+qk_norm_rope",
-                   lib.STAGE_ATTN: "attention", lib.STAGE_OUT_PROJ: "out_proj"}
-    stage_ms = {n: 0.0 for n in stage_names.values()}
-    per_layer = []
-    for L in layers:
-        row = {}
-        for bit, name in stage_names.items():
-            a, b = stream_events(torch)
-            a.record()
-            for _ in range(args.stage_reps):
-                lib.prefill(x, pos, L["wts"], workspace=L["ws"], y=L["y"], stages=bit,
-                            **L["kw"])
-            b.record()
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / args.stage_reps
-            row[name] = ms
-            stage_ms[name] += ms
-        per_layer.append(row)
-        log(f"  {L['layer'].attn_type:13s} " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in row.items()))
-    step()  # leave the workspaces consistent
-    torch.cuda.synchronize()
-
-    proj_flops = {"qkv_proj+qk_norm_rope": sum(2 * w.B * w.T * w.D * (w.H + 2 * w.H_kv) * w.d_h
-                                               for _ in layers),
-                  "out_proj": sum(2 * w.B * w.T * w.H * w.d_h * w.D for _ in layers),
-                  "attention": sum(L["attn"] for L in layers)}
-    dominant = max(stage_ms, key=stage_ms.get)
-    ach = proj_flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
-    traffic = (measured_traffic(os.path.join(ROOT, "global_layers_amd", "csrc", "flash_attn.hip"))
-               if dominant == "attention" else None)
-    roofline = {"kernel": dominant + (" (flash_attn_fwd_bf16 + split merge)"
-                                      if dominant == "attention" else ""),
-                "bound": "mfma", "achieved": round(ach, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "launches_per_step": len(layers),
-                "flops_per_launch": proj_flops[dominant] // len(layers),
-                "us_per_launch": round(stage_ms[dominant] * 1e3 / len(layers), 2)}
-    attn_tflops = proj_flops["attention"] / (stage_ms["attention"] * 1e-3) / 1e12
-    log(f"  dominant kernel {dominant}: {roofline['achieved']} {roofline['unit']}; "
-        f"attention core {attn_tflops:.1f} TFLOP/s")
+    # ---------------------------------------------------------------- headline
+    head, (x_cpu, cpu_w) = bench_prefill(args, torch, W, I, lib, dev, HEADLINE,
+                                         cpu_copy=not args.no_cpu)
+    w = W.WORKLOADS[HEADLINE]
+    # dominant kernel: the single stage launch with the longest time per step
+    dom = max(head["kernels"], key=lambda k: k["us"])
+    tkey = f"{w.name}/layer{dom['layer']}/{dom['stage']}"
+    roofline = {"kernel": f"{dom['kernel']}, layer {dom['layer']} ({dom['type']})",
+                "bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": dom["frac"], "traffic": measured_traffic(tkey),
+                "flops_per_launch": dom["flops"], "us_per_launch": dom["us"],
+                "launches_per_step": 1}
+    attn = [k for k in head["kernels"] if k["stage"] == "attention"]
+    attn_tflops = sum(k["flops"] for k in attn) / (sum(k["us"] for k in attn) * 1e-6) / 1e12
+    log(f"  dominant kernel {roofline['kernel']}: {dom['tflops']} TFLOP/s "
+        f"({dom['frac']:.1%}); attention stages {attn_tflops:.1f} TFLOP/s")
 
     result = {
         "metric": "prefill attn TFLOP/s (% MFMA bf16 peak); decode KV GB/s (% HBM peak)",
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "H": w.H, "H_kv": w.H_kv,
-                   "d_h": w.d_h, "window": w.window,
-                   "layers": [f"{L['layer'].attn_type}(theta={L['layer'].rope_theta:g},"
-                              f"scale={L['layer'].rope_scale:g})" for L in layers],
-                   "step_flops": step_flops, "parallelism": "none (1 GPU)"},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
-        "attention_core_tflops": round(attn_tflops, 2),
+        "config": head["config"],
+        "frac_of_peak": head["frac_of_peak"],
+        "attention_stage_tflops": round(attn_tflops, 2),
+        "kernels": head["kernels"],
         "roofline": roofline,
     }
+
+    # ---------------------------------------------------------------- other prefill workloads
+    if not args.no_extra:
+        extra = {}
+        for wid in EXTRA:
+            r, _ = bench_prefill(args, torch, W, I, lib, dev, wid)
+            extra[r["workload"]] = {k: r[k] for k in ("value", "unit", "ms_per_step",
+                                                      "frac_of_peak", "step_flops", "kernels")}
+        result["prefill_other"] = extra
 
     # ---------------------------------------------------------------- decode
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, np, W, I, lib, dev)
-        for L in layers:
-            L["ws"] = None
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU baseline
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, step_flops)
+        result["cpu_baseline"] = cpu_baseline(w, x_cpu, cpu_w)
 
     print(json.dumps(result), flush=True)
 
@@ -315,7 +363,7 @@ def bench_decode(args, torch, np, W, I, lib, dev):
             "roofline": {"kernel": "decode attention (split-KV partial + combine)",
                          "bound": "hbm", "achieved": round(core_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(core_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic(f"{w.name}/{name}/attention")},
         }
         log(f"decode {name}: {med * 1e3:.1f} us -> {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%}); "
             f"attention core {core_gbs:.0f} GB/s; stages {out[name]['stage_us']}")
@@ -324,30 +372,34 @@ def bench_decode(args, torch, np, W, I, lib, dev):
     return out
 
 
-def cpu_baseline(w, step_flops):
-    """The fp64 oracle on this host's cores, on the same step (both layers)."""
+def cpu_baseline(w, x_cpu, cpu_w):
+    """The fp64 oracle on this host's cores, on a bounded sample of the
+    headline workload: its first CPU_SAMPLE_T tokens (the same x rows and
+    weights), both layers, so the run stays within about ten seconds."""
     import numpy as np
 
     import oracle as O
-    from workloads import inputs as I
+    import workloads as W
 
     try:
         from threadpoolctl import threadpool_info
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # noqa: BLE001
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    x = I.prefill_x(w).float().numpy().astype(np.float64)
-    pos = I.prefill_positions(w).numpy()
-    total = 0.0
+    ws = W.scaled(w, T=CPU_SAMPLE_T)
+    x = x_cpu[:, :CPU_SAMPLE_T].float().numpy().astype(np.float64)
+    pos = np.tile(np.arange(CPU_SAMPLE_T), (w.B, 1))
+    total, flops = 0.0, 0
     for li, layer in enumerate(w.layers):
-        wt = {k: v.float().numpy().astype(np.float64) for k, v in I.layer_weights(w, li).items()}
+        wt = {k: v.float().numpy().astype(np.float64) for k, v in cpu_w[li].items()}
+        flops += sum(stage_flops(ws, layer).values())
         t0 = time.perf_counter()
         O.prefill(x, pos, wt["w_q"], wt["w_kv"], wt["w_o"], wt["gamma_q"], wt["gamma_k"],
                   num_heads=w.H, num_kv_heads=w.H_kv, head_dim=w.d_h,
                   attn_type=layer.attn_type, window=w.window, rope_theta=layer.rope_theta,
                   rope_scale=layer.rope_scale, query_scale=w.query_scale)
         total += time.perf_counter() - t0
-    value = step_flops / total / 1e12
+    value = flops / total / 1e12
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -356,13 +408,14 @@ def cpu_baseline(w, step_flops):
                 break
     except OSError:
         pass
-    log(f"cpu baseline (fp64 oracle): {total:.2f} s for one step -> {value * 1e3:.2f} GFLOP/s "
-        f"on {threads} BLAS threads")
+    log(f"cpu baseline (fp64 oracle): {total:.2f} s for {flops:.3g} FLOP -> "
+        f"{value * 1e3:.2f} GFLOP/s on {threads} BLAS threads")
     return {"value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step ({w.name}, both layers), fp64 numpy; BLAS threads "
-                      f"{threads}, affinity {len(os.sched_getaffinity(0))} cores, "
-                      f"numpy elementwise ops single-threaded; {cpu_model}",
-            "seconds": round(total, 3)}
+            "sample": f"first {CPU_SAMPLE_T} of {w.T} tokens of {w.name} (same inputs), both "
+                      f"layers, algorithmic FLOPs of that sample; fp64 numpy, BLAS threads "
+                      f"{threads}, affinity {len(os.sched_getaffinity(0))} cores, numpy "
+                      f"elementwise ops single-threaded; {cpu_model}",
+            "seconds": round(total, 3), "sample_flops": flops}
 
 
 if __name__ == "__main__":

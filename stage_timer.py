@@ -1,7 +1,7 @@
 """Per-stage timing of the prefill path on the seeded synthetic workloads.
 
-    python global_layers_amd/stage_timer.py --workload 4 [--reps 10] [--warmup 3] [--cache] [--block]
-    python global_layers_amd/stage_timer.py --workload 5 --block   (decode: whole-block steps)
+    python stage_timer.py --workload 4 [--reps 10] [--warmup 3] [--cache] [--block]
+    python stage_timer.py --workload 5 --block   (decode: whole-block steps)
 
 Every layer of the workload goes through the C ABI one stage at a time
 (gemma3_attn_prefill_stages): the projection with its QK-norm / RoPE
@@ -28,7 +28,7 @@ import ctypes
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
