@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/gemma3_attn.h"
 #include "../../include/gemma3_attn_stages.h"
@@ -410,6 +411,8 @@ const char *gemma3_attn_status_string(int status) {
     case GEMMA3_ERR_UNSUPPORTED: return "shape has no kernel in this build";
     case GEMMA3_ERR_HIP: return "a HIP kernel launch failed";
     case GEMMA3_ERR_ALIGN: return "pointer is not 16-byte aligned";
+    case GEMMA3_ERR_SCRATCH:
+      return "the call needs more workspace than the static scratch holds (GEMMA3_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -868,6 +871,53 @@ int gemma3_attn_decode(const gemma3_attn_desc *desc, const void *x, const int32_
                        void *y, void *workspace, size_t workspace_bytes, void *hip_stream) {
   return gemma3_attn_decode_stages(desc, x, segment_pos, w, k_cache, v_cache, S, y, workspace,
                                    workspace_bytes, hip_stream, GEMMA3_DSTAGE_ALL);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the decode step's workspace lives in a static
+// device array, one copy per GPU, resident from the first call on that GPU
+// until the process ends. In host code `scratch` is only a stand-in for the
+// symbol: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever passed to kernels.
+namespace {
+static __device__ __align__(256) char scratch[GEMMA3_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch copy (NULL on failure).
+void *scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int gemma3_attn_decode_static(const gemma3_attn_desc *desc, const void *x,
+                              const int32_t *segment_pos, const gemma3_attn_weights *w,
+                              void *k_cache, void *v_cache, int32_t S, void *y,
+                              void *hip_stream) {
+  if (S < 1) return desc ? GEMMA3_ERR_SHAPE : GEMMA3_ERR_NULL;
+  gemma3_ws_layout L;
+  int st = layout(desc, S, &L);
+  if (st != GEMMA3_OK) return st;
+  if (L.total_bytes > GEMMA3_STATIC_SCRATCH_BYTES) return GEMMA3_ERR_SCRATCH;
+  void *ws = scratch_of_current_device();
+  if (!ws) return GEMMA3_ERR_HIP;
+  return gemma3_attn_decode_stages(desc, x, segment_pos, w, k_cache, v_cache, S, y, ws,
+                                   GEMMA3_STATIC_SCRATCH_BYTES, hip_stream, GEMMA3_DSTAGE_ALL);
 }
 
 }  // extern "C"

@@ -31,7 +31,7 @@ F32, BF16 = 0, 1
 OK = 0
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_WINDOW", 4: "ERR_DTYPE",
           5: "ERR_ROPE", 6: "ERR_WORKSPACE", 7: "ERR_UNSUPPORTED", 8: "ERR_HIP",
-          9: "ERR_ALIGN"}
+          9: "ERR_ALIGN", 10: "ERR_SCRATCH"}
 
 STAGE_QKV_PROJ, STAGE_QK_NORM, STAGE_ATTN, STAGE_OUT_PROJ, STAGE_ALL = 1, 2, 4, 8, 15
 STAGE_FORCE_EXACT_MAX = 16  # diagnostic: attention takes the exact-row-maximum pass
@@ -133,6 +133,10 @@ class KvFootprint(ctypes.Structure):
                 ("local_window_bytes", ctypes.c_size_t)]
 
 
+_lib.gemma3_attn_decode_static.restype = ctypes.c_int
+_lib.gemma3_attn_decode_static.argtypes = [ctypes.POINTER(Desc), _P, _P, ctypes.POINTER(Weights),
+                                           _P, _P, ctypes.c_int32, _P, _P]
+STATIC_SCRATCH_BYTES = 64 << 20   # GEMMA3_STATIC_SCRATCH_BYTES
 _lib.gemma3_kv_cache_footprint.restype = ctypes.c_int
 _lib.gemma3_kv_cache_footprint.argtypes = [ctypes.c_int32] * 7 + [ctypes.POINTER(KvFootprint)]
 _PREFILL_ARGS = [ctypes.POINTER(Desc), _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
@@ -162,7 +166,7 @@ EXPORTED = ("gemma3_attn_workspace_bytes", "gemma3_attn_prefill", "gemma3_attn_d
             "gemma3_stack_workspace_bytes", "gemma3_kv_cache_bytes", "gemma3_block_decode",
             "gemma3_block_decode_workspace_bytes", "gemma3_stack_prefill_cache",
             "gemma3_stack_decode", "gemma3_stack_decode_workspace_bytes",
-            "gemma3_kv_cache_footprint")
+            "gemma3_kv_cache_footprint", "gemma3_attn_decode_static")
 
 
 class Gemma3AttnError(ValueError):
@@ -552,6 +556,33 @@ def decode(x, segment_pos, weights: dict, k_cache, v_cache, *, H, H_kv, d_h, att
     _check(_lib.gemma3_attn_decode_stages(
         ctypes.byref(desc), _ptr(x), _ptr(segment_pos), ctypes.byref(w), _ptr(k_cache),
         _ptr(v_cache), S, _ptr(y), _ptr(workspace), workspace.numel(), _stream(), stages))
+    return y
+
+
+def decode_static(x, segment_pos, weights: dict, k_cache, v_cache, *, H, H_kv, d_h, attn_type,
+                  window, rope_theta, rope_scale, query_scale, y=None):
+    """decode() without a workspace: the library's static per-GPU scratch
+    (gemma3_attn_decode_static; nothing is allocated but y when not given)."""
+    dev = x.device
+    B, T, D = x.shape
+    S = k_cache.shape[1]
+    desc = make_desc(B=B, T=T, D=D, H=H, H_kv=H_kv, d_h=d_h, attn_type=attn_type,
+                     window=window, rope_theta=rope_theta, rope_scale=rope_scale,
+                     query_scale=query_scale, dtype=x.dtype)
+    _dev_tensor(x, x.dtype, "x", dev)
+    _dev_tensor(segment_pos, torch.int32, "segment_pos", dev)
+    if segment_pos.numel() != B:
+        raise ValueError("segment_pos must hold one position per row")
+    for n, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(c, x.dtype, n, dev)
+        if c.shape != (B, S, H_kv, d_h):
+            raise ValueError(f"{n} must be [B, S, H_kv, d_h]")
+    w = _weights(weights, x.dtype, dev)
+    if y is None:
+        y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    _check(_lib.gemma3_attn_decode_static(
+        ctypes.byref(desc), _ptr(x), _ptr(segment_pos), ctypes.byref(w), _ptr(k_cache),
+        _ptr(v_cache), S, _ptr(y), _stream()))
     return y
 
 

@@ -47,7 +47,8 @@
  *
  * Ownership and threading: every pointer is a DEVICE pointer unless noted;
  * the caller owns every buffer, the library allocates nothing, keeps no
- * pointer after it returns and holds no global state. Work is enqueued on
+ * pointer after it returns and holds no global state (the one exception is
+ * the static scratch of gemma3_attn_decode_static, described there). Work is enqueued on
  * `hip_stream` (a hipStream_t, NULL = the default stream) and the call
  * returns without synchronising; buffers must stay alive until the stream
  * passes the work. y must not alias an input; the workspace must not alias
@@ -89,7 +90,8 @@ typedef enum {
   GEMMA3_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gemma3_attn_workspace_bytes */
   GEMMA3_ERR_UNSUPPORTED = 7, /* valid shape this build has no kernel for (see below) */
   GEMMA3_ERR_HIP = 8,         /* a kernel launch failed */
-  GEMMA3_ERR_ALIGN = 9        /* a pointer is not 16-byte aligned */
+  GEMMA3_ERR_ALIGN = 9,       /* a pointer is not 16-byte aligned */
+  GEMMA3_ERR_SCRATCH = 10     /* workspace need exceeds GEMMA3_STATIC_SCRATCH_BYTES (static entry points) */
 } gemma3_status;
 
 /* One attention layer. All sizes are element counts. */
@@ -198,6 +200,29 @@ int gemma3_attn_decode(const gemma3_attn_desc *desc, const void *x,
                        const int32_t *segment_pos, const gemma3_attn_weights *w,
                        void *k_cache, void *v_cache, int32_t S, void *y,
                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gemma3_attn_decode with the same arguments, results and errors,
+ * but no workspace argument. Its workspace is a static device array of
+ * GEMMA3_STATIC_SCRATCH_BYTES in the library, one copy per GPU, set up by
+ * the first call on that GPU (with the caller's current device, which must
+ * be the device of hip_stream) and held until the process ends; the call
+ * itself allocates nothing. Shapes whose decode workspace
+ * (gemma3_attn_workspace_bytes(desc, S)) exceeds it return
+ * GEMMA3_ERR_SCRATCH and enqueue nothing (the 12B-like step, B = 16,
+ * S = 131072, needs 36.5 MiB). Every call on one GPU shares that GPU's
+ * array and nothing in it needs to start at any value: calls that may
+ * overlap on one GPU (different streams, or threads without ordering) race
+ * on it; serialise them, e.g. on one stream. GEMMA3_ERR_HIP also when the
+ * array's device address cannot be obtained.
+ */
+#define GEMMA3_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int gemma3_attn_decode_static(const gemma3_attn_desc *desc, const void *x,
+                              const int32_t *segment_pos, const gemma3_attn_weights *w,
+                              void *k_cache, void *v_cache, int32_t S, void *y,
+                              void *hip_stream);
 
 /*
  * One Gemma 3 block over the residual stream ("Full Gemma 3 Block", How it

@@ -288,3 +288,20 @@ def test_workspace_layout_prefill_and_decode():
     dl = _desc(B=16, T=1, D=3840, H=16, H_kv=8, d_h=256, window=1024)
     Ll = lib.workspace_layout(dl, 131072)
     assert Ll.n_chunks * Ll.chunk >= 1024 and Ll.total_bytes < Ld.total_bytes
+
+
+def test_static_decode_refuses_before_any_device_call():
+    # the allocation-free decode checks its workspace need against the
+    # static scratch before touching the device: 27B-shaped rows at full
+    # cache length need 300 MiB (scratch error), invalid shapes keep their
+    # own status; no GPU is needed for either
+    big = _desc(B=128, T=1, D=5376, H=32, H_kv=16, d_h=128, attn_type="GLOBAL", window=0)
+    assert lib.workspace_bytes(big, 131072) > lib.STATIC_SCRATCH_BYTES
+    w = lib.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    f = lib._lib.gemma3_attn_decode_static
+    assert f(ctypes.byref(big), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, 131072, FAKE, None) == 10
+    assert f(ctypes.byref(big), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, 0, FAKE, None) == 2
+    assert f(None, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, 0, FAKE, None) == 1
+    fits = _desc(B=16, T=1, D=3840, H=16, H_kv=8, d_h=256, attn_type="GLOBAL", window=0)
+    assert lib.workspace_bytes(fits, 131072) <= lib.STATIC_SCRATCH_BYTES
+    assert lib.STATUS[10] == "ERR_SCRATCH"
