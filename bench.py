@@ -332,8 +332,10 @@ def bench_decode(args, torch, np, W, I, lib, dev):
         for _ in range(3):
             call()
         times = []
-        stage_t = {"qkv_proj": [], "qk_norm_cache_write": [], "attention": [], "out_proj": []}
-        bits = [lib.DSTAGE_QKV_PROJ, lib.DSTAGE_QK_NORM, lib.DSTAGE_ATTN, lib.DSTAGE_OUT_PROJ]
+        # the attention stage forms q and the step's k, v (QK-norm, RoPE, alpha,
+        # cache write) itself, so it runs without the norm stage
+        stage_t = {"qkv_proj": [], "attention": [], "out_proj": []}
+        bits = [lib.DSTAGE_QKV_PROJ, lib.DSTAGE_ATTN, lib.DSTAGE_OUT_PROJ]
         for _ in range(args.decode_reps):
             flush.max()
             a, b = stream_events(torch)
@@ -360,7 +362,8 @@ def bench_decode(args, torch, np, W, I, lib, dev):
             "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "kv_bytes": kv_bytes, "other_bytes": other_bytes,
             "stage_us": {k: round(v * 1e3, 2) for k, v in st.items()},
-            "roofline": {"kernel": "decode attention (split-KV partial + combine)",
+            "roofline": {"kernel": "decode attention (split-KV partial with QK-norm/RoPE/cache "
+                                   "write + combine)",
                          "bound": "hbm", "achieved": round(core_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(core_gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic(f"{w.name}/{name}/attention")},

@@ -100,8 +100,9 @@ int layout(const gemma3_attn_desc *d, int32_t S, gemma3_ws_layout *L) {
   } else {
     const bool bf = d->dtype == GEMMA3_BF16;
     const bool local = d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING;
-    L->ksplit_qkv = bf ? gemv_ksplit((int)n_qkv, d->D) : 1;
-    L->ksplit_out = bf ? gemv_ksplit(d->D, d->H * d->d_h) : 1;
+    // the bf16 projections run over the whole K per workgroup (no split partials)
+    L->ksplit_qkv = 1;
+    L->ksplit_out = 1;
     L->chunk = decode_chunk(local, d->window, S, d->d_h);
     const int range = local && d->window < S ? d->window : S;
     L->n_chunks = div_up_h(range, L->chunk);
@@ -167,8 +168,8 @@ int block_layout(const gemma3_attn_desc *d, int32_t D_ff, gemma3_ws_layout *L, B
 }
 
 // Block decode workspace: the attention decode's, then the normed token, the
-// sublayer output, h, gate|up, the activation and the fp32 split-K partials
-// of the MLP's two projections.
+// sublayer output, h, gate|up, the activation and (fp32 path) the fp32
+// projection outputs before rounding.
 struct BlockDecodeLayout {
   size_t hn, a, h, gu, z, part, total;
   int ks_gu, ks_dn;
@@ -195,8 +196,8 @@ int block_decode_layout(const gemma3_attn_desc *d, int32_t D_ff, int32_t S, gemm
   off = align_up(off + B * 2 * (size_t)D_ff * esz);
   K->z = off;
   off = align_up(off + B * (size_t)D_ff * esz);
-  K->ks_gu = bf ? gemv_ksplit(2 * D_ff, d->D) : 1;
-  K->ks_dn = bf ? gemv_ksplit(d->D, D_ff) : 1;
+  K->ks_gu = 1;
+  K->ks_dn = 1;
   K->part = off;
   const size_t p1 = (size_t)K->ks_gu * B * 2 * D_ff, p2 = (size_t)K->ks_dn * B * d->D;
   off = align_up(off + (p1 > p2 ? p1 : p2) * 4);
@@ -292,13 +293,16 @@ int decode_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
 
   if (stages & GEMMA3_DSTAGE_QKV_PROJ) {
     if (bf)
-      RUN(launch_gemv16_bf16((const bf16 *)x, (const bf16 *)w->w_q, (const bf16 *)w->w_kv, Nq,
-                             pqkv, B, Nq + Nkv, d->D, L.ksplit_qkv, s));
+      RUN(launch_gemv16_bf16_wg<float>((const bf16 *)x, (const bf16 *)w->w_q,
+                                       (const bf16 *)w->w_kv, Nq, pqkv, B, Nq + Nkv, d->D, s));
     else
       RUN(launch_gemv_f32((const float *)x, (const float *)w->w_q, (const float *)w->w_kv, Nq,
                           pqkv, B, Nq + Nkv, d->D, s));
   }
-  if (stages & GEMMA3_DSTAGE_QK_NORM) {
+  // The attention stage forms q (and the step's k, v, written to the cache)
+  // itself; the norm stage alone runs the stand-alone kernel (q to the
+  // workspace, k and v to the cache) for inspection.
+  if ((stages & GEMMA3_DSTAGE_QK_NORM) && !(stages & GEMMA3_DSTAGE_ATTN)) {
     NormRopeArgs a{B, 1, d->H, d->H_kv, d->d_h, 0, d->rope_theta, d->rope_scale, d->query_scale};
     RUN(launch_qk_norm_rope_decode<T>(pqkv, L.ksplit_qkv, pos, (const T *)w->gamma_q,
                                       (const T *)w->gamma_k, qf, (T *)kc, (T *)vc, S, a, s));
@@ -306,17 +310,19 @@ int decode_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
   if (stages & GEMMA3_DSTAGE_ATTN) {
     DecodeArgs a{B, d->H, d->H_kv, d->d_h, S,
                  d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window, L.chunk,
-                 L.n_chunks};
-    RUN(launch_decode_attn<T>(qf, (const T *)kc, (const T *)vc, pos, part, o, a, s));
+                 L.n_chunks, d->rope_theta, d->rope_scale, d->query_scale};
+    RUN(launch_decode_attn<T>(pqkv, (const T *)w->gamma_q, (const T *)w->gamma_k, (T *)kc,
+                              (T *)vc, pos, part, o, a, s));
   }
   if (stages & GEMMA3_DSTAGE_OUT_PROJ) {
-    if (bf)
-      RUN(launch_gemv16_bf16((const bf16 *)o, (const bf16 *)w->w_o, (const bf16 *)w->w_o, d->D,
-                             ypart, B, d->D, Nq, L.ksplit_out, s));
-    else
+    if (bf) {
+      RUN(launch_gemv16_bf16_wg<bf16>((const bf16 *)o, (const bf16 *)w->w_o,
+                                      (const bf16 *)w->w_o, d->D, (bf16 *)y, B, d->D, Nq, s));
+    } else {
       RUN(launch_gemv_f32((const float *)o, (const float *)w->w_o, (const float *)w->w_o, d->D,
                           ypart, B, d->D, Nq, s));
-    RUN(launch_splitk_reduce<T>(ypart, L.ksplit_out, (T *)y, (long)B * d->D, s));
+      RUN(launch_splitk_reduce<T>(ypart, L.ksplit_out, (T *)y, (long)B * d->D, s));
+    }
   }
   return GEMMA3_OK;
 }
@@ -373,22 +379,20 @@ int block_decode_impl(const gemma3_attn_desc *d, int D_ff, const T *x, const int
   RUN(launch_rms_norm_add<T>(x, a, (const T *)w->post_attn_norm, h, B, D, s));
   RUN(launch_rms_norm_add<T>(nullptr, h, (const T *)w->pre_ffw_norm, hn, B, D, s));
   if constexpr (sizeof(T) == 2) {
-    RUN(launch_gemv16_bf16(hn, (const bf16 *)w->w_gating, (const bf16 *)w->w_gating, 2 * D_ff,
-                           part, B, 2 * D_ff, D, K.ks_gu, s));
+    RUN(launch_gemv16_bf16_wg<bf16>(hn, (const bf16 *)w->w_gating, (const bf16 *)w->w_gating,
+                                    2 * D_ff, gu, B, 2 * D_ff, D, s));
+    RUN(launch_geglu<T>(gu, z, B, D_ff, s));
+    RUN(launch_gemv16_bf16_wg<bf16>(z, (const bf16 *)w->w_linear, (const bf16 *)w->w_linear, D,
+                                    a, B, D, D_ff, s));
   } else {
     RUN(launch_gemv_f32(hn, (const float *)w->w_gating, (const float *)w->w_gating, 2 * D_ff,
                         part, B, 2 * D_ff, D, s));
-  }
-  RUN(launch_splitk_reduce<T>(part, K.ks_gu, gu, (long)B * 2 * D_ff, s));
-  RUN(launch_geglu<T>(gu, z, B, D_ff, s));
-  if constexpr (sizeof(T) == 2) {
-    RUN(launch_gemv16_bf16(z, (const bf16 *)w->w_linear, (const bf16 *)w->w_linear, D, part, B,
-                           D, D_ff, K.ks_dn, s));
-  } else {
+    RUN(launch_splitk_reduce<T>(part, K.ks_gu, gu, (long)B * 2 * D_ff, s));
+    RUN(launch_geglu<T>(gu, z, B, D_ff, s));
     RUN(launch_gemv_f32(z, (const float *)w->w_linear, (const float *)w->w_linear, D, part, B, D,
                         D_ff, s));
+    RUN(launch_splitk_reduce<T>(part, K.ks_dn, a, (long)B * D, s));
   }
-  RUN(launch_splitk_reduce<T>(part, K.ks_dn, a, (long)B * D, s));
   RUN(launch_rms_norm_add<T>(h, a, (const T *)w->post_ffw_norm, y, B, D, s));
   return GEMMA3_OK;
 }

@@ -106,3 +106,13 @@ DEVI void load_lds16(const void *sbase, uint32_t lane_off, uint32_t lds_wave_off
                : "v"(lane_off), "s"(sbase), "{m0}"(lds_wave_off)
                : "memory");
 }
+
+// RoPE rotation of one channel pair at integer position p: angle
+// p / scale * inv_freq, reduced modulo one turn in fp64 (positions reach
+// 131071, where an fp32 angle would be off by ~1e-2 rad), then fp32 sincos.
+DEVI void rope_sincos(int p, double inv_scale, double inv_freq, float &c, float &s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = (double)p * inv_scale * inv_freq;
+  a -= rint(a * (1.0 / two_pi)) * two_pi;
+  sincosf((float)a, &s, &c);
+}

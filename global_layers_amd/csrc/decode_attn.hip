@@ -7,14 +7,20 @@
 //  * The allowed slot range [lo, pos] of row b is cut into chunks of C slots.
 //    One workgroup streams one (row, chunk, KV head): K and V rows of that
 //    head, d_h contiguous elements per slot, 16-byte loads, each byte read once
-//    for all the query heads of the GQA group.
-//  * Inside a wave, d_h/32 lanes share one slot (32 channels each); per-slot
-//    logits are a short xor-shuffle sum. Each slot group keeps an online
-//    softmax state (m, l, acc) per query head; groups and waves are merged by
-//    log-sum-exp, and the chunk's (acc, m, l) go to the workspace.
-//  * A second kernel merges the chunks of each (row, head) the same way and
-//    divides by the total weight. Logits are in log2 units (q pre-scaled by
-//    log2 e), so every exponential is an exp2.
+//    for all the query heads of the GQA group, in double-buffered rounds (the
+//    next round's loads are in flight while this one is computed).
+//  * The workgroup forms its queries itself from the raw projections
+//    (RMSNorm with (1 + gamma), RoPE, alpha: "QK-Norm", How it works) while
+//    its first round of loads is in flight; the workgroup whose chunk ends at
+//    the row's position also forms the step's own key and value, writes them to
+//    that cache slot and uses them there.
+//  * Inside a wave, d_h/16 lanes share one slot (16 channels each); per-slot
+//    logits are a short DPP sum. Each slot group keeps an online softmax state
+//    (m, l, acc) per query head; groups and waves are merged by log-sum-exp,
+//    and the chunk's (acc, m, l) go to the workspace.
+//  * A second kernel merges the chunks of each (row, head) the same way, one
+//    channel per thread, and divides by the total weight. Logits are in log2
+//    units (q pre-scaled by log2 e), so every exponential is an exp2.
 #include <type_traits>
 
 #include "common.h"
@@ -75,15 +81,28 @@ DEVI void row_range(const int32_t *pos, int b, int S, int local, int window, int
 }
 
 // grid: x = chunk, y = b, z = kh * n_hgrp + head group. GQ query heads per workgroup.
+// The workgroup forms its own queries from the raw projections (QK-norm,
+// RoPE, alpha), and the workgroup whose chunk ends at the row's position also
+// forms the step's own key and value, writes them to that cache slot (head
+// group 0 only) and uses them for that slot. The first round of cache loads is
+// issued before this set-up, so its latency hides the norm and RoPE work.
 template <typename T, int D, int GQ>
 __global__ void __launch_bounds__(kDecThreads)
-decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
-                    const T *__restrict__ v_cache, const int32_t *__restrict__ pos,
+decode_attn_partial(const float *__restrict__ qkv, const T *__restrict__ gamma_q,
+                    const T *__restrict__ gamma_k, T *__restrict__ k_cache,
+                    T *__restrict__ v_cache, const int32_t *__restrict__ pos,
                     float *__restrict__ part, DecodeArgs a, int n_hgrp) {
   constexpr int LPS = D / kChansPerLane;         // lanes per slot
   constexpr int kGroupsPerWave = kWave / LPS;
-  constexpr int NG = kGroupsPerWave * (kDecThreads / kWave);
-  __shared__ float red[kDecThreads / kWave][GQ][D + 2];
+  constexpr int kWaves = kDecThreads / kWave;
+  constexpr int NG = kGroupsPerWave * kWaves;
+  constexpr int kHalf = D / 2;
+  constexpr int kVec = GQ + 2;                   // query heads, the step's key, its value
+  __shared__ float red[kWaves][GQ][D + 2];
+  __shared__ float raw[kVec][D];                 // raw projections, then finished queries
+  __shared__ float ssq[kVec];
+  __shared__ float2 rot[kHalf];                  // (cos, sin) of each channel pair
+  __shared__ __attribute__((aligned(16))) T kv_new[2][D];  // the step's key and value, as cached
 
   const int chunk = blockIdx.x, b = blockIdx.y;
   const int kh = blockIdx.z / n_hgrp, hgrp = blockIdx.z % n_hgrp;
@@ -94,19 +113,105 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   const int c_lo = lo + chunk * a.chunk;
   if (c_lo > hi) return;  // chunk past this row's range (uniform per block)
   const int c_hi = min(hi, c_lo + a.chunk - 1);
+  const bool has_new = c_hi == hi;  // this chunk ends at the row's position
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane % LPS;             // which 16-channel slice
   const int grp = wave * kGroupsPerWave + lane / LPS;
 
+  const size_t slot_stride = (size_t)a.Hk * D;
+  const T *kb = k_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D;
+  const T *vb = v_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D;
+
+  // Rounds of kDecUnroll slots per slot group, double-buffered: the loads of
+  // round r + 1 are in flight while round r is computed, so each wave keeps
+  // streaming from HBM without a gap per round.
+  struct Round {
+    Slice<T> k[kDecUnroll], v[kDecUnroll];
+    bool ok[kDecUnroll];
+  };
+  Round buf[2];
+  constexpr int kStep = NG * kDecUnroll;  // slots of one round of the workgroup
+  auto issue = [&](Round &r, int s_base) {
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int s = s_base + u * NG;
+      r.ok[u] = s <= c_hi;
+      if (r.ok[u]) {
+        r.k[u].template load<LPS>(kb + (size_t)s * slot_stride, sub);
+        r.v[u].template load<LPS>(vb + (size_t)s * slot_stride, sub);
+      } else {
+        r.k[u].zero();
+        r.v[u].zero();
+      }
+    }
+  };
+  const int s_first = c_lo + grp;
+  issue(buf[0], s_first);
+
+  // ---- queries (and the step's key / value) from the raw projections
+  // ("QK-Norm", How it works: RMSNorm with (1 + gamma) over d_h, then RoPE,
+  // then alpha; V is not normalised)
+  const int n_qkv = (a.H + 2 * a.Hk) * D;
+  const float *row = qkv + (size_t)b * n_qkv;
+  const int n_vec = GQ + (has_new ? 2 : 0);
+  for (int e = tid; e < n_vec * D; e += kDecThreads) {
+    const int v = e / D, c = e % D;
+    const int col = v < GQ ? (h0 + v) * D : v == GQ ? (a.H + kh) * D : (a.H + a.Hk + kh) * D;
+    raw[v][c] = row[col + c];
+  }
+  if (tid < kHalf) {
+    // theta^(-2i/d_h) = 2^(-(2i/d_h) log2 theta), in fp64
+    const double inv_freq = exp2(-2.0 * (double)tid / (double)D * log2((double)a.theta));
+    float c, sn;
+    rope_sincos(hi, 1.0 / (double)a.scale, inv_freq, c, sn);
+    rot[tid] = make_float2(c, sn);
+  }
+  __syncthreads();
+  for (int v = wave; v < n_vec - (has_new ? 1 : 0); v += kWaves) {  // sums of squares (not V)
+    float sq = 0.f;
+#pragma unroll
+    for (int c = lane; c < D; c += kWave) sq = fmaf(raw[v][c], raw[v][c], sq);
+    sq = wave_sum(sq);
+    if (lane == 0) ssq[v] = sq;
+  }
+  __syncthreads();
+  const float q_mul = a.alpha * kLog2e;  // logits in log2 units: every exponential is an exp2
+  for (int e = tid; e < (GQ + (has_new ? 1 : 0)) * kHalf; e += kDecThreads) {
+    const int v = e / kHalf, i = e % kHalf;
+    const bool is_q = v < GQ;
+    const T *gam = is_q ? gamma_q : gamma_k;
+    const float r = rsqrtf(ssq[v] / (float)D + 1e-6f);
+    const float y1 = raw[v][i] * r * (1.f + to_f32(gam[i]));
+    const float y2 = raw[v][i + kHalf] * r * (1.f + to_f32(gam[i + kHalf]));
+    const float2 cs = rot[i];
+    const float o1 = y1 * cs.x - y2 * cs.y, o2 = y2 * cs.x + y1 * cs.y;
+    if (is_q) {
+      raw[v][i] = o1 * q_mul;
+      raw[v][i + kHalf] = o2 * q_mul;
+    } else {
+      kv_new[0][i] = from_f32<T>(o1);
+      kv_new[0][i + kHalf] = from_f32<T>(o2);
+    }
+  }
+  if (has_new)
+    for (int c = tid; c < D; c += kDecThreads) kv_new[1][c] = from_f32<T>(raw[GQ + 1][c]);
+  __syncthreads();
+  if (has_new && hgrp == 0) {  // the cache write ("Gemma 3 Attention Block", Cache)
+    T *kd = k_cache + ((size_t)b * a.S + hi) * slot_stride + (size_t)kh * D;
+    T *vd = v_cache + ((size_t)b * a.S + hi) * slot_stride + (size_t)kh * D;
+    for (int c = tid; c < D; c += kDecThreads) {
+      kd[c] = kv_new[0][c];
+      vd[c] = kv_new[1][c];
+    }
+  }
+
   float qv[GQ][kChansPerLane];
 #pragma unroll
-  for (int g = 0; g < GQ; ++g) {
-    const float *qp = q + ((size_t)b * a.H + h0 + g) * D;
+  for (int g = 0; g < GQ; ++g)
 #pragma unroll
     for (int i = 0; i < kChansPerLane; ++i)
-      qv[g][i] = qp[Slice<T>::template chan<LPS>(sub, i)] * kLog2e;
-  }
+      qv[g][i] = raw[g][Slice<T>::template chan<LPS>(sub, i)];
   float m[GQ], l[GQ], acc[GQ][kChansPerLane];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) {
@@ -116,25 +221,14 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
     for (int i = 0; i < kChansPerLane; ++i) acc[g][i] = 0.f;
   }
 
-  const size_t slot_stride = (size_t)a.Hk * D;
-  const T *kb = k_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D;
-  const T *vb = v_cache + ((size_t)b * a.S) * slot_stride + (size_t)kh * D;
-
-  for (int s_base = c_lo + grp; s_base <= c_hi; s_base += NG * kDecUnroll) {
-    Slice<T> ks[kDecUnroll], vs[kDecUnroll];
-    bool ok[kDecUnroll];
-    // all K and V loads of the iteration are in flight before any math
+  auto compute = [&](Round &r, int s_base) {
+    if (has_new) {  // the step's own slot: its key and value as just formed
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      const int s = s_base + u * NG;
-      ok[u] = s <= c_hi;
-      if (ok[u]) {
-        ks[u].template load<LPS>(kb + (size_t)s * slot_stride, sub);
-        vs[u].template load<LPS>(vb + (size_t)s * slot_stride, sub);
-      } else {
-        ks[u].zero();
-        vs[u].zero();
-      }
+      for (int u = 0; u < kDecUnroll; ++u)
+        if (r.ok[u] && s_base + u * NG == hi) {
+          r.k[u].template load<LPS>(kv_new[0], sub);
+          r.v[u].template load<LPS>(kv_new[1], sub);
+        }
     }
     float x[kDecUnroll][GQ];
 #pragma unroll
@@ -143,9 +237,9 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
       for (int g = 0; g < GQ; ++g) {
         float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < kChansPerLane; ++i) d = fmaf(qv[g][i], ks[u].get(i), d);
+        for (int i = 0; i < kChansPerLane; ++i) d = fmaf(qv[g][i], r.k[u].get(i), d);
         d = group_sum_dpp<LPS>(d);
-        x[u][g] = ok[u] ? d : -INFINITY;
+        x[u][g] = r.ok[u] ? d : -INFINITY;
       }
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
@@ -170,7 +264,15 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
       for (int g = 0; g < GQ; ++g)
 #pragma unroll
         for (int i = 0; i < kChansPerLane; ++i)
-          acc[g][i] = fmaf(x[u][g], vs[u].get(i), acc[g][i]);
+          acc[g][i] = fmaf(x[u][g], r.v[u].get(i), acc[g][i]);
+  };
+  // rounds alternate between the two buffers (compile-time indices)
+  for (int s_base = s_first; s_base <= c_hi; s_base += 2 * kStep) {
+    if (s_base + kStep <= c_hi) issue(buf[1], s_base + kStep);
+    compute(buf[0], s_base);
+    if (s_base + kStep > c_hi) break;
+    if (s_base + 2 * kStep <= c_hi) issue(buf[0], s_base + 2 * kStep);
+    compute(buf[1], s_base + kStep);
   }
 
   // merge the slot groups of this wave (lanes with equal `sub` hold equal channels)
@@ -227,74 +329,61 @@ decode_attn_partial(const float *__restrict__ q, const T *__restrict__ k_cache,
   }
 }
 
-// grid: x = H, y = B; D threads. Each chunk's (m, l) is read once into LDS;
-// the chunk weights exp2(m_j - M) are formed there, then each thread sums its
-// channel over the chunks with kCombineBatch loads in flight per round trip.
+// grid: x = H, y = B; D threads, one channel each. Every thread loads, for a
+// batch of up to kCombineBatch chunks at once, each chunk's (m, l) (the same
+// addresses across the workgroup) and its own channel of each partial, then
+// merges them by log-sum-exp with a running maximum: one round trip per batch
+// and no barrier.
 constexpr int kMaxChunks = 128;  // decode_chunk keeps every row at <= 128 chunks
-constexpr int kCombineBatch = 32;
+constexpr int kCombineBatch = 16;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
 decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos,
                     T *__restrict__ o, DecodeArgs a) {
-  __shared__ float m_s[kMaxChunks], l_s[kMaxChunks], wgt[kMaxChunks];
-  __shared__ float red[D / 64];
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int lane = c & 63, wave = c >> 6;
   int lo, hi;
   row_range(pos, b, a.S, a.local, a.window, lo, hi);
   const int n = hi >= lo ? div_up(hi - lo + 1, a.chunk) : 0;
   const float *pp = part + ((size_t)b * a.H + h) * a.n_chunks * (D + 2);
-
-  float mx = -INFINITY;
-  for (int j = c; j < n; j += D) {
-    const float2 ml = *reinterpret_cast<const float2 *>(pp + (size_t)j * (D + 2) + D);
-    m_s[j] = ml.x;
-    l_s[j] = ml.y;
-    mx = fmaxf(mx, ml.x);
-  }
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) M = fmaxf(M, red[i]);
-  const float mu = M == -INFINITY ? 0.f : M;
-  __syncthreads();
-  float sl = 0.f;
-  for (int j = c; j < n; j += D) {  // the entries this thread wrote above
-    const float wj = exp2f(m_s[j] - mu);
-    wgt[j] = wj;
-    sl += wj * l_s[j];
-  }
-  sl = wave_sum(sl);
-  if (lane == 0) red[wave] = sl;
-  __syncthreads();
-  float L = 0.f;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) L += red[i];
-
-  float sa = 0.f;
+  float M = -INFINITY, sa = 0.f, sl = 0.f;
   for (int j = 0; j < n; j += kCombineBatch) {
-    float v[kCombineBatch];
+    float mv[kCombineBatch], lv[kCombineBatch], v[kCombineBatch];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u)
-      v[u] = j + u < n ? pp[(size_t)(j + u) * (D + 2) + c] : 0.f;
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const bool ok = j + u < n;
+      const float *pj = pp + (size_t)(ok ? j + u : 0) * (D + 2);
+      const float2 ml = *reinterpret_cast<const float2 *>(pj + D);
+      mv[u] = ok ? ml.x : -INFINITY;
+      lv[u] = ml.y;
+      v[u] = pj[c];
+    }
+    float mb = M;
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u)
-      if (j + u < n) sa = fmaf(wgt[j + u], v[u], sa);
+    for (int u = 0; u < kCombineBatch; ++u) mb = fmaxf(mb, mv[u]);
+    // every chunk holds at least one allowed slot, so mb is finite
+    const float corr = exp2f(M - mb);
+    sa *= corr;
+    sl *= corr;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float wj = exp2f(mv[u] - mb);  // 0 for the unused tail of a batch
+      sa = fmaf(wj, v[u], sa);
+      sl = fmaf(wj, lv[u], sl);
+    }
+    M = mb;
   }
-  o[((size_t)b * a.H + h) * D + c] = from_f32<T>(L > 0.f ? sa / L : 0.f);
+  o[((size_t)b * a.H + h) * D + c] = from_f32<T>(sl > 0.f ? sa / sl : 0.f);
 }
 
 template <typename T, int D, int GQ>
-hipError_t launch_dec(const float *q, const T *kc, const T *vc, const int32_t *pos, float *part,
-                      T *o, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_dec(const float *qkv, const T *gq, const T *gk, T *kc, T *vc,
+                      const int32_t *pos, float *part, T *o, const DecodeArgs &a, hipStream_t s) {
   const int G = a.H / a.Hk;
   const int n_hgrp = G / GQ;
   dim3 grid(a.n_chunks, a.B, a.Hk * n_hgrp);
-  hipLaunchKernelGGL((decode_attn_partial<T, D, GQ>), grid, dim3(kDecThreads), 0, s, q, kc, vc,
-                     pos, part, a, n_hgrp);
+  hipLaunchKernelGGL((decode_attn_partial<T, D, GQ>), grid, dim3(kDecThreads), 0, s, qkv, gq, gk,
+                     kc, vc, pos, part, a, n_hgrp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_attn_combine<T, D>), dim3(a.H, a.B), dim3(D), 0, s, part, pos, o, a);
@@ -302,12 +391,13 @@ hipError_t launch_dec(const float *q, const T *kc, const T *vc, const int32_t *p
 }
 
 template <typename T, int D>
-hipError_t launch_dec_g(const float *q, const T *kc, const T *vc, const int32_t *pos,
-                        float *part, T *o, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_dec_g(const float *qkv, const T *gq, const T *gk, T *kc, T *vc,
+                        const int32_t *pos, float *part, T *o, const DecodeArgs &a,
+                        hipStream_t s) {
   const int G = a.H / a.Hk;
-  if (G % 4 == 0) return launch_dec<T, D, 4>(q, kc, vc, pos, part, o, a, s);
-  if (G % 2 == 0) return launch_dec<T, D, 2>(q, kc, vc, pos, part, o, a, s);
-  return launch_dec<T, D, 1>(q, kc, vc, pos, part, o, a, s);
+  if (G % 4 == 0) return launch_dec<T, D, 4>(qkv, gq, gk, kc, vc, pos, part, o, a, s);
+  if (G % 2 == 0) return launch_dec<T, D, 2>(qkv, gq, gk, kc, vc, pos, part, o, a, s);
+  return launch_dec<T, D, 1>(qkv, gq, gk, kc, vc, pos, part, o, a, s);
 }
 
 template <typename T>
@@ -329,19 +419,25 @@ int decode_chunk(int local, int window, int S, int d_h) {
   // global: at most 128 chunks per row, so no workgroup streams for long
   // after the others (a shorter tail) while the combine stays cheap
   const int range = local && window < S ? window : S;
-  int c = local ? 64 : 256;  // a workgroup covers 16 slot groups x kDecUnroll slots per pass
+  // a workgroup streams rounds of 16 slot groups x kDecUnroll slots; local
+  // rows take chunks of 256 slots (4 rounds), so the W = 1024 window of a
+  // (row, KV head) is 4 workgroups and the whole step fits one wave of
+  // resident workgroups, each paying its query set-up once
+  int c = 256;
   while (div_up_h(range, c) > kMaxChunks) c *= 2;
   return c;
 }
 
 template <typename T>
-hipError_t launch_decode_attn(const float *q, const T *k_cache, const T *v_cache,
-                              const int32_t *pos, float *part, T *o, const DecodeArgs &a,
-                              hipStream_t s) {
+hipError_t launch_decode_attn(const float *qkv, const T *gamma_q, const T *gamma_k, T *k_cache,
+                              T *v_cache, const int32_t *pos, float *part, T *o,
+                              const DecodeArgs &a, hipStream_t s) {
   switch (a.d_h) {
-    case 64: return launch_dec_g<T, 64>(q, k_cache, v_cache, pos, part, o, a, s);
-    case 128: return launch_dec_g<T, 128>(q, k_cache, v_cache, pos, part, o, a, s);
-    case 256: return launch_dec_g<T, 256>(q, k_cache, v_cache, pos, part, o, a, s);
+    case 64: return launch_dec_g<T, 64>(qkv, gamma_q, gamma_k, k_cache, v_cache, pos, part, o, a, s);
+    case 128:
+      return launch_dec_g<T, 128>(qkv, gamma_q, gamma_k, k_cache, v_cache, pos, part, o, a, s);
+    case 256:
+      return launch_dec_g<T, 256>(qkv, gamma_q, gamma_k, k_cache, v_cache, pos, part, o, a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -354,11 +450,11 @@ hipError_t launch_splitk_reduce(const float *part, int ksplit, T *y, long MN, hi
   return hipGetLastError();
 }
 
-template hipError_t launch_decode_attn<bf16>(const float *, const bf16 *, const bf16 *,
-                                             const int32_t *, float *, bf16 *,
+template hipError_t launch_decode_attn<bf16>(const float *, const bf16 *, const bf16 *, bf16 *,
+                                             bf16 *, const int32_t *, float *, bf16 *,
                                              const DecodeArgs &, hipStream_t);
-template hipError_t launch_decode_attn<float>(const float *, const float *, const float *,
-                                              const int32_t *, float *, float *,
+template hipError_t launch_decode_attn<float>(const float *, const float *, const float *, float *,
+                                              float *, const int32_t *, float *, float *,
                                               const DecodeArgs &, hipStream_t);
 template hipError_t launch_splitk_reduce<bf16>(const float *, int, bf16 *, long, hipStream_t);
 template hipError_t launch_splitk_reduce<float>(const float *, int, float *, long, hipStream_t);

@@ -10,9 +10,9 @@
 //    before the barrier. The MFMA is issued with the weight fragment as its
 //    first operand so that each lane ends up holding 4 consecutive output
 //    columns (one 8-byte store).
-//  * gemv16_bf16_splitk: decode (M = batch <= 16 per M block). Weight-streaming
-//    16x16x32 MFMAs, each workgroup one 16-column block over one K split, fp32
-//    partials per split; the consumer adds the splits.
+//  * gemv16_bf16_wg: decode (M = batch <= 16 per M block). Weight-streaming
+//    16x16x32 MFMAs, each workgroup one or two 16-column blocks over the whole
+//    K range split among its 8 waves, added through LDS; fp32 or bf16 output.
 #include "common.h"
 #include "kernels.h"
 
@@ -434,83 +434,80 @@ hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf
 }
 
 // ---------------------------------------------------------------------------
-// Decode projections: P[split][m][n] = sum_{k in split} A[m][k] * W[n][k]
+// Decode projections: Y[m][n] = sum_k A[m][k] * W[n][k] for M <= 16 rows per
+// M block (the batch of one-token rows)
 // ---------------------------------------------------------------------------
-constexpr int kGemvWaves = 4;
-constexpr int kGemvNB = 4;      // 16-column blocks per workgroup (one activation load feeds 4)
-constexpr int kGemvUnroll = 8;  // k-steps a wave keeps in flight (5 KB of loads each)
+// Whole-K variant: one workgroup = NB 16-column blocks over the whole K
+// range, its kGemvWgWaves waves taking consecutive slices of the 32-wide
+// k-steps; every load of a wave's slice (up to kGemvWgSteps steps) is in
+// flight before its first MFMA, each activation fragment feeds NB MFMAs, and
+// the waves' 16 x 16 accumulators are added through LDS, the finished
+// outputs stored as fp32 or rounded to bf16. No split partials and no
+// reduction launch.
+constexpr int kGemvWgWaves = 8;
+constexpr int kGemvWgSteps = 16;
 
-// One workgroup = kGemvNB 16-column blocks over one K split; its 4 waves take
-// consecutive quarters of the split's 32-wide k-steps and add their 16 x 16
-// accumulators through LDS, so the split count (and the partial traffic)
-// stays small while every CU still streams from many waves. Each activation
-// fragment feeds kGemvNB MFMAs, so nearly all load traffic is weights.
-__global__ void __launch_bounds__(kGemvWaves * 64)
-gemv16_bf16_splitk(const bf16 *__restrict__ A, const bf16 *__restrict__ W0,
-                   const bf16 *__restrict__ W1, int N0, float *__restrict__ P, int M, int N, int K,
-                   int k_per_split) {
-  __shared__ f32x4 red[kGemvWaves][kGemvNB][64];
+template <typename OutT, int NB>
+__global__ void __launch_bounds__(kGemvWgWaves * 64)
+gemv16_bf16_wg(const bf16 *__restrict__ A, const bf16 *__restrict__ W0,
+               const bf16 *__restrict__ W1, int N0, OutT *__restrict__ Y, int M, int N, int K) {
+  __shared__ f32x4 red[kGemvWgWaves][NB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nb = blockIdx.x;  // group of kGemvNB 16-column blocks
-  const int split = blockIdx.y, mb = blockIdx.z;
+  const int mb = blockIdx.y;
   const int m = mb * 16 + (lane & 15);
   const int koff = (lane >> 4) * 8;
-  const int steps = k_per_split / 32;
-  const int per_wave = div_up(steps, kGemvWaves);
-  const int k_begin = split * k_per_split + wave * per_wave * 32;
-  const int k_end = min(split * k_per_split + k_per_split, k_begin + per_wave * 32);
+  const int steps = K / 32;
+  const int per_wave = div_up(steps, kGemvWgWaves);
+  const int s_begin = wave * per_wave, s_end = min(steps, s_begin + per_wave);
   const bool m_ok = m < M;
   const bf16 *ap = A + (size_t)(m_ok ? m : 0) * K + koff;
-  // a group never straddles N0 (the caller keeps N0 a multiple of 16 kGemvNB)
-  const bf16 *wp[kGemvNB];
-  bool n_ok[kGemvNB];
+  const bf16 *wp[NB];
+  bool n_ok[NB];
 #pragma unroll
-  for (int j = 0; j < kGemvNB; ++j) {
-    const int n = (nb * kGemvNB + j) * 16 + (lane & 15);
+  for (int j = 0; j < NB; ++j) {
+    const int n = (blockIdx.x * NB + j) * 16 + (lane & 15);
     n_ok[j] = n < N;
     const int nn = n_ok[j] ? n : 0;
     wp[j] = (nn < N0 ? W0 + (size_t)nn * K : W1 + (size_t)(nn - N0) * K) + koff;
   }
 
-  f32x4 acc[kGemvNB];
+  f32x4 acc[NB];
 #pragma unroll
-  for (int j = 0; j < kGemvNB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = k_begin; k < k_end; k += 32 * kGemvUnroll) {
-    u32x4 wv[kGemvUnroll][kGemvNB], av[kGemvUnroll];
-    // every load of the round is in flight before the first MFMA; steps past
-    // the range contribute zero operands
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = s_begin; s0 < s_end; s0 += kGemvWgSteps) {
+    u32x4 wv[kGemvWgSteps][NB], av[kGemvWgSteps];
 #pragma unroll
-    for (int u = 0; u < kGemvUnroll; ++u) {
-      const int kk = k + u * 32;
-      const bool ok = kk < k_end;
-      av[u] = ok && m_ok ? ld16(ap + kk) : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < kGemvWgSteps; ++u) {
+      const int st = s0 + u;
+      const bool ok = st < s_end;
 #pragma unroll
-      for (int j = 0; j < kGemvNB; ++j)
-        wv[u][j] = ok && n_ok[j] ? ld16(wp[j] + kk) : u32x4{0, 0, 0, 0};
+      for (int j = 0; j < NB; ++j)
+        wv[u][j] = ok && n_ok[j] ? ld16(wp[j] + st * 32) : u32x4{0, 0, 0, 0};
+      av[u] = ok && m_ok ? ld16(ap + st * 32) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kGemvUnroll; ++u)
+    for (int u = 0; u < kGemvWgSteps; ++u)
 #pragma unroll
-      for (int j = 0; j < kGemvNB; ++j)
+      for (int j = 0; j < NB; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
                                                          __builtin_bit_cast(bf16x8, wv[u][j]),
                                                          acc[j], 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < kGemvNB; ++j) red[wave][j][lane] = acc[j];
+  for (int j = 0; j < NB; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
-  // wave w finishes column block w (kGemvNB == kGemvWaves)
-  static_assert(kGemvNB == kGemvWaves, "one column block per finishing wave");
+  if (wave >= NB) return;
+  // wave j finishes column block j
   f32x4 sum = red[0][wave][lane];
 #pragma unroll
-  for (int w = 1; w < kGemvWaves; ++w) sum += red[w][wave][lane];
+  for (int w = 1; w < kGemvWgWaves; ++w) sum += red[w][wave][lane];
   // D[m][n]: lane column n = lane % 16, rows m = (lane / 16) * 4 + r.
-  const int col = (nb * kGemvNB + wave) * 16 + (lane & 15);
-  if (col >= N) return;
+  const int n = (blockIdx.x * NB + wave) * 16 + (lane & 15);
+  if (n >= N) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = mb * 16 + (lane >> 4) * 4 + r;
-    if (row < M) P[((size_t)split * M + row) * N + col] = sum[r];
+    if (row < M) Y[(size_t)row * N + n] = from_f32<OutT>(sum[r]);
   }
 }
 
@@ -557,21 +554,25 @@ hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_k
   return launch_gemm<128, 256, 2, 4, 64, 3, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
 }
 
-int gemv_ksplit(int N, int K) {
-  // about 6+ waves per CU in flight (4 per workgroup, up to 40 KB of loads each), K
-  // splits of whole k-steps; more splits cost more partial traffic than they gain
-  const long nblk = div_up_h(N, 16 * kGemvNB);
-  int s = 1;
-  while (s < 16 && nblk * s * kGemvWaves < 1536) s *= 2;
-  while (s > 1 && (K / 32) % s != 0) s /= 2;
-  return s;
-}
-
-hipError_t launch_gemv16_bf16(const bf16 *A, const bf16 *W0, const bf16 *W1, int N0, float *P,
-                              int M, int N, int K, int ksplit, hipStream_t s) {
-  if (N0 < N && N0 % (16 * kGemvNB) != 0) return hipErrorInvalidValue;
-  dim3 grid(div_up_h(N, 16 * kGemvNB), ksplit, div_up_h(M, 16));
-  hipLaunchKernelGGL(gemv16_bf16_splitk, grid, dim3(kGemvWaves * 64), 0, s, A, W0, W1, N0, P, M,
-                     N, K, K / ksplit);
+template <typename OutT>
+hipError_t launch_gemv16_bf16_wg(const bf16 *A, const bf16 *W0, const bf16 *W1, int N0, OutT *Y,
+                                 int M, int N, int K, hipStream_t s) {
+  if (K % 32 != 0 || (N0 < N && N0 % 32 != 0)) return hipErrorInvalidValue;
+  // two column blocks per workgroup (one activation load feeds two MFMAs)
+  // while that still leaves a workgroup for every CU, else one
+  if (div_up_h(N, 32) >= 256) {
+    dim3 grid(div_up_h(N, 32), div_up_h(M, 16));
+    hipLaunchKernelGGL((gemv16_bf16_wg<OutT, 2>), grid, dim3(kGemvWgWaves * 64), 0, s, A, W0, W1,
+                       N0, Y, M, N, K);
+  } else {
+    dim3 grid(div_up_h(N, 16), div_up_h(M, 16));
+    hipLaunchKernelGGL((gemv16_bf16_wg<OutT, 1>), grid, dim3(kGemvWgWaves * 64), 0, s, A, W0, W1,
+                       N0, Y, M, N, K);
+  }
   return hipGetLastError();
 }
+template hipError_t launch_gemv16_bf16_wg<float>(const bf16 *, const bf16 *, const bf16 *, int,
+                                                 float *, int, int, int, hipStream_t);
+template hipError_t launch_gemv16_bf16_wg<bf16>(const bf16 *, const bf16 *, const bf16 *, int,
+                                                bf16 *, int, int, int, hipStream_t);
+

@@ -29,10 +29,10 @@ hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_k
 
 hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C,
                                int M, int N, int K, hipStream_t s);
-// K1d: P[ksplit][M][N] (fp32 partials) = A[M,K] * W[N,K]^T per K split; K % (32 ksplit) == 0.
-int gemv_ksplit(int N, int K);
-hipError_t launch_gemv16_bf16(const bf16 *A, const bf16 *W0, const bf16 *W1, int N0, float *P,
-                              int M, int N, int K, int ksplit, hipStream_t s);
+// K1d, whole K per workgroup: Y[M,N] (fp32 or bf16) = A[M,K] * W[N,K]^T; K % 32 == 0.
+template <typename OutT>
+hipError_t launch_gemv16_bf16_wg(const bf16 *A, const bf16 *W0, const bf16 *W1, int N0, OutT *Y,
+                                 int M, int N, int K, hipStream_t s);
 
 // Arguments shared by the norm/RoPE kernels.
 struct NormRopeArgs {
@@ -76,16 +76,20 @@ hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
                                   hipStream_t s);
 
 // K4 + K4c (decode attention): split-KV partials then combine into o [B, H*d_h].
+// The partial kernel reads the raw fp32 projections qkv [B, (H + 2 H_kv) d_h]
+// and applies QK-norm, RoPE and alpha itself; it also writes the step's
+// rotated key and its value into cache slot pos[b].
 struct DecodeArgs {
   int B, H, Hk, d_h, S;
   int local, window;
   int chunk, n_chunks;
+  float theta, scale, alpha;
 };
 int decode_chunk(int local, int window, int S, int d_h);
 template <typename T>
-hipError_t launch_decode_attn(const float *q, const T *k_cache, const T *v_cache,
-                              const int32_t *pos, float *part, T *o, const DecodeArgs &a,
-                              hipStream_t s);
+hipError_t launch_decode_attn(const float *qkv, const T *gamma_q, const T *gamma_k, T *k_cache,
+                              T *v_cache, const int32_t *pos, float *part, T *o,
+                              const DecodeArgs &a, hipStream_t s);
 
 // Sum of fp32 split partials [ksplit][M][N] into y [M][N].
 // Copy the valid tokens' rotated keys (k [B,Hk,T_pad,d_h]) and values

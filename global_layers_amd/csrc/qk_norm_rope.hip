@@ -17,13 +17,6 @@ namespace {
 
 constexpr int kMaxHalf = 128;  // d_h <= 256
 
-DEVI void rope_sincos(int p, double inv_scale, double inv_freq, float &c, float &s) {
-  const double two_pi = 6.283185307179586476925286766559;
-  double a = (double)p * inv_scale * inv_freq;
-  a -= rint(a * (1.0 / two_pi)) * two_pi;
-  sincosf((float)a, &s, &c);
-}
-
 // 16-element slices of a head vector: 8 channels of the first half and the
 // 8 channels they pair with in the second half (two 16-byte vectors for bf16).
 template <typename T> struct Pair8;

@@ -32,9 +32,11 @@ extern "C" {
 #define GEMMA3_STAGE_FORCE_EXACT_MAX 0x10u
 
 /* Decode stages ("Gemma 3 Attention Block", How it works, Cache). */
-#define GEMMA3_DSTAGE_QKV_PROJ 0x1u /* split-K projections of the B new tokens               */
-#define GEMMA3_DSTAGE_QK_NORM 0x2u  /* norm, RoPE, alpha; write k, v into cache slot pos_b    */
-#define GEMMA3_DSTAGE_ATTN 0x4u     /* split-KV partial softmax over cache chunks + combine   */
+#define GEMMA3_DSTAGE_QKV_PROJ 0x1u /* raw fp32 projections of the B new tokens              */
+#define GEMMA3_DSTAGE_QK_NORM 0x2u  /* alone (without ATTN): norm, RoPE, alpha -> q in the
+                                       workspace; k, v into cache slot pos_b                  */
+#define GEMMA3_DSTAGE_ATTN 0x4u     /* norm, RoPE, alpha and the cache write inside the
+                                       split-KV partial softmax kernel, then the combine     */
 #define GEMMA3_DSTAGE_OUT_PROJ 0x8u /* y = o W_o^T                                            */
 #define GEMMA3_DSTAGE_ALL 0xFu
 
@@ -54,11 +56,12 @@ extern "C" {
  *                                 (only when the grid is too small to fill the GPU)
  *   T_pad = T rounded up to a multiple of 64.
  * Decode (S > 0):
- *   qkv  fp32 [ksplit_qkv, B, (H + 2 H_kv) d_h]  split-K partial projections
- *   q    fp32 [B, H, d_h]         normalised, rotated, times alpha
+ *   qkv  fp32 [ksplit_qkv, B, (H + 2 H_kv) d_h]  projections (ksplit_qkv is 1)
+ *   q    fp32 [B, H, d_h]         normalised, rotated, times alpha (written by the
+ *                                 QK_NORM stage when it runs without ATTN)
  *   part fp32 [B, H, n_chunks, d_h + 2]  per-chunk (acc[d_h], m, l), m in log2 units
  *   o    [B, H d_h]               attention output
- *   ypart fp32 [ksplit_out, B, D] split-K partial output projection
+ *   ypart fp32 [ksplit_out, B, D] output projection before rounding (fp32 path only)
  */
 typedef struct {
   size_t total_bytes;

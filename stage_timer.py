@@ -1,7 +1,7 @@
 """Per-stage timing of the prefill path on the seeded synthetic workloads.
 
     python stage_timer.py --workload 4 [--reps 10] [--warmup 3] [--cache] [--block]
-    python stage_timer.py --workload 5 --block   (decode: whole-block steps)
+    python stage_timer.py --workload 5 [--block]   (decode stages, or whole-block steps)
 
 Every layer of the workload goes through the C ABI one stage at a time
 (gemma3_attn_prefill_stages): the projection with its QK-norm / RoPE
@@ -179,6 +179,48 @@ def time_block_decode(w, layer_id: int, reps: int, warmup: int):
     return e0.elapsed_time(e1) * 1e3 / reps, kv + weights
 
 
+def time_decode(w, layer_id: int, reps: int, warmup: int) -> dict:
+    """The attention decode step of the decode workload stage by stage (the
+    projection, split-KV attention with QK-norm/RoPE/cache write, the output
+    projection), each stage alone after a 1 GiB read that leaves the 256 MB
+    Infinity Cache holding nothing of the step's data; median event time."""
+    layer = w.layers[layer_id]
+    lengths = I.decode_lengths(w)
+    inp = I.decode_inputs(w, layer_id, lengths)
+    kc, vc = I.decode_cache(w, layer_id, lengths, device="cuda", poison=True)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    weights = {k: d[k] for k in ("w_q", "w_kv", "w_o", "gamma_q", "gamma_k")}
+    kw = dict(H=w.H, H_kv=w.H_kv, d_h=w.d_h, attn_type=layer.attn_type, window=w.window,
+              rope_theta=layer.rope_theta, rope_scale=layer.rope_scale,
+              query_scale=w.query_scale)
+    desc = lib.make_desc(B=w.B, T=1, D=w.D, dtype=d["x"].dtype, **kw)
+    ws = lib.new_workspace(desc, w.cache_len)
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device="cuda")
+    out = {}
+    for name, st in (("qkv", lib.DSTAGE_QKV_PROJ), ("attention", lib.DSTAGE_ATTN),
+                     ("out", lib.DSTAGE_OUT_PROJ), ("step", lib.DSTAGE_ALL)):
+        run = lambda: lib.decode(d["x"], d["segment_pos"], weights, kc, vc,  # noqa: E731
+                                 workspace=ws, stages=st if name != "step" else lib.DSTAGE_ALL,
+                                 **kw)
+        if name == "qkv":
+            run_all = lambda: lib.decode(d["x"], d["segment_pos"], weights, kc, vc,  # noqa: E731
+                                         workspace=ws, **kw)
+            for _ in range(warmup):
+                run_all()
+        ts = []
+        for _ in range(reps):
+            flush.max()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        out[name] = float(np.median(ts))
+    return out
+
+
 def main() -> None:
     p = argparse.ArgumentParser()
     p.add_argument("--workload", default="4", help="workload ids, comma separated (2, 3, 4)")
@@ -186,14 +228,26 @@ def main() -> None:
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--cache", action="store_true", help="also time the cache-filling prefill")
     p.add_argument("--block", action="store_true", help="also time the whole Gemma 3 block")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run a plain 512 MiB device copy first (scales the HBM byte counters)")
     args = p.parse_args()
     if not torch.cuda.is_available():
         sys.exit("stage_timer needs a GPU")
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for wid in (int(x) for x in args.workload.split(",")):
         w = W.WORKLOADS[wid]
+        if w.T == 1 and not args.block:
+            for li, layer in enumerate(w.layers):
+                t = time_decode(w, li, args.reps, args.warmup)
+                print(f"workload {wid} layer {li} {layer.attn_type:13s} decode " +
+                      " | ".join(f"{k} {v:8.1f} us" for k, v in t.items()), flush=True)
+            continue
         if w.T == 1:
-            if not args.block:
-                sys.exit(f"workload {wid} is a decode workload (time it with --block)")
             for li, layer in enumerate(w.layers):
                 us, nbytes = time_block_decode(w, li, args.reps, args.warmup)
                 print(f"workload {wid} layer {li} {layer.attn_type:13s} block decode step "
