@@ -80,17 +80,16 @@ def test_decode_small(gpu_lib, case):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("layer_id", [0, 1], ids=["global", "local"])
-def test_cfg5_full_size_sampled_rows(gpu_lib, layer_id):
+def test_cfg5_full_size_every_row(gpu_lib, layer_id):
     w = W.WORKLOADS[5]
     lengths = I.decode_lengths(w)
     log(f"cfg5 layer {layer_id} lengths {lengths.tolist()}")
     inp, kw, y, kc, vc, kc0, vc0 = _run(gpu_lib, w, layer_id, lengths)
     pos = lengths - 1
-    rows = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 3, 11})
     for b in range(w.B):  # every row's written slot and its neighbours
         p = int(pos[b])
         assert torch.isnan(kc[b, p + 1:p + 3].float()).all() or p + 1 >= w.cache_len
-    for b in rows:
+    for b in range(w.B):  # every row against the oracle
         log(f"  row {b} length {lengths[b]}")
         yr, k_new, v_new = _oracle_row(inp, kw, kc0, vc0, b)
         assert_bf16_close(f64(y[b:b + 1]), yr, f"row {b} y")
