@@ -40,9 +40,17 @@ def common_flags():
             "-Wno-unused-result"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer instrumentation
+# (device code is built as usual); the sanitizer runtime is not linked in, the
+# process that loads such a library preloads it (see tests/test_abi_sanitized.py).
+SANITIZE_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                  "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, build_dir: str = BUILD, sanitize: bool = False) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    flags = common_flags() + (SANITIZE_FLAGS if sanitize else [])
+    cmd = [hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,19 +62,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, out_dir: str = None, sanitize: bool = False) -> str:
+    """Compile every source and link the library (into the package, or into
+    out_dir with its objects, e.g. for the host-sanitizer build)."""
+    build_dir = BUILD if out_dir is None else os.path.join(out_dir, "_build")
+    lib_path = LIB if out_dir is None else os.path.join(out_dir, os.path.basename(LIB))
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, sanitize), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":
