@@ -63,12 +63,12 @@ AttnArgs attn_args(const gemma3_attn_desc *d, int T_pad, int q0 = 0) {
                   d->attn_type == GEMMA3_ATTN_LOCAL_SLIDING ? 1 : 0, d->window, q0};
 }
 
-// Workspace of a prefill chunk after `start` cached tokens: the prefill's
-// (projections, Q, the chunk's own K / V^T) followed by the attention's key
-// buffers over all start + T keys and their split-KV partials.
+// Workspace of a prefill chunk: the prefill's (projections, Q, the chunk's
+// own K / V^T) followed by room for the attention's split-KV partials (the
+// attention reads every key straight from the caches, so nothing here
+// depends on how many tokens the caches already hold).
 struct ChunkLayout {
-  size_t kc, vtc, part, total;
-  int T_kpad;
+  size_t part, total;
 };
 
 int layout(const gemma3_attn_desc *d, int32_t S, gemma3_ws_layout *L) {
@@ -125,15 +125,9 @@ int chunk_layout(const gemma3_attn_desc *d, int32_t start, gemma3_ws_layout *L, 
   int st = layout(d, 0, L);
   if (st != GEMMA3_OK) return st;
   if (start < 0 || (long)start + d->T > INT32_MAX - kTokPad) return GEMMA3_ERR_SHAPE;
-  const size_t esz = elem_size(d->dtype);
-  C->T_kpad = div_up_h(start + d->T, kTokPad) * kTokPad;
   size_t off = L->total_bytes;
-  C->kc = off;
-  off = align_up(off + (size_t)d->B * d->H_kv * C->T_kpad * d->d_h * esz);
-  C->vtc = off;
-  off = align_up(off + (size_t)d->B * d->H_kv * d->d_h * C->T_kpad * esz);
   C->part = off;
-  if (d->dtype == GEMMA3_BF16) off = align_up(off + flash_attn_partial_bytes(attn_args(d, C->T_kpad, start)));
+  if (d->dtype == GEMMA3_BF16) off = align_up(off + flash_attn_partial_bytes_bound(attn_args(d, L->T_pad)));
   C->total = off;
   return GEMMA3_OK;
 }
@@ -519,25 +513,24 @@ int gemma3_attn_prefill_chunk(const gemma3_attn_desc *desc, const void *x,
   if (!aligned16(workspace)) return GEMMA3_ERR_ALIGN;
   hipStream_t s = (hipStream_t)hip_stream;
   char *base = (char *)workspace;
-  const AttnArgs a = attn_args(desc, C.T_kpad, start);
+  // the attention reads every key, the cached ones and the chunk's own, from the caches
+  AttnArgs a = attn_args(desc, L.T_pad, start);
+  a.S_cache = S;
   // projections with QK-norm / RoPE (Q, and the chunk's K / V^T) ...
   if (desc->dtype == GEMMA3_BF16) {
     st = prefill_impl<bf16>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
                             GEMMA3_STAGE_QKV_PROJ | GEMMA3_STAGE_QK_NORM);
     if (st != GEMMA3_OK) return st;
-    // ... the chunk's keys and values into their slots, all start + T slots
-    // into the attention layouts, attention, output projection
+    // ... the chunk's keys and values into their slots, attention over the
+    // caches, output projection
     RUN(launch_prefill_cache_write<bf16>((const bf16 *)(base + L.k), (const bf16 *)(base + L.vt),
                                          segment_pos, kv_valid_len, (bf16 *)k_cache,
                                          (bf16 *)v_cache, desc->B, desc->T, L.T_pad,
                                          desc->H_kv, desc->d_h, S, s));
-    RUN(launch_cache_gather_keys<bf16>((const bf16 *)k_cache, (const bf16 *)v_cache, kv_valid_len,
-                                       (bf16 *)(base + C.kc), (bf16 *)(base + C.vtc), desc->B,
-                                       start, desc->T, C.T_kpad, desc->H_kv, desc->d_h, S, s));
-    RUN(launch_flash_attn_bf16((const bf16 *)(base + L.q), (const bf16 *)(base + C.kc),
-                               (const bf16 *)(base + C.vtc), kv_valid_len,
-                               (const bf16 *)w->gamma_k, (bf16 *)(base + L.o),
-                               C.part < C.total ? base + C.part : nullptr, a, false, s));
+    RUN(launch_flash_attn_bf16((const bf16 *)(base + L.q), (const bf16 *)k_cache,
+                               (const bf16 *)v_cache, kv_valid_len, (const bf16 *)w->gamma_k,
+                               (bf16 *)(base + L.o), C.part < C.total ? base + C.part : nullptr,
+                               a, false, s));
     return prefill_impl<bf16>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
                               GEMMA3_STAGE_OUT_PROJ);
   }
@@ -548,12 +541,8 @@ int gemma3_attn_prefill_chunk(const gemma3_attn_desc *desc, const void *x,
                                         segment_pos, kv_valid_len, (float *)k_cache,
                                         (float *)v_cache, desc->B, desc->T, L.T_pad, desc->H_kv,
                                         desc->d_h, S, s));
-  RUN(launch_cache_gather_keys<float>((const float *)k_cache, (const float *)v_cache,
-                                      kv_valid_len, (float *)(base + C.kc),
-                                      (float *)(base + C.vtc), desc->B, start, desc->T, C.T_kpad,
-                                      desc->H_kv, desc->d_h, S, s));
-  RUN(launch_attn_f32((const float *)(base + L.q), (const float *)(base + C.kc),
-                      (const float *)(base + C.vtc), kv_valid_len, (float *)(base + L.o), a, s));
+  RUN(launch_attn_f32((const float *)(base + L.q), (const float *)k_cache,
+                      (const float *)v_cache, kv_valid_len, (float *)(base + L.o), a, s));
   return prefill_impl<float>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
                              GEMMA3_STAGE_OUT_PROJ);
 }

@@ -60,75 +60,7 @@ prefill_cache_write(const T *__restrict__ k, const T *__restrict__ vt,
   }
 }
 
-// The reverse move for a prefill chunk: slots 0 .. T_kpad - 1 of the cache
-// into the attention kernel's layouts k [B, H_kv, T_kpad, d_h] and
-// vt [B, H_kv, d_h, T_kpad]; slots at or past the valid keys
-// (q0 + kv_len[b]) become zeros, so that every key and value the attention
-// reads is finite (a masked key still meets a zero weight in the PV sum).
-template <typename T>
-__global__ void __launch_bounds__(kCacheThreads)
-cache_gather_keys(const T *__restrict__ k_cache, const T *__restrict__ v_cache,
-                  const int32_t *__restrict__ kv_len, T *__restrict__ k, T *__restrict__ vt,
-                  int q0, int T_len, int T_kpad, int Hk, int d_h, int S, int cw) {
-  constexpr int E = 16 / sizeof(T);
-  constexpr int kTT = tile_tokens<T>();
-  struct alignas(16) Piece { T e[E]; };
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  T *tile = reinterpret_cast<T *>(smem);  // [kTT][cw + E]
-  const int pitch = cw + E;
-  const int n_cb = d_h / cw;
-  const int s0 = blockIdx.x * kTT, kh = blockIdx.y / n_cb, c0 = (blockIdx.y % n_cb) * cw;
-  const int b = blockIdx.z;
-  const int n_valid = q0 + (kv_len ? min(kv_len[b], T_len) : T_len);
-  const int pc = cw / E;
-
-  T *kdst = k + (((size_t)b * Hk + kh) * T_kpad + s0) * d_h + c0;
-  for (int item = threadIdx.x; item < kTT * pc; item += kCacheThreads) {
-    const int tt = item / pc, j = item % pc;
-    const int s = s0 + tt;
-    u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
-    if (s < n_valid) {
-      const size_t src = (((size_t)b * S + s) * Hk + kh) * d_h + c0 + E * j;
-      kv = ld16(k_cache + src);
-      vv = ld16(v_cache + src);
-    }
-    st16(kdst + (size_t)tt * d_h + E * j, kv);
-    st16(tile + tt * pitch + E * j, vv);
-  }
-  __syncthreads();
-  T *vdst = vt + (((size_t)b * Hk + kh) * d_h + c0) * T_kpad + s0;
-  for (int item = threadIdx.x; item < cw * (kTT / E); item += kCacheThreads) {
-    const int c = item / (kTT / E), j = item % (kTT / E);
-    Piece p;
-#pragma unroll
-    for (int i = 0; i < E; ++i) p.e[i] = tile[(E * j + i) * pitch + c];
-    st16(vdst + (size_t)c * T_kpad + E * j, __builtin_bit_cast(u32x4, p));
-  }
-}
-
 }  // namespace
-
-template <typename T>
-hipError_t launch_cache_gather_keys(const T *k_cache, const T *v_cache, const int32_t *kv_len,
-                                    T *k, T *vt, int B, int q0, int T_len, int T_kpad, int Hk,
-                                    int d_h, int S, hipStream_t s) {
-  constexpr int E = 16 / sizeof(T);
-  constexpr int kTT = tile_tokens<T>();
-  const int cw = d_h < 64 ? d_h : 64;
-  if (d_h % E != 0 || d_h % cw != 0 || T_kpad % kTT != 0) return hipErrorInvalidValue;
-  const size_t lds = (size_t)kTT * (cw + E) * sizeof(T);
-  dim3 grid((unsigned)(T_kpad / kTT), (unsigned)(Hk * (d_h / cw)), (unsigned)B);
-  hipLaunchKernelGGL(cache_gather_keys<T>, grid, dim3(kCacheThreads), lds, s, k_cache, v_cache,
-                     kv_len, k, vt, q0, T_len, T_kpad, Hk, d_h, S, cw);
-  return hipGetLastError();
-}
-
-template hipError_t launch_cache_gather_keys<bf16>(const bf16 *, const bf16 *, const int32_t *,
-                                                   bf16 *, bf16 *, int, int, int, int, int, int,
-                                                   int, hipStream_t);
-template hipError_t launch_cache_gather_keys<float>(const float *, const float *,
-                                                    const int32_t *, float *, float *, int, int,
-                                                    int, int, int, int, int, hipStream_t);
 
 template <typename T>
 hipError_t launch_prefill_cache_write(const T *k, const T *vt, const int32_t *pos,

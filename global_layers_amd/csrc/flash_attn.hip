@@ -68,6 +68,12 @@ template <int D> struct AttnCfg {
 //    XOR with (r >> 1) & 7.
 template <int D> DEVI int swz_k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
 DEVI int swz_v(int r) { return (r >> 1) & 7; }
+// Key-major V tiles (cache mode): a transposing read touches, per 32 lanes,
+// 4 consecutive key rows x 64 bytes; XOR chunk bits 2-3 with r mod 4 (d_h
+// >= 128: rows of 256 B and more start in the same bank) or chunk bit 2 with
+// bit 1 of r (d_h = 64: 128-byte rows, odd rows already in the other half)
+// so the 4 rows take distinct banks.
+template <int D> DEVI int swz_vc(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0) and lgkmcnt(0), expcnt free.
 constexpr int kWaitVmLgkm0 = 0x7 << 4;
@@ -158,7 +164,14 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
 // on sliding-window layers the twice longer query tile also halves the
 // per-row share of each workgroup's prologue (measured 1-3% faster on the
 // 27B-shaped local layer).
-template <int D, int RB>
+// kCache: keys and values come straight from the caches ([B, S_cache, H_kv,
+// d_h] each, V key-major, as a chunk of a longer prefill finds them). K rows
+// land in LDS as in the workspace layout; a V tile lands key-major and the
+// PV operand (8 consecutive keys of one channel per lane) is read with the
+// transposing LDS read of gfx950 (two 4-key halves). Rows at or past the
+// valid length are loaded as copies of the last valid row, so whatever the
+// slots beyond it hold (NaN included) never reaches the arithmetic.
+template <int D, int RB, bool kCache>
 __global__ void __launch_bounds__(kThreads)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
@@ -205,8 +218,11 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) l_run[rb] = 0.f;
 
-  const char *kbase = (const char *)(k + ((size_t)b * a.Hk + kh) * a.T_pad * D);
-  const char *vbase = (const char *)(vt + ((size_t)b * a.Hk + kh) * D * a.T_pad);
+  const char *kbase = kCache ? (const char *)(k + ((size_t)b * a.S_cache * a.Hk + kh) * D)
+                             : (const char *)(k + ((size_t)b * a.Hk + kh) * a.T_pad * D);
+  const char *vbase = kCache ? (const char *)(vt + ((size_t)b * a.S_cache * a.Hk + kh) * D)
+                             : (const char *)(vt + ((size_t)b * a.Hk + kh) * D * a.T_pad);
+  const uint32_t cache_pitch = (uint32_t)a.Hk * D * 2;  // bytes between cache slots
 
   const int n_tiles = my_end > my_begin ? div_up(my_end - my_begin, kBN) : 0;
   // Loads past the last tile are clamped to it: such a load only rewrites a
@@ -219,32 +235,64 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // offset. The swizzle pattern of K pieces repeats every 2 pieces (V: every
   // piece), and pieces i and i + 2 (V: i + 1) are a fixed number of rows apart,
   // so two (one) lane offsets plus a uniform step cover every piece.
+  // With kCache a lane keeps its row within the piece and its chunk offset
+  // instead; each load clamps the row to the last valid key and addresses it
+  // from the tile's first row (wave-uniform base, 32-bit lane offset). A V
+  // tile is then key-major: piece i holds keys 4 i (1024 / (2 d_h)) + ..., row
+  // r with chunk position p holding logical chunk p ^ swz_vc(r); the swizzle
+  // depends on r mod 4 only, which is the same for every piece of a lane.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   uint32_t k_lane[2];
+  int k_row[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int byte = (w + 4 * i) * 1024 + 16 * lane;
     const int r = byte / Cfg::kKRowBytes, pch = (byte % Cfg::kKRowBytes) / 16;
-    k_lane[i] = (uint32_t)(r * Cfg::kKRowBytes + 16 * (pch ^ swz_k<D>(r)));
+    k_lane[i] = (uint32_t)((kCache ? 0 : r * Cfg::kKRowBytes) + 16 * (pch ^ swz_k<D>(r)));
+    k_row[i] = r;
   }
   uint32_t v_lane;
+  int v_row;
   {
     const int byte = w * 1024 + 16 * lane;
-    const int r = byte / Cfg::kVRowBytes, pch = (byte % Cfg::kVRowBytes) / 16;
-    v_lane = (uint32_t)(r * a.T_pad * 2 + 16 * (pch ^ swz_v(r)));
+    if constexpr (kCache) {
+      const int r = byte / (2 * D), pch = (byte % (2 * D)) / 16;
+      v_lane = (uint32_t)(16 * (pch ^ swz_vc<D>(r)));
+      v_row = r;
+    } else {
+      const int r = byte / Cfg::kVRowBytes, pch = (byte % Cfg::kVRowBytes) / 16;
+      v_lane = (uint32_t)(r * a.T_pad * 2 + 16 * (pch ^ swz_v(r)));
+      v_row = 0;
+    }
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+  // cache slot of key row s0 + r, clamped to the last valid key, as an offset from row s0
+  auto clamped = [&](int s0, int r) { return (uint32_t)(min(s0 + r, len - 1) - s0) * cache_pitch; };
   // K rows 32 kbh .. 32 kbh + 31 of tile t into half slot `slot`
   auto issue_k_piece = [&](int t, int kbh, int slot, int i) {
-    const char *src =
-        kbase + (size_t)(tile_s0(t) + 32 * kbh) * Cfg::kKRowBytes + (size_t)(i >> 1) * 8192;
-    load_lds16(src, k_lane[i & 1], lds0 + slot * Cfg::kKHalfBytes + (wu + 4 * i) * 1024);
+    const uint32_t dst = lds0 + slot * Cfg::kKHalfBytes + (wu + 4 * i) * 1024;
+    if constexpr (kCache) {
+      const int s0 = tile_s0(t);
+      const int r = 32 * kbh + k_row[i & 1] + (i >> 1) * (8192 / Cfg::kKRowBytes);
+      load_lds16(kbase + (size_t)s0 * cache_pitch, clamped(s0, r) + k_lane[i & 1], dst);
+    } else {
+      const char *src =
+          kbase + (size_t)(tile_s0(t) + 32 * kbh) * Cfg::kKRowBytes + (size_t)(i >> 1) * 8192;
+      load_lds16(src, k_lane[i & 1], dst);
+    }
   };
-  // V^T columns of tile t into V buffer `buf` (piece i: channel rows 32 i + ...)
+  // V^T columns of tile t into V buffer `buf` (piece i: channel rows 32 i + ...),
+  // or with kCache its key rows (piece i: rows 4 i (1024 / (2 d_h)) + ...)
   auto issue_v_piece = [&](int t, int buf, int i) {
-    const char *src = vbase + (size_t)tile_s0(t) * 2 + (size_t)i * 32 * a.T_pad * 2;
-    load_lds16(src, v_lane,
-               lds0 + 4 * Cfg::kKHalfBytes + buf * Cfg::kVTileBytes + (wu + 4 * i) * 1024);
+    const uint32_t dst = lds0 + 4 * Cfg::kKHalfBytes + buf * Cfg::kVTileBytes + (wu + 4 * i) * 1024;
+    if constexpr (kCache) {
+      const int s0 = tile_s0(t);
+      load_lds16(vbase + (size_t)s0 * cache_pitch,
+                 clamped(s0, v_row + i * (4096 / (2 * D))) + v_lane, dst);
+    } else {
+      const char *src = vbase + (size_t)tile_s0(t) * 2 + (size_t)i * 32 * a.T_pad * 2;
+      load_lds16(src, v_lane, dst);
+    }
   };
 
   auto issue_prologue = [&]() {  // K halves 0, 1, 2 (slots 0-2) and V tile 0
@@ -298,9 +346,37 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     return *reinterpret_cast<const bf16x8 *>(lds + slot * Cfg::kKHalfBytes + koff[ks % kKBases] +
                                              (ks / kKBases) * 32 * kKBases);
   };
+  // kCache: the PV operand from a key-major V tile by two transposing reads.
+  // Within each 16 lanes, element e of lane i of such a read is element i & 3
+  // at the address of lane 4 e + (i >> 2). So lane 16 G + 4 e + u points at
+  // channels 32 db + 16 (G & 1) + 4 u .. + 3 of key 16 kk + 8 (G >> 1) + 4 r + e
+  // (r: which 4-key half), and lane 16 G + i receives keys 16 kk + 8 hh + 4 r +
+  // 0..3 of channel 32 db + (lane & 31). The key row's swizzle XORs the 8-byte
+  // unit index with 8 (e or e >> 1), which permutes 64-byte blocks of the row:
+  // per-lane bases for db mod 4, the rest immediates.
+  constexpr int kTB = Cfg::kDB < 4 ? Cfg::kDB : 4;
+  int vtr[kTB];
+  {
+    const int G = lane >> 4, e = (lane >> 2) & 3, u = lane & 3;
+    const int f = D >= 128 ? e : ((e >> 1) & 1);
+#pragma unroll
+    for (int dl = 0; dl < kTB; ++dl)
+      vtr[dl] = 4 * Cfg::kKHalfBytes + (8 * hh + e) * (2 * D) + 8 * (8 * (dl ^ f) + 4 * (G & 1) + u);
+  }
   auto vfrag = [&](int buf, int db, int kk) {
-    return *reinterpret_cast<const bf16x8 *>(lds + buf * Cfg::kVTileBytes +
-                                             db * 32 * Cfg::kVRowBytes + voff[kk]);
+    if constexpr (kCache) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      char *p = lds + buf * Cfg::kVTileBytes + vtr[db % kTB] + (db / kTB) * 256 + 16 * kk * (2 * D);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)p);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(p + 4 * (2 * D)));
+      return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return *reinterpret_cast<const bf16x8 *>(lds + buf * Cfg::kVTileBytes +
+                                               db * 32 * Cfg::kVRowBytes + voff[kk]);
+    }
   };
 
   // Fixed softmax reference. The queries arrive scaled by log2(e), so a
@@ -465,8 +541,11 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
       }
       if constexpr (gi + 1 < 2 * kNGT) read_frags(std::integral_constant<int, gi + 1>{}, frn);
+      // LDS read instructions of the next group (a cache-mode V fragment takes two)
+      constexpr bool kNextS = (gi + 1) % kNGT < kNG;
       constexpr int n_reads = (gi + 1 < 2 * kNGT)
-                                  ? (((gi + 1) % kNGT < kNG && (gi + 1) / kNGT == 1 && !kNext) ? 0 : 4)
+                                  ? ((kNextS && (gi + 1) / kNGT == 1 && !kNext) ? 0
+                                                                             : (kNextS || !kCache ? 4 : 8))
                                   : 0;
       if constexpr (kSActive) {
 #pragma unroll
@@ -806,12 +885,12 @@ Plan plan(const AttnArgs &a) {
   return p;
 }
 
-template <int D, int RB>
+template <int D, int RB, bool kCache>
 hipError_t launch_rb(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
                      const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml,
                      const AttnArgs &a, const Plan &p, int force, hipStream_t s) {
   using Cfg = AttnCfg<D>;
-  auto kern = flash_attn_fwd_bf16<D, RB>;
+  auto kern = flash_attn_fwd_bf16<D, RB, kCache>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
@@ -833,11 +912,18 @@ hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t 
                     const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
                     int force, hipStream_t s) {
   const Plan p = plan(a);
+  if (a.S_cache > 0) {
+    if constexpr (D == 128) {
+      if (p.rb == 2)
+        return launch_rb<D, 2, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+    }
+    return launch_rb<D, 1, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+  }
   if constexpr (D == 128) {
     if (p.rb == 2)
-      return launch_rb<D, 2>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+      return launch_rb<D, 2, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
   }
-  return launch_rb<D, 1>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+  return launch_rb<D, 1, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
 }
 
 }  // namespace
@@ -846,6 +932,14 @@ size_t flash_attn_partial_bytes(const AttnArgs &a) {
   const Plan p = plan(a);
   if (p.n_split == 1) return 0;
   return (size_t)p.n_split * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8);
+}
+
+size_t flash_attn_partial_bytes_bound(const AttnArgs &a) {
+  // key ranges are split (into at most 8 chunks) only when the query tiles
+  // alone leave CUs idle, and that count does not depend on q0
+  const Plan p = plan(a);
+  if (p.n_base >= kCUs) return 0;
+  return (size_t)8 * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8);
 }
 
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,

@@ -55,7 +55,9 @@ gemm_f32_nt(const float *__restrict__ A, const float *__restrict__ B0,
 
 // One wave per (b, h, query row t). Keys are visited 64 at a time (one per
 // lane); the softmax state is wave-uniform; o is accumulated d_h/64 channels
-// per lane. q [B,H,T,d_h], k [B,Hk,T_pad,d_h], vt [B,Hk,d_h,T_pad].
+// per lane. q [B,H,T,d_h]; k [B,Hk,T_pad,d_h] and vt [B,Hk,d_h,T_pad], or
+// with a.S_cache > 0 the caches [B,S_cache,Hk,d_h] themselves. Only allowed
+// keys are read.
 constexpr int kMaxD = 256;
 
 __global__ void __launch_bounds__(64)
@@ -71,15 +73,21 @@ attn_f32(const float *__restrict__ q, const float *__restrict__ k, const float *
   const int ta = a.q0 + t;  // absolute index of the query
   const int lo = a.local ? max(0, ta - a.window + 1) : 0;
   const int hi = min(ta, len - 1);  // inclusive
-  const float *kb = k + ((size_t)b * a.Hk + kh) * a.T_pad * D;
-  const float *vb = vt + ((size_t)b * a.Hk + kh) * D * a.T_pad;
+  const bool cache = a.S_cache > 0;
+  const float *kb = cache ? k + ((size_t)b * a.S_cache * a.Hk + kh) * D
+                          : k + ((size_t)b * a.Hk + kh) * a.T_pad * D;
+  const float *vb = cache ? vt + ((size_t)b * a.S_cache * a.Hk + kh) * D
+                          : vt + ((size_t)b * a.Hk + kh) * D * a.T_pad;
+  // element strides: key row of K; key and channel of V
+  const size_t ks = cache ? (size_t)a.Hk * D : (size_t)D;
+  const size_t vs = cache ? (size_t)a.Hk * D : 1, vc = cache ? 1 : (size_t)a.T_pad;
   float m = -INFINITY, l = 0.f, acc[kMaxD / 64] = {};
   for (int s0 = lo; s0 <= hi; s0 += 64) {
     const int s = s0 + lane;
     float x = -INFINITY;
     if (s <= hi) {
       float d = 0.f;
-      for (int c = 0; c < D; ++c) d = fmaf(qs[c], kb[(size_t)s * D + c], d);
+      for (int c = 0; c < D; ++c) d = fmaf(qs[c], kb[(size_t)s * ks + c], d);
       x = d;
     }
     const float mn = fmaxf(m, wave_max(x));  // finite: key s0 is allowed
@@ -95,7 +103,7 @@ attn_f32(const float *__restrict__ q, const float *__restrict__ k, const float *
 #pragma unroll
       for (int i = 0; i < kMaxD / 64; ++i) {
         const int c = lane + 64 * i;
-        if (c < D) acc[i] = fmaf(pj, vb[(size_t)c * a.T_pad + s0 + j], acc[i]);
+        if (c < D) acc[i] = fmaf(pj, vb[(size_t)(s0 + j) * vs + c * vc], acc[i]);
       }
     }
   }

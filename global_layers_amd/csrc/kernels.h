@@ -56,17 +56,25 @@ hipError_t launch_qk_norm_rope_decode(const float *part, int ksplit, const int32
 
 // K3 (prefill attention, bf16).
 // Queries are the T rows of q; their absolute index (the one the causal and
-// sliding masks use) is q0 + row. Keys have absolute indices 0 .. T_pad - 1
-// in k / vt; key s is valid below q0 + kv_len[b] (q0 + T without kv_len).
-// A plain prefill has q0 = 0; a chunk after q0 cached tokens has q0 > 0.
+// sliding masks use) is q0 + row. Key s is valid below q0 + kv_len[b]
+// (q0 + T without kv_len). A plain prefill has q0 = 0; a chunk after q0
+// cached tokens has q0 > 0. Key layouts:
+//  * S_cache == 0: k [B, H_kv, T_pad, d_h] and vt [B, H_kv, d_h, T_pad]
+//    (the prefill workspace; keys 0 .. T_pad - 1, rows past the valid ones zero);
+//  * S_cache > 0: k and vt are the caches themselves, [B, S_cache, H_kv, d_h]
+//    each (V key-major as stored); only the valid slots are read, any others
+//    may hold anything (NaN included).
 struct AttnArgs {
   int B, T, H, Hk, d_h, T_pad;
   int local, window;
   int q0;
+  int S_cache;
 };
 // `partial` (flash_attn_partial_bytes(a) bytes, may be NULL when that is 0)
-// holds the split-KV partial outputs.
+// holds the split-KV partial outputs. flash_attn_partial_bytes_bound(a) is
+// at least that for every q0 (the split plan depends on q0, the bound not).
 size_t flash_attn_partial_bytes(const AttnArgs &a);
+size_t flash_attn_partial_bytes_bound(const AttnArgs &a);
 // gamma_k [d_h] bounds the key norms (fixed softmax reference).
 // force_exact_max: every workgroup takes the exact-row-maximum pass that
 // normally runs only where the logit bound is too loose.
@@ -100,13 +108,6 @@ hipError_t launch_prefill_cache_write(const T *k, const T *vt, const int32_t *po
                                       const int32_t *kv_len, T *k_cache, T *v_cache, int B,
                                       int T_len, int T_pad, int Hk, int d_h, int S,
                                       hipStream_t s);
-
-// Cache slots 0 .. T_kpad - 1 into the attention layouts k [B,Hk,T_kpad,d_h]
-// and vt [B,Hk,d_h,T_kpad]; slots from q0 + kv_len[b] on become zeros.
-template <typename T>
-hipError_t launch_cache_gather_keys(const T *k_cache, const T *v_cache, const int32_t *kv_len,
-                                    T *k, T *vt, int B, int q0, int T_len, int T_kpad, int Hk,
-                                    int d_h, int S, hipStream_t s);
 
 // Block pieces: out = (res ? res : 0) + RMSNorm(a) (1 + gamma) per row of D
 // (D <= 6144), and z = GELU_tanh(g) * u with gu rows [g | u] of 2 D_ff.

@@ -175,9 +175,11 @@ int gemma3_attn_prefill_cache(const gemma3_attn_desc *desc, const void *x,
  * earlier keys and values (from gemma3_attn_prefill_cache, earlier chunks or
  * decode steps). With start = 0 this is gemma3_attn_prefill_cache.
  * Caches: [B, S, H_kv, d_h] device arrays of the descriptor's dtype,
- * 16-byte aligned, start + T <= S. Workspace:
- * gemma3_attn_prefill_chunk_workspace_bytes(desc, start) bytes (it grows with
- * start: the attention reads its keys from a copy in its own layout).
+ * 16-byte aligned, start + T <= S. The attention reads the keys and values
+ * in the caches where they are (slots at or past start + kv_valid_len[b] are
+ * never used, whatever they hold). Workspace:
+ * gemma3_attn_prefill_chunk_workspace_bytes(desc, start) bytes; the size
+ * does not depend on start (the argument is only validated: < 0 -> 0).
  * Errors: those of gemma3_attn_prefill; start < 0, S < 1 or start + T > S ->
  * GEMMA3_ERR_SHAPE; a NULL cache -> GEMMA3_ERR_NULL; misaligned ->
  * GEMMA3_ERR_ALIGN; a short workspace -> GEMMA3_ERR_WORKSPACE.

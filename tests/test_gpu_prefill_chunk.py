@@ -1,6 +1,8 @@
 """GPU parity of the prefill chunk against a cache (gemma3_attn_prefill_chunk;
 "Gemma 3 Attention Block", How it works: the prefill steps with the Cache
-passage's slot = position).
+passage's slot = position). The chunk's attention reads the caches in place
+(keys row by row, values key-major through transposing LDS reads), and the
+caches start NaN-filled, so a read of a slot past the valid keys would show.
 
 A sequence prefilled as a cached first part (gemma3_attn_prefill_cache) and
 one or more chunks must give the chunk rows of one prefill over the whole
@@ -68,6 +70,9 @@ CASES = [
     (3, 321, 256, 4, 4, 64, "bf16", (1, 64, 200), (121, 1, 77), 321),
     (2, 150, 96, 2, 1, 16, "f32", (70,), (80, 33), 160),
     (1, 128, 256, 4, 1, 64, "f32", (50, 51), None, 128),
+    # the 27B-shaped heads (d_h = 128, two query heads per KV head, two row
+    # blocks per wave), a chunk of 512 after 1024 cached tokens
+    (1, 1536, 5376, 32, 16, 128, "bf16", (1024,), None, 1600),
 ]
 
 
@@ -110,7 +115,7 @@ def test_chunks_equal_one_long_prefill(gpu_lib, case, attn_type, window):
     check(vg[m], vr[m], "v slots")
 
 
-@pytest.mark.parametrize("dtype,d_h", [("bf16", 64), ("bf16", 256), ("f32", 32)])
+@pytest.mark.parametrize("dtype,d_h", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 32)])
 @pytest.mark.parametrize("attn_type,window", [(L, 37), (G, 0)])
 def test_chunk_from_empty_cache_is_cache_filling_prefill(gpu_lib, dtype, d_h, attn_type, window):
     B, T, H, Hk, S = 2, 200, 4, 2, 256
