@@ -7,10 +7,10 @@
 //  * Blocked logits get exactly zero weight, as K_MASK does in fp32 whenever a
 //    row has an allowed key; the fill value itself is never formed. Tiles that
 //    no row of the workgroup may see are never visited.
-//  * One workgroup = 4 waves = 128 query rows (256 when each wave owns two
-//    32-row blocks) of one KV head: the query heads of a GQA group (up to 4)
-//    are packed into the workgroup, so each K/V tile staged in LDS feeds every
-//    query head that reads it.
+//  * One workgroup = 4 waves = 128 query rows of one KV head: the query heads
+//    of a GQA group (up to 4) are packed into the workgroup, so each K/V tile
+//    staged in LDS feeds every query head that reads it. At d_h <= 128 two
+//    workgroups share each CU (registers capped at 256 per lane).
 //  * Each wave computes S^T = K Q^T with 32x32x16 bf16 MFMAs: a lane owns one
 //    query row and 32 of the 64 keys of a tile. K rows are fed in the
 //    permuted order kappa(i) so that the S^T accumulators of a lane are, in
@@ -157,13 +157,14 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
   return g;
 }
 
-// RB: blocks of 32 query rows per wave. Each K / V^T fragment read from LDS
-// feeds RB MFMAs; one wave per SIMD reads LDS at less than one 1 KB fragment
-// per MFMA, so two blocks run closer to the matrix pipe's rate. Used at
-// d_h = 128 (at d_h = 256 two blocks' O and Q do not fit the register file);
-// on sliding-window layers the twice longer query tile also halves the
-// per-row share of each workgroup's prologue (measured 1-3% faster on the
-// 27B-shaped local layer).
+// RB: blocks of 32 query rows per wave; each K / V^T fragment read from LDS
+// feeds RB MFMAs. The planner takes RB = 1. At d_h <= 128 the kernel is
+// built for two waves per SIMD (256 registers per lane), so two workgroups
+// share a CU and each one's barriers and post-barrier fragment waits fall
+// while the other computes; that measured faster than two row blocks per
+// wave at one wave per SIMD (27B-shaped layers: global 7.12 against
+// 7.46 ms, local 0.62 against 0.76 ms). At d_h = 256 one wave per SIMD
+// either way (O alone takes 128 registers per row block).
 // kCache: keys and values come straight from the caches ([B, S_cache, H_kv,
 // d_h] each, V key-major, as a chunk of a longer prefill finds them). K rows
 // land in LDS as in the workspace layout; a V tile lands key-major and the
@@ -172,7 +173,7 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
 // valid length are loaded as copies of the last valid row, so whatever the
 // slots beyond it hold (NaN included) never reaches the arithmetic.
 template <int D, int RB, bool kCache>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, D <= 128 ? 2 : 1)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
                     const bf16 *__restrict__ gamma_k, bf16 *__restrict__ o,
@@ -836,14 +837,18 @@ struct Plan {
 // costs about 2.5 tiles; a split adds the merge launch and its reads, about
 // 8 (measured: splitting the 1B-shaped local layer in two is slower).
 constexpr double kPrologueTiles = 2.5, kMergeTiles = 8.0;
-constexpr int kCUs = 256;  // MI355X compute units; one 131 KB-LDS workgroup each
+constexpr int kCUs = 256;  // MI355X compute units
+// workgroups resident per CU: two at d_h <= 128 (64 KB of LDS and at most
+// 256 registers per lane each), one at d_h = 256 (131 KB, 512 registers)
+constexpr int wgs_per_cu(int d_h) { return d_h <= 128 ? 2 : 1; }
 
 Plan plan(const AttnArgs &a) {
   Plan p;
   const int G = a.H / a.Hk;
   p.gp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   // (a window covering every key takes the global layer's plan and bits)
-  p.rb = a.d_h == 128 ? 2 : 1;
+  p.rb = 1;
+  const int slots = kCUs * wgs_per_cu(a.d_h);  // workgroups running at once
   const int TQ = 32 * p.rb * (4 / p.gp);
   p.n_qtiles = div_up_h(a.T, TQ);
   p.n_hgrp = G / p.gp;
@@ -864,16 +869,16 @@ Plan plan(const AttnArgs &a) {
   for (int qt = 0; qt < p.n_qtiles; ++qt) max_tiles = max(max_tiles, tiles_of(qt));
   // Split key ranges only when the query tiles alone leave CUs idle: pick
   // the chunk count minimising rounds x (chunk + prologue) (+ merge), where
-  // a round is kCUs concurrent workgroups of similar length.
+  // a round is `slots` concurrent workgroups of similar length.
   p.n_split = 1;
-  if (p.n_base < kCUs) {
+  if (p.n_base < slots) {
     double best = max_tiles + kPrologueTiles;
     for (int ns = 2; ns <= 8; ++ns) {  // flash_combine merges at most 8 chunks
       const int c = div_up_h(max_tiles, ns);
       long active = 0;
       for (int qt = 0; qt < p.n_qtiles; ++qt) active += div_up_h(tiles_of(qt), c);
       active *= n_groups;
-      const double cost = div_up_h(active, kCUs) * (c + kPrologueTiles) + kMergeTiles;
+      const double cost = div_up_h(active, slots) * (c + kPrologueTiles) + kMergeTiles;
       if (cost < best) {
         best = cost;
         p.n_split = ns;
@@ -911,18 +916,9 @@ template <int D>
 hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
                     const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
                     int force, hipStream_t s) {
-  const Plan p = plan(a);
-  if (a.S_cache > 0) {
-    if constexpr (D == 128) {
-      if (p.rb == 2)
-        return launch_rb<D, 2, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
-    }
+  const Plan p = plan(a);  // p.rb == 1
+  if (a.S_cache > 0)
     return launch_rb<D, 1, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
-  }
-  if constexpr (D == 128) {
-    if (p.rb == 2)
-      return launch_rb<D, 2, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
-  }
   return launch_rb<D, 1, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
 }
 
@@ -938,7 +934,7 @@ size_t flash_attn_partial_bytes_bound(const AttnArgs &a) {
   // key ranges are split (into at most 8 chunks) only when the query tiles
   // alone leave CUs idle, and that count does not depend on q0
   const Plan p = plan(a);
-  if (p.n_base >= kCUs) return 0;
+  if (p.n_base >= (long)kCUs * wgs_per_cu(a.d_h)) return 0;
   return (size_t)8 * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8);
 }
 
