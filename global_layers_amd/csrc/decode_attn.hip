@@ -329,30 +329,33 @@ decode_attn_partial(const float *__restrict__ qkv, const T *__restrict__ gamma_q
   }
 }
 
-// grid: x = H, y = B; D threads, one channel each. Every thread loads, for a
-// batch of up to kCombineBatch chunks at once, each chunk's (m, l) (the same
-// addresses across the workgroup) and its own channel of each partial, then
-// merges them by log-sum-exp with a running maximum: one round trip per batch
-// and no barrier.
+// grid: x = H, y = B; CG x D threads: channel c of chunk group cg (chunks
+// j with j mod CG = cg). Every thread loads, for a batch of up to
+// kCombineBatch of its chunks at once, each chunk's (m, l) (the same
+// addresses across the group) and its own channel of each partial, then
+// merges them by log-sum-exp with a running maximum: one round trip per batch.
+// With CG > 1 the groups' (M, sum, l) meet in LDS and group 0 merges them
+// the same way (long rows: 128 chunks take two round trips, not eight).
 constexpr int kMaxChunks = 128;  // decode_chunk keeps every row at <= 128 chunks
 constexpr int kCombineBatch = 16;
 
-template <typename T, int D>
-__global__ void __launch_bounds__(D)
+template <typename T, int D, int CG>
+__global__ void __launch_bounds__(D * CG)
 decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos,
                     T *__restrict__ o, DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x % D, cg = threadIdx.x / D;
   int lo, hi;
   row_range(pos, b, a.S, a.local, a.window, lo, hi);
   const int n = hi >= lo ? div_up(hi - lo + 1, a.chunk) : 0;
   const float *pp = part + ((size_t)b * a.H + h) * a.n_chunks * (D + 2);
   float M = -INFINITY, sa = 0.f, sl = 0.f;
-  for (int j = 0; j < n; j += kCombineBatch) {
+  for (int j = cg; j < n; j += CG * kCombineBatch) {
     float mv[kCombineBatch], lv[kCombineBatch], v[kCombineBatch];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
-      const bool ok = j + u < n;
-      const float *pj = pp + (size_t)(ok ? j + u : 0) * (D + 2);
+      const int jj = j + CG * u;
+      const bool ok = jj < n;
+      const float *pj = pp + (size_t)(ok ? jj : 0) * (D + 2);
       const float2 ml = *reinterpret_cast<const float2 *>(pj + D);
       mv[u] = ok ? ml.x : -INFINITY;
       lv[u] = ml.y;
@@ -373,6 +376,30 @@ decode_attn_combine(const float *__restrict__ part, const int32_t *__restrict__ 
     }
     M = mb;
   }
+  if constexpr (CG > 1) {
+    __shared__ float red[3][CG][D];
+    red[0][cg][c] = M;
+    red[1][cg][c] = sa;
+    red[2][cg][c] = sl;
+    __syncthreads();
+    if (cg != 0) return;
+    float mb = M;
+#pragma unroll
+    for (int g = 1; g < CG; ++g) mb = fmaxf(mb, red[0][g][c]);
+    if (mb == -INFINITY) {  // a row without chunks (position outside the cache)
+      sa = 0.f;
+      sl = 0.f;
+    } else {
+      sa = 0.f;
+      sl = 0.f;
+#pragma unroll
+      for (int g = 0; g < CG; ++g) {
+        const float wg = exp2f(red[0][g][c] - mb);  // 0 for a group without chunks
+        sa = fmaf(wg, red[1][g][c], sa);
+        sl = fmaf(wg, red[2][g][c], sl);
+      }
+    }
+  }
   o[((size_t)b * a.H + h) * D + c] = from_f32<T>(sl > 0.f ? sa / sl : 0.f);
 }
 
@@ -386,7 +413,13 @@ hipError_t launch_dec(const float *qkv, const T *gq, const T *gk, T *kc, T *vc,
                      kc, vc, pos, part, a, n_hgrp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_attn_combine<T, D>), dim3(a.H, a.B), dim3(D), 0, s, part, pos, o, a);
+  // rows of many chunks: four chunk groups per (row, head)
+  if (a.n_chunks > 2 * kCombineBatch && D * 4 <= 1024)
+    hipLaunchKernelGGL((decode_attn_combine<T, D, 4>), dim3(a.H, a.B), dim3(D * 4), 0, s, part,
+                       pos, o, a);
+  else
+    hipLaunchKernelGGL((decode_attn_combine<T, D, 1>), dim3(a.H, a.B), dim3(D), 0, s, part, pos,
+                       o, a);
   return hipGetLastError();
 }
 
