@@ -855,10 +855,14 @@ Plan plan(const AttnArgs &a) {
   const long n_groups = (long)a.B * a.Hk * p.n_hgrp;
   p.n_base = n_groups * p.n_qtiles;
   // XCD-contiguous order when whole (b, kh, head group) runs divide evenly
-  // among the 8 XCDs (each L2 then holds the K/V its CUs share); otherwise
-  // the plain order, which deals neighbouring query tiles to different XCDs
-  // and keeps their loads balanced.
-  p.remap = n_groups % 8 == 0;
+  // among the 8 XCDs (each L2 then holds the K/V its CUs share), and on
+  // sliding-window layers (every query tile spans about W keys, so runs of
+  // neighbouring tiles stay balanced and share most of their window in one
+  // L2; measured: the 1B-shaped local layer's time unchanged, its K/V read
+  // by one XCD each instead of all eight); otherwise the plain order, which
+  // deals neighbouring causal query tiles to different XCDs and keeps their
+  // loads balanced.
+  p.remap = n_groups % 8 == 0 || a.local;
   // Key tiles of query tile qt (data-independent: padding is ignored here).
   auto tiles_of = [&](int qt) {
     const int t_lo = qt * TQ, t_hi = min(a.T, t_lo + TQ);
