@@ -155,3 +155,24 @@ def test_chunk_1b_shape_second_half(gpu_lib, layer_id):
     rows = np.sort(np.random.default_rng(7).choice(np.arange(2048, w.T), 96, replace=False))
     ref = oracle_prefill(inp, kw, rows=rows)
     assert_bf16_close(f64(ys[0])[:, rows - 2048], ref, "sampled chunk rows")
+
+
+@pytest.mark.parametrize("d_h", [64, 128, 256])
+@pytest.mark.parametrize("attn_type,window", [(L, 90), (G, 0)])
+def test_chunk_exact_max_pass_reads_cache(gpu_lib, d_h, attn_type, window):
+    # alpha = 1 puts every row's logit bound past the fixed-reference range,
+    # so the chunk's attention takes the exact-row-maximum pass, whose key
+    # loads also come from the caches (NaN past the valid slots). Against the
+    # fp64 oracle such logits are limited by the bf16 storage of q and k, so
+    # the reference is the GPU's own one-long prefill with the same alpha
+    # (same q, k and v bits; the row arithmetic differs only where the key
+    # range of a query tile is split differently): bf16 tolerance.
+    B, N, D, H, Hk, S, cut = 2, 300, 512, 4, 2, 320, 170
+    inp = small_prefill_inputs(46, B, N, D, H, Hk, d_h, "bf16")
+    kw = _kw(H, Hk, d_h, attn_type, window, alpha=1.0)
+    log(f"exact-max chunk d_h={d_h} {attn_type}")
+    ys, _, _ = _chunked(gpu_lib, inp, kw, (cut,), S)
+    d = to_dev(inp)
+    y_full = gpu_lib.prefill(d["x"], d["segment_pos"], weights_of(d), **kw)
+    torch.cuda.synchronize()
+    assert_bf16_close(f64(ys[0]), f64(y_full)[:, cut:], "exact-max chunk y")
