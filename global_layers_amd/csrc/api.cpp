@@ -342,9 +342,15 @@ int block_impl(const gemma3_attn_desc *d, int D_ff, const T *x, const int32_t *p
   RUN(launch_rms_norm_add<T>(x, a, (const T *)w->post_attn_norm, h, M, D, s));
   RUN(launch_rms_norm_add<T>(nullptr, h, (const T *)w->pre_ffw_norm, hn, M, D, s));
   if constexpr (sizeof(T) == 2) {
-    RUN(launch_gemm_bf16_nt(hn, (const bf16 *)w->w_gating, (const bf16 *)w->w_gating, 2 * D_ff,
-                            gu, M, 2 * D_ff, D, s));
-    RUN(launch_geglu<T>(gu, z, M, D_ff, s));
+    // gate|up projection with the activation in its epilogue (D_ff a multiple
+    // of 128), else the projection then the activation pass
+    if (D_ff % 128 == 0) {
+      RUN(launch_gemm_geglu(hn, (const bf16 *)w->w_gating, D_ff, z, M, D, s));
+    } else {
+      RUN(launch_gemm_bf16_nt(hn, (const bf16 *)w->w_gating, (const bf16 *)w->w_gating,
+                              2 * D_ff, gu, M, 2 * D_ff, D, s));
+      RUN(launch_geglu<T>(gu, z, M, D_ff, s));
+    }
     RUN(launch_gemm_bf16_nt(z, (const bf16 *)w->w_linear, (const bf16 *)w->w_linear, D, a, M, D,
                             D_ff, s));
   } else {

@@ -85,9 +85,7 @@ geglu(const T *__restrict__ gu, T *__restrict__ z, int Dff, long n_vec) {
     V o;
 #pragma unroll
     for (int k = 0; k < E; ++k) {
-      const float x = to_f32(g.e[k]);
-      const float t = tanhf(0.7978845608028654f * fmaf(0.044715f * x * x, x, x));
-      o.e[k] = from_f32<T>(0.5f * x * (1.f + t) * to_f32(u.e[k]));
+      o.e[k] = from_f32<T>(gelu_tanh_times(to_f32(g.e[k]), to_f32(u.e[k])));
     }
     reinterpret_cast<V *>(z + row * Dff)[j] = o;
   }

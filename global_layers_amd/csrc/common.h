@@ -107,6 +107,15 @@ DEVI void load_lds16(const void *sbase, uint32_t lane_off, uint32_t lds_wave_off
                : "memory");
 }
 
+// GeGLU activation of one element pair ("Full Gemma 3 Block", How it works:
+// the MLP's GELU, tanh approximation, times the up projection), in fp32.
+// Shared by the stand-alone activation pass and the gate|up projection's
+// fused epilogue, so both round the same value.
+DEVI float gelu_tanh_times(float x, float u) {
+  const float t = tanhf(0.7978845608028654f * fmaf(0.044715f * x * x, x, x));
+  return 0.5f * x * (1.f + t) * u;
+}
+
 // RoPE rotation of one channel pair at integer position p: angle
 // p / scale * inv_freq, reduced modulo one turn in fp64 (positions reach
 // 131071, where an fp32 angle would be off by ~1e-2 rad), then fp32 sincos.

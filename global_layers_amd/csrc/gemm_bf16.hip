@@ -214,7 +214,12 @@ DEVI void qkv_epilogue(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, int n0,
   qkv_epilogue_impl<BM, BN, WM, WN, kFM, kFN>(acc, lds, m0, n0, M, ep);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, bool kQkv>
+// Epilogues of gemm_bf16_nt.
+constexpr int kEpiPlain = 0;  // C rows of bf16
+constexpr int kEpiQkv = 1;    // the fused QK-norm / RoPE / V-transpose epilogue below
+constexpr int kEpiGeglu = 2;  // z = GELU_tanh(g) * u of a gate|up tile, below
+
+template <int BM, int BN, int WM, int WN, int BK, int NST, int kEpi>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16 *__restrict__ B1,
              int N0, bf16 *__restrict__ C, int ldc, int M, int N, int K, int n_tiles_n,
@@ -246,7 +251,12 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   // slice; the slice only moves the wave-uniform base. A tile never straddles
   // N0 (the launcher splits such problems), so its weight rows come from one
   // matrix.
-  const bf16 *b_tile = n0 < N0 ? B0 + (size_t)n0 * K : B1 + (size_t)(n0 - N0) * K;
+  // kEpiGeglu: tile t holds gate rows 128 t .. 128 t + 127 of W (B0) and the
+  // matching up rows N0 + 128 t .. (N0 = D_ff, N = 2 D_ff): the second half of
+  // the tile's rows sits N0 - 128 rows further.
+  const bf16 *b_tile = kEpi == kEpiGeglu ? B0 + (size_t)(n0 / 2) * K
+                       : n0 < N0         ? B0 + (size_t)n0 * K
+                                         : B1 + (size_t)(n0 - N0) * K;
   const bf16 *a_tile = A + (size_t)m0 * K;
   uint32_t a_off[Cfg::kALoads], b_off[Cfg::kBLoads];
 #pragma unroll
@@ -261,7 +271,9 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
     const int byte = (wave + Cfg::kWaves * i) * 1024 + 16 * lane;
     const int r = byte / Cfg::kRowBytes, p = (byte % Cfg::kRowBytes) / 16;
     const int c = p ^ gemm_swz<Cfg::kChunks>(r);
-    b_off[i] = (uint32_t)(((size_t)(min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
+    const size_t brow = kEpi == kEpiGeglu ? (size_t)(r < BN / 2 ? r : N0 - BN / 2 + r)
+                                          : (size_t)(min(n0 + r, N - 1) - n0);
+    b_off[i] = (uint32_t)((brow * K + 8 * c) * 2);
   }
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
@@ -363,7 +375,7 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   static_assert(kKK % 2 == 0, "step 0 of every slice reads into buffer 0");
 
   drain_loads();
-  if constexpr (kQkv) {
+  if constexpr (kEpi == kEpiQkv) {
     qkv_epilogue<BM, BN, WM, WN, Cfg::kFM, Cfg::kFN>(acc, lds, m0, n0, M, ep);
     return;
   }
@@ -387,6 +399,23 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
         *reinterpret_cast<bf16x4 *>(lds + row * kPitch + c * 2) = v;
       }
   __syncthreads();
+  if constexpr (kEpi == kEpiGeglu) {
+    // z columns n0 / 2 .. n0 / 2 + BN / 2 - 1 (row stride ldc = D_ff): each
+    // item takes 8 gate values and the 8 up values of the same columns
+    constexpr int kZ16 = BN / 16;  // 16-byte pieces of z per tile row
+    for (int item = tid; item < BM * kZ16; item += Cfg::kThreads) {
+      const int row = item / kZ16, c = item % kZ16;
+      const int gm = m0 + row;
+      if (gm >= M) continue;
+      const bf16x8 g = *reinterpret_cast<const bf16x8 *>(lds + row * kPitch + 16 * c);
+      const bf16x8 u = *reinterpret_cast<const bf16x8 *>(lds + row * kPitch + (BN / 2) * 2 + 16 * c);
+      bf16x8 z;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) z[x] = (bf16)gelu_tanh_times((float)g[x], (float)u[x]);
+      *reinterpret_cast<bf16x8 *>(C + (size_t)gm * ldc + n0 / 2 + 8 * c) = z;
+    }
+    return;
+  }
   constexpr int kP16 = BN / 8;  // 16-byte pieces per tile row
 #pragma unroll 4
   for (int item = tid; item < BM * kP16; item += Cfg::kThreads) {
@@ -406,14 +435,16 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, bool kQkv = false>
+template <int BM, int BN, int WM, int WN, int BK, int NST, int kEpi = kEpiPlain>
 hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C, int M,
                        int N, int K, hipStream_t s, const QkvEpilogue &ep = QkvEpilogue{},
                        int ldc = -1) {
   if (ldc < 0) ldc = N;
-  // every tile's weight rows come from one matrix
-  if (N0 < N && N0 % BN != 0) {
-    if (kQkv) return hipErrorInvalidValue;
+  if (kEpi == kEpiGeglu && (N != 2 * N0 || N0 % (BN / 2) != 0)) return hipErrorInvalidValue;
+  // every tile's weight rows come from one matrix (a gate|up tile from its
+  // two halves, above)
+  if (kEpi != kEpiGeglu && N0 < N && N0 % BN != 0) {
+    if (kEpi == kEpiQkv) return hipErrorInvalidValue;
     hipError_t e = launch_gemm<BM, BN, WM, WN, BK, NST>(A, B0, B0, N0, C, M, N0, K, s,
                                                        QkvEpilogue{}, ldc);
     if (e != hipSuccess) return e;
@@ -422,8 +453,9 @@ hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf
   }
   using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
   const int tm = div_up_h(M, BM), tn = div_up_h(N, BN);
-  auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST, kQkv>;
-  constexpr int kTileLds = kQkv ? BM * qkv_tile_pitch<BN>() : BM * plain_tile_pitch<BN>();
+  auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST, kEpi>;
+  constexpr int kTileLds =
+      kEpi == kEpiQkv ? BM * qkv_tile_pitch<BN>() : BM * plain_tile_pitch<BN>();
   constexpr int kLds = Cfg::kLdsBytes > kTileLds ? Cfg::kLdsBytes : kTileLds;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
@@ -550,8 +582,26 @@ hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_k
   const double c256 = (double)div_up_h(t256, 256) * 256 * 256 / 1.0;
   const double c128 = (double)div_up_h(t128, 256) * 128 * 256 / 0.9;
   if (c256 <= c128)
-    return launch_gemm<256, 256, 2, 4, 64, 2, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
-  return launch_gemm<128, 256, 2, 4, 64, 3, true>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
+    return launch_gemm<256, 256, 2, 4, 64, 2, kEpiQkv>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
+  return launch_gemm<128, 256, 2, 4, 64, 3, kEpiQkv>(x, w_q, w_kv, N0, nullptr, M, N, K, s, ep);
+}
+
+hipError_t launch_gemm_geglu(const bf16 *x, const bf16 *w_gating, int D_ff, bf16 *z, int M, int K,
+                             hipStream_t s) {
+  // gate|up tiles of 128 + 128 columns; 256 or 128 rows by the same rounds x
+  // tile-cost model as the other projections
+  if (D_ff % 128 != 0 || (size_t)(D_ff + 128) * K * 2 >= ((size_t)1 << 32))
+    return hipErrorInvalidValue;
+  const bf16 *w_up = w_gating + (size_t)D_ff * K;
+  const long t256 = (long)div_up_h(M, 256) * (D_ff / 128);
+  const long t128 = (long)div_up_h(M, 128) * (D_ff / 128);
+  const double c256 = (double)div_up_h(t256, 256) * 256 * 256 / 1.0;
+  const double c128 = (double)div_up_h(t128, 256) * 128 * 256 / 0.9;
+  if (c256 <= c128)
+    return launch_gemm<256, 256, 2, 4, 64, 2, kEpiGeglu>(x, w_gating, w_up, D_ff, z, M, 2 * D_ff,
+                                                         K, s, QkvEpilogue{}, D_ff);
+  return launch_gemm<128, 256, 2, 4, 64, 3, kEpiGeglu>(x, w_gating, w_up, D_ff, z, M, 2 * D_ff, K,
+                                                       s, QkvEpilogue{}, D_ff);
 }
 
 template <typename OutT>

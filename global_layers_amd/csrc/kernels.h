@@ -26,6 +26,12 @@ struct QkvEpilogue {
 // Requires (H d_h) % 256 == 0 and (H_kv d_h) % 256 == 0.
 hipError_t launch_gemm_qkv_fused(const bf16 *x, const bf16 *w_q, const bf16 *w_kv, int N0, int M,
                                  int N, int K, const QkvEpilogue &ep, hipStream_t s);
+// The MLP's gate|up projection with the GeGLU activation fused into its
+// epilogue: z [M, D_ff] = GELU_tanh(x W_g^T) * (x W_u^T), W_gating [2, D_ff, K]
+// (gate rows, then up rows), D_ff a multiple of 128. The gate and up values
+// are rounded to bf16 before the activation, as the unfused path stores them.
+hipError_t launch_gemm_geglu(const bf16 *x, const bf16 *w_gating, int D_ff, bf16 *z, int M, int K,
+                             hipStream_t s);
 
 hipError_t launch_gemm_bf16_nt(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C,
                                int M, int N, int K, hipStream_t s);
