@@ -75,6 +75,45 @@ def test_prefill_sweep(gpu_lib, case):
     (assert_bf16_close if dtype == "bf16" else assert_f32_close)(f64(y), ref, "y")
 
 
+def _narrow_cases(n=6, seed=2028):
+    # D < H d_h (a model narrower than its heads; no Gemma 3 size, but the
+    # ABI allows it)
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d_h = int(r.choice([64, 128, 256]))
+        Hk = int(r.choice([1, 2, 4]))
+        H = Hk * int(r.choice([1, 2, 4]))
+        if H * d_h > 2048 or H * d_h < 256:
+            continue
+        D = max(64, H * d_h // int(r.choice([2, 4])))
+        B, T = int(r.integers(1, 3)), int(r.integers(1, 500))
+        t = G if r.random() < 0.4 else L
+        Wn = 0 if t == G else int(r.choice([1, 17, 100, 600]))
+        cases.append((B, T, D, H, Hk, d_h, t, Wn))
+    return cases
+
+
+NARROW = _narrow_cases()
+
+
+@pytest.mark.parametrize("case", NARROW, ids=[f"n{i}" for i in range(len(NARROW))])
+def test_prefill_sweep_narrow_model(gpu_lib, case):
+    """D < H d_h. y = o W_o^T sums H d_h terms of weights ~ N(0, 1/D), so y
+    and its absolute error from the bf16 roundings of o (and of the earlier
+    values) both grow by sqrt(H d_h / D) against the D >= H d_h shapes, while
+    the relative error does not: the bar's absolute term scales by that
+    factor, the relative term and the relative-RMS bound stay."""
+    B, T, D, H, Hk, d_h, t, Wn = case
+    log(f"narrow case {case}")
+    inp = small_prefill_inputs(33, B, T, D, H, Hk, d_h, "bf16")
+    kw = dict(H=H, H_kv=Hk, d_h=d_h, attn_type=t, window=Wn, rope_theta=1e4,
+              rope_scale=1.0, query_scale=d_h ** -0.5)
+    y = gpu_prefill(gpu_lib, inp, kw)
+    ref = oracle_prefill(inp, kw)
+    assert_bf16_close(f64(y), ref, "y", atol=2e-2 * float(np.sqrt(H * d_h / D)))
+
+
 def _decode_cases(n=8, seed=2027):
     r = np.random.default_rng(seed)
     cases = []
