@@ -24,15 +24,51 @@ template <int N> struct VmWait {
   static constexpr int kImm = (N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 };
 
-// Tile of BM x BN outputs, K sliced by BK, NST LDS stages. Waves WM x WN.
-// Each stage holds A [BM][BK] and B [BN][BK] bf16, rows of BK*2 bytes, 16-byte
-// chunks XOR-swizzled by row so fragment reads by 16 consecutive rows hit all banks.
-template <int BM, int BN, int WM, int WN, int BK, int NST>
+// MFMA shapes of the block GEMM (bf16 in, fp32 accumulators), issued with the
+// weight fragment as the first operand so the accumulator holds D^T: lane
+// column = output row m, registers = consecutive output columns n.
+//  * 32x32x16: a fragment is 32 rows x 16 k; lane l holds row l % 32, 16-byte
+//    k-chunk l / 32 of the step. Accumulator element e: m = l % 32,
+//    n = 8 (e / 4) + 4 (l / 32) + e % 4.
+//  * 16x16x32: a fragment is 16 rows x 32 k; lane l holds row l % 16, k-chunk
+//    l / 16 of the step. Element e: m = l % 16, n = 4 (l / 16) + e.
+// Same FLOPs per LDS byte; the 16x16x32 form sustains a higher shader clock
+// under a dense MFMA load on gfx950 (2.2-2.3 against 1.75-1.95 GHz measured,
+// 16 against 32 clocks per instruction), so it is the faster one.
+template <int kMf> struct Mfma;
+template <> struct Mfma<32> {
+  using Acc = f32x16;
+  static constexpr int kK = 16;  // k per instruction
+  static DEVI Acc mma(bf16x8 w, bf16x8 x, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, x, c, 0, 0, 0);
+  }
+  static DEVI int row(int lane) { return lane & 31; }
+  static DEVI int chunk(int step, int lane) { return 2 * step + (lane >> 5); }
+  static constexpr int kGroups = 4;  // runs of 4 consecutive columns per accumulator
+  static DEVI int col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
+};
+template <> struct Mfma<16> {
+  using Acc = f32x4;
+  static constexpr int kK = 32;
+  static DEVI Acc mma(bf16x8 w, bf16x8 x, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, c, 0, 0, 0);
+  }
+  static DEVI int row(int lane) { return lane & 15; }
+  static DEVI int chunk(int step, int lane) { return 4 * step + (lane >> 4); }
+  static constexpr int kGroups = 1;
+  static DEVI int col(int, int lane) { return 4 * (lane >> 4); }
+};
+
+// Tile of BM x BN outputs, K sliced by BK, NST LDS stages. Waves WM x WN,
+// kMf x kMf MFMAs. Each stage holds A [BM][BK] and B [BN][BK] bf16, rows of
+// BK*2 bytes, 16-byte chunks XOR-swizzled by row so fragment reads by 16
+// consecutive rows hit all banks.
+template <int BM, int BN, int WM, int WN, int BK, int NST, int kMf = 16>
 struct GemmCfg {
   static constexpr int kThreads = WM * WN * kWave;
   static constexpr int kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
-  static constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
+  static constexpr int kFM = kWaveM / kMf, kFN = kWaveN / kMf;
   static constexpr int kRowBytes = BK * 2;
   static constexpr int kChunks = kRowBytes / 16;
   static constexpr int kABytes = BM * kRowBytes, kBBytes = BN * kRowBytes;
@@ -41,7 +77,7 @@ struct GemmCfg {
   static constexpr int kALoads = kABytes / 1024 / kWaves;  // 1 KB loads per wave per stage
   static constexpr int kBLoads = kBBytes / 1024 / kWaves;
   static constexpr int kLoadsPerTile = kALoads + kBLoads;
-  static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be 32-aligned");
+  static_assert(kWaveM % kMf == 0 && kWaveN % kMf == 0, "wave tile must be MFMA-aligned");
   static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "loads");
   static_assert(kChunks == 8 || kChunks == 4, "BK must be 64 or 32");
 };
@@ -73,31 +109,39 @@ template <int BN> constexpr int plain_tile_pitch() { return BN * 2 + 16; }
 // i.e. p f_i revolutions with f_i = theta^(-2i/d_h) / (2 pi scale). The
 // product is reduced modulo 1 in fp64 (positions reach 131071), and the
 // reduced angle goes to the hardware sine and cosine, which take revolutions.
-template <int BM, int BN, int WM, int WN, int kFM, int kFN>
-DEVI void qkv_epilogue_impl(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, int n0, int M,
-                            const QkvEpilogue &ep) {
-  constexpr int kThreads = WM * WN * kWave;
+// The wave tiles' accumulators, rounded to bf16, into a BM x BN tile in LDS
+// with a row pitch of kPitch bytes (8-byte stores of 4 consecutive columns).
+template <int kMf, int WM, int WN, int BM, int BN, int kPitch, int kFM, int kFN>
+DEVI void stage_tile(const typename Mfma<kMf>::Acc (&acc)[kFM][kFN], char *lds) {
+  using Mf = Mfma<kMf>;
   constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
-  constexpr int kPitch = qkv_tile_pitch<BN>();
-  static_assert(BN == 256, "one tile row = 256 columns");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int lrow = lane & 31, hh = lane >> 5;
-
-  __syncthreads();  // every wave is done with the k-loop stages (and its loads have landed)
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < kFN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = wm * kWaveM + i * 32 + lrow;
-        const int c = wn * kWaveN + j * 32 + 8 * g + 4 * hh;
+      for (int g = 0; g < Mf::kGroups; ++g) {
+        const int row = wm * kWaveM + i * kMf + Mf::row(lane);
+        const int c = wn * kWaveN + j * kMf + Mf::col(g, lane);
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][g * 4 + r];
         *reinterpret_cast<bf16x4 *>(lds + row * kPitch + c * 2) = v;
       }
+}
+
+template <int BM, int BN, int WM, int WN, int kMf, int kFM, int kFN>
+DEVI void qkv_epilogue_impl(const typename Mfma<kMf>::Acc (&acc)[kFM][kFN], char *lds, int m0,
+                            int n0, int M, const QkvEpilogue &ep) {
+  constexpr int kThreads = WM * WN * kWave;
+  constexpr int kPitch = qkv_tile_pitch<BN>();
+  static_assert(BN == 256, "one tile row = 256 columns");
+  const int tid = threadIdx.x, lane = tid & 63;
+
+  __syncthreads();  // every wave is done with the k-loop stages (and its loads have landed)
+  stage_tile<kMf, WM, WN, BM, BN, kPitch>(acc, lds);
   __syncthreads();
 
   const int d_h = ep.d_h, half = d_h / 2;
@@ -208,10 +252,10 @@ DEVI void qkv_epilogue_impl(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, in
   }
 }
 
-template <int BM, int BN, int WM, int WN, int kFM, int kFN>
-DEVI void qkv_epilogue(const f32x16 (&acc)[kFM][kFN], char *lds, int m0, int n0, int M,
-                       const QkvEpilogue &ep) {
-  qkv_epilogue_impl<BM, BN, WM, WN, kFM, kFN>(acc, lds, m0, n0, M, ep);
+template <int BM, int BN, int WM, int WN, int kMf, int kFM, int kFN>
+DEVI void qkv_epilogue(const typename Mfma<kMf>::Acc (&acc)[kFM][kFN], char *lds, int m0, int n0,
+                       int M, const QkvEpilogue &ep) {
+  qkv_epilogue_impl<BM, BN, WM, WN, kMf, kFM, kFN>(acc, lds, m0, n0, M, ep);
 }
 
 // Epilogues of gemm_bf16_nt.
@@ -219,12 +263,13 @@ constexpr int kEpiPlain = 0;  // C rows of bf16
 constexpr int kEpiQkv = 1;    // the fused QK-norm / RoPE / V-transpose epilogue below
 constexpr int kEpiGeglu = 2;  // z = GELU_tanh(g) * u of a gate|up tile, below
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, int kEpi>
+template <int BM, int BN, int WM, int WN, int BK, int NST, int kEpi, int kMf>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16 *__restrict__ B1,
              int N0, bf16 *__restrict__ C, int ldc, int M, int N, int K, int n_tiles_n,
              QkvEpilogue ep) {
-  using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
+  using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST, kMf>;
+  using Mf = Mfma<kMf>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
@@ -288,11 +333,11 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
       load_lds16(bk, b_off[i], sb + Cfg::kABytes + (wu + Cfg::kWaves * i) * 1024);
   };
 
-  f32x16 acc[Cfg::kFM][Cfg::kFN];
+  typename Mf::Acc acc[Cfg::kFM][Cfg::kFN];
 #pragma unroll
   for (int i = 0; i < Cfg::kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::kFN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < Cfg::kFN; ++j) acc[i][j] = typename Mf::Acc{};
 
   const int nk = K / BK;
   // Every iteration issues one k-tile (past the end: the last one again, into
@@ -303,7 +348,6 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
 #pragma unroll
   for (int s0 = 0; s0 < NST - 1; ++s0) issue_clamped(s0);
 
-  const int lrow = lane & 31, hh = lane >> 5;
   // wait until the oldest k-tile in flight has landed, then for every wave
   auto wait_tile = [&]() {
     __builtin_amdgcn_s_waitcnt(VmWait<(NST - 2) * Cfg::kLoadsPerTile>::kImm);
@@ -312,20 +356,19 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   };
 
   // Fragment byte offsets inside a stage: row r of the A (B) slice, logical
-  // chunk 2 kk + hh. The swizzle flips only the low chunk bits, so per
-  // fragment one base plus a compile-time kk term covers the slice.
-  constexpr int kKK = BK / 16;
+  // chunk Mf::chunk(kk, lane) of k-step kk.
+  constexpr int kKK = BK / Mf::kK;
   uint32_t a_fo[Cfg::kFM], b_fo[Cfg::kFN];
   int a_sw[Cfg::kFM], b_sw[Cfg::kFN];
 #pragma unroll
   for (int i = 0; i < Cfg::kFM; ++i) {
-    const int r = wm * Cfg::kWaveM + i * 32 + lrow;
+    const int r = wm * Cfg::kWaveM + i * kMf + Mf::row(lane);
     a_fo[i] = r * Cfg::kRowBytes;
     a_sw[i] = gemm_swz<Cfg::kChunks>(r);
   }
 #pragma unroll
   for (int j = 0; j < Cfg::kFN; ++j) {
-    const int r = wn * Cfg::kWaveN + j * 32 + lrow;
+    const int r = wn * Cfg::kWaveN + j * kMf + Mf::row(lane);
     b_fo[j] = Cfg::kABytes + r * Cfg::kRowBytes;
     b_sw[j] = gemm_swz<Cfg::kChunks>(r);
   }
@@ -336,10 +379,10 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
     const char *sb = lds + st * Cfg::kStageBytes;
 #pragma unroll
     for (int i = 0; i < Cfg::kFM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8 *>(sb + a_fo[i] + 16 * ((2 * kk + hh) ^ a_sw[i]));
+      a[i] = *reinterpret_cast<const bf16x8 *>(sb + a_fo[i] + 16 * (Mf::chunk(kk, lane) ^ a_sw[i]));
 #pragma unroll
     for (int j = 0; j < Cfg::kFN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8 *>(sb + b_fo[j] + 16 * ((2 * kk + hh) ^ b_sw[j]));
+      b[j] = *reinterpret_cast<const bf16x8 *>(sb + b_fo[j] + 16 * (Mf::chunk(kk, lane) ^ b_sw[j]));
   };
 
   // The epilogues below stage the C tile in the k-loop's LDS stages. The
@@ -364,8 +407,7 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
       for (int i = 0; i < Cfg::kFM; ++i)
 #pragma unroll
         for (int j = 0; j < Cfg::kFN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j],
-                                                              0, 0, 0);
+          acc[i][j] = Mf::mma(bfr[cur][j], af[cur][i], acc[i][j]);
       // the next step's reads go out first, then the MFMAs
       if (kk + 1 < kKK) __builtin_amdgcn_sched_group_barrier(0x100, Cfg::kFM + Cfg::kFN, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, Cfg::kFM * Cfg::kFN, 0);
@@ -376,28 +418,15 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
 
   drain_loads();
   if constexpr (kEpi == kEpiQkv) {
-    qkv_epilogue<BM, BN, WM, WN, Cfg::kFM, Cfg::kFN>(acc, lds, m0, n0, M, ep);
+    qkv_epilogue<BM, BN, WM, WN, kMf, Cfg::kFM, Cfg::kFN>(acc, lds, m0, n0, M, ep);
     return;
   }
-  // acc[i][j] holds D[n][m]: lane column m = lane % 32, rows n = 8g + 4h + r.
   // The bf16 tile is staged in LDS (the k-loop stages are free once every
   // wave has passed the barrier below) and written back as whole rows of
   // 16-byte pieces.
   constexpr int kPitch = plain_tile_pitch<BN>();
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < Cfg::kFM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::kFN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = wm * Cfg::kWaveM + i * 32 + lrow;
-        const int c = wn * Cfg::kWaveN + j * 32 + 8 * g + 4 * hh;
-        bf16x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][g * 4 + r];
-        *reinterpret_cast<bf16x4 *>(lds + row * kPitch + c * 2) = v;
-      }
+  stage_tile<kMf, WM, WN, BM, BN, kPitch>(acc, lds);
   __syncthreads();
   if constexpr (kEpi == kEpiGeglu) {
     // z columns n0 / 2 .. n0 / 2 + BN / 2 - 1 (row stride ldc = D_ff): each
@@ -435,7 +464,7 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, int kEpi = kEpiPlain>
+template <int BM, int BN, int WM, int WN, int BK, int NST, int kEpi = kEpiPlain, int kMf = 16>
 hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf16 *C, int M,
                        int N, int K, hipStream_t s, const QkvEpilogue &ep = QkvEpilogue{},
                        int ldc = -1) {
@@ -445,15 +474,15 @@ hipError_t launch_gemm(const bf16 *A, const bf16 *B0, const bf16 *B1, int N0, bf
   // two halves, above)
   if (kEpi != kEpiGeglu && N0 < N && N0 % BN != 0) {
     if (kEpi == kEpiQkv) return hipErrorInvalidValue;
-    hipError_t e = launch_gemm<BM, BN, WM, WN, BK, NST>(A, B0, B0, N0, C, M, N0, K, s,
-                                                       QkvEpilogue{}, ldc);
+    hipError_t e = launch_gemm<BM, BN, WM, WN, BK, NST, kEpiPlain, kMf>(A, B0, B0, N0, C, M, N0,
+                                                                      K, s, QkvEpilogue{}, ldc);
     if (e != hipSuccess) return e;
-    return launch_gemm<BM, BN, WM, WN, BK, NST>(A, B1, B1, N - N0, C + N0, M, N - N0, K, s,
-                                               QkvEpilogue{}, ldc);
+    return launch_gemm<BM, BN, WM, WN, BK, NST, kEpiPlain, kMf>(A, B1, B1, N - N0, C + N0, M,
+                                                              N - N0, K, s, QkvEpilogue{}, ldc);
   }
-  using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST>;
+  using Cfg = GemmCfg<BM, BN, WM, WN, BK, NST, kMf>;
   const int tm = div_up_h(M, BM), tn = div_up_h(N, BN);
-  auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST, kEpi>;
+  auto kern = gemm_bf16_nt<BM, BN, WM, WN, BK, NST, kEpi, kMf>;
   constexpr int kTileLds =
       kEpi == kEpiQkv ? BM * qkv_tile_pitch<BN>() : BM * plain_tile_pitch<BN>();
   constexpr int kLds = Cfg::kLdsBytes > kTileLds ? Cfg::kLdsBytes : kTileLds;
