@@ -11,10 +11,15 @@
 //    of a GQA group (up to 4) are packed into the workgroup, so each K/V tile
 //    staged in LDS feeds every query head that reads it. At d_h <= 128 two
 //    workgroups share each CU (registers capped at 256 per lane).
-//  * Each wave computes S^T = K Q^T with 32x32x16 bf16 MFMAs: a lane owns one
-//    query row and 32 of the 64 keys of a tile. K rows are fed in the
-//    permuted order kappa(i) so that the S^T accumulators of a lane are, in
-//    register order, the 16-byte B operand of the PV MFMA (O^T += V^T P^T)
+//  * A wave owns 32 query rows as two blocks of 16 and computes S^T = K Q^T
+//    with 16x16x32 bf16 MFMAs (gfx950 sustains a higher shader clock on them
+//    than on 32x32x16 ones: 2.2-2.3 against 1.75-1.95 GHz measured under a
+//    dense load). Each K fragment (16 keys x 32 channels) feeds both row
+//    blocks. Lane l owns query l % 16 of each block and, of every 32-key
+//    half, the 8 keys 8 (l / 16) .. + 7: the K rows of a half are fed as two
+//    16-key sub-tiles in the order pi(j, i) (sub-tile j, MFMA row i), so that
+//    a lane's S^T accumulators of the two sub-tiles are, in register order,
+//    the 16-byte B operand of the PV MFMA (O^T += V^T P^T over the 32 keys)
 //    without moving data.
 //  * V arrives transposed ([d_h][T]) so the PV A operand is a contiguous
 //    16-byte LDS read.
@@ -26,9 +31,9 @@
 //  * Tiles move global -> LDS with direct loads (16 bytes per lane, no
 //    staging registers) into XOR-swizzled, unpadded layouts that keep the
 //    fragment reads free of bank conflicts. Each 64-key tile runs as two
-//    32-key halves in one fixed sequence of 4-MFMA groups; the S MFMAs of the
-//    next half overlap the softmax and PV of this one. K sits in four 32-key
-//    slots and V^T in two tile buffers; one barrier per tile.
+//    32-key halves in one fixed sequence of groups of 4 fragments; the S
+//    MFMAs of the next half overlap the softmax and PV of this one. K sits in
+//    four 32-key slots and V^T in two tile buffers; one barrier per tile.
 //  * Split-KV: when (rows x heads) give too few workgroups to fill the chip,
 //    the key range of each query tile is cut into chunks handled by separate
 //    workgroups; a query tile with several chunks writes normalised partial
@@ -44,6 +49,7 @@ namespace {
 
 constexpr int kBN = 64;       // keys per tile
 constexpr int kThreads = 256; // 4 waves
+constexpr int kQB = 2;        // 16-row query blocks per wave
 
 template <int D> struct AttnCfg {
   static constexpr int kKRowBytes = 2 * D;            // one key row of K
@@ -54,26 +60,39 @@ template <int D> struct AttnCfg {
   static constexpr int kLdsBytes = 4 * kKHalfBytes + 2 * kVTileBytes;
   static constexpr int kKHalfLoads = kKHalfBytes / 1024 / 4;  // 1 KB loads per wave per K half
   static constexpr int kVLoads = kVTileBytes / 1024 / 4;      // per V tile
-  static constexpr int kKS = D / 16;                          // k-steps of the QK^T contraction
-  static constexpr int kDB = D / 32;                          // 32-row blocks of O^T
+  static constexpr int kKS = D / 32;                          // 32-channel k-steps of QK^T
+  static constexpr int kCB = D / 16;                          // 16-channel blocks of O^T
 };
+
+// K row of a 32-key half fed as MFMA row i (0..15) of sub-tile j (0, 1):
+// lane l's accumulator rows 4 (l / 16) + r of sub-tile j are then keys
+// 8 (l / 16) + 4 j + r of the half.
+DEVI int pi_row(int j, int i) { return 8 * (i >> 2) + 4 * j + (i & 3); }
 
 // XOR swizzles of the 16-byte chunk index inside a row. The LDS serves a
 // 16-byte-per-lane read 16 lanes (256 bytes, all 64 banks) per cycle, so the
 // 16 rows that lanes 16j .. 16j+15 read must land on 16 distinct 16-byte bank
-// positions. K fragment reads of lanes 0-15 hit rows kappa(0..15), a
-// permutation of 0..15 (+32 per key block); V^T reads hit 16 consecutive rows.
-//  * rows of >= 256 bytes (K, d_h >= 128): position = chunk mod 16, so XOR with r & 15;
-//  * 128-byte rows (V^T, K at d_h = 64): position = 8 (r & 1) + chunk mod 8, so
-//    XOR with (r >> 1) & 7.
-template <int D> DEVI int swz_k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
+// positions. K fragment reads of lanes 0-15 hit rows pi_row(j, 0..15), i.e.
+// rows {0-3, 8-11, 16-19, 24-27} (+4 for j = 1); V^T reads hit 16
+// consecutive rows.
+//  * K rows of >= 256 bytes (d_h >= 128): position = chunk mod 16; XOR with
+//    bits 0, 1, 3, 4 of r, which differ across such a row set;
+//  * 128-byte rows (V^T, K at d_h = 64): position = 8 (r & 1) + chunk mod 8;
+//    K: XOR with bits 1, 3, 4 of r; V^T: with (r >> 1) & 7.
+template <int D> DEVI int swz_k(int r) {
+  return D >= 128 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | ((r >> 2) & 6));
+}
 DEVI int swz_v(int r) { return (r >> 1) & 7; }
 // Key-major V tiles (cache mode): a transposing read touches, per 32 lanes,
-// 4 consecutive key rows x 64 bytes; XOR chunk bits 2-3 with r mod 4 (d_h
-// >= 128: rows of 256 B and more start in the same bank) or chunk bit 2 with
-// bit 1 of r (d_h = 64: 128-byte rows, odd rows already in the other half)
-// so the 4 rows take distinct banks.
-template <int D> DEVI int swz_vc(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+// 8 key rows (8 (l / 16) + 0..3, + 4 for the second read) x 32 bytes. The
+// 32-byte unit index within the row is XORed with a function of the key that
+// differs across those 8 rows (d_h >= 128: rows of 256 B and more start in
+// the same bank, 8 units per 256 B; d_h = 64: 128-byte rows, odd rows in the
+// other half, 4 units per row). As a 16-byte chunk XOR: twice that.
+template <int D> DEVI int swz_vc_unit(int r) {
+  return D >= 128 ? ((r & 3) | ((r >> 1) & 4)) : (((r >> 1) & 1) | ((r >> 2) & 2));
+}
+template <int D> DEVI int swz_vc(int r) { return 2 * swz_vc_unit<D>(r); }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0) and lgkmcnt(0), expcnt free.
 constexpr int kWaitVmLgkm0 = 0x7 << 4;
@@ -94,35 +113,29 @@ template <int N, typename F> DEVI void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Key permutation inside a 32-key block (see the header comment).
-DEVI int kappa(int i) {
-  const int g = i >> 3, h = (i >> 2) & 1, r = i & 3;
-  return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + r;
-}
-
 // Group schedule of one 64-key tile (see the tile step in the attention
-// kernel): for each 32-key half, kNG groups of 4 S MFMAs then kPG groups of 4
-// PV MFMAs.
+// kernel): for each 32-key half, kNG groups of 4 K fragments (8 S MFMAs) then
+// kPG groups of 4 V^T fragments (8 PV MFMAs).
 template <int D> struct TileSched {
   using Cfg = AttnCfg<D>;
-  static constexpr int kG = 4;                   // MFMAs per group
-  static constexpr int kNG = Cfg::kKS / kG;      // S groups per half
-  static constexpr int kPG = Cfg::kDB / 2;       // PV groups per half
+  static constexpr int kG = 4;                   // fragments per group
+  static constexpr int kNG = 2 * Cfg::kKS / kG;  // S groups per half
+  static constexpr int kPG = Cfg::kCB / kG;      // PV groups per half
   static constexpr int kNGT = kNG + kPG;         // groups per half
   static constexpr int kQPG = 4 / kNG;           // weight quads whose exponentials share an S group
   static constexpr int kPieces = 2 * Cfg::kKHalfLoads + Cfg::kVLoads;  // prefetch loads per tile
   static constexpr int kPPG = (kPieces + kNGT - 1) / kNGT;             // of them per first-half group
-  // The 16 weights of a half (4 quads of 4) pass three stages: exp2, packing
-  // to bf16 pairs (the PV B operand), and the row sum of the packed values
-  // (l sums the bf16-rounded weights the PV MFMAs use, so numerator and
-  // denominator of O / l carry the same rounding). A quad's stages sit in
-  // successive groups, so no instruction waits on the one just before it and
-  // the in-order issue keeps feeding the matrix pipe: exps of quad q in S
-  // group q / kQPG, its packing one group later, its sum one more. The PV
-  // MFMAs take the first bf16 operand (quads 0, 1) before the second.
+  // The 16 weights of a half (4 quads of 4: quad 2 b + j holds row block b,
+  // sub-tile j) pass three stages: exp2, packing to bf16 (the PV B operand of
+  // row block b), and the row sum of the packed values (l sums the
+  // bf16-rounded weights the PV MFMAs use, so numerator and denominator of
+  // O / l carry the same rounding). Exps of quad q and their packing sit in
+  // S group q / kQPG (every PV group takes both row blocks' operands, so all
+  // packing precedes the first PV group; packing right after the exps keeps
+  // the exponentials' registers short-lived), its sum one group later.
   static constexpr int e_grp(int qd) { return qd / kQPG; }
-  static constexpr int c_grp(int qd) { return kNG > 1 ? qd / kQPG + 1 : 0; }
-  static constexpr int d_grp(int qd) { return (qd / kQPG + 2 < kNGT) ? qd / kQPG + 2 : kNGT - 1; }
+  static constexpr int c_grp(int qd) { return qd / kQPG; }
+  static constexpr int d_grp(int qd) { return c_grp(qd) + 1 < kNGT ? c_grp(qd) + 1 : kNGT - 1; }
 };
 
 struct Geo {  // per-workgroup geometry, identical in the attention and combine kernels
@@ -149,14 +162,10 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
   return g;
 }
 
-// RB: blocks of 32 query rows per wave; each K / V^T fragment read from LDS
-// feeds RB MFMAs. The planner takes RB = 1. At d_h <= 128 the kernel is
-// built for two waves per SIMD (256 registers per lane), so two workgroups
-// share a CU and each one's barriers and post-barrier fragment waits fall
-// while the other computes; that measured faster than two row blocks per
-// wave at one wave per SIMD (27B-shaped layers: global 7.12 against
-// 7.46 ms, local 0.62 against 0.76 ms). At d_h = 256 one wave per SIMD
-// either way (O alone takes 128 registers per row block).
+// At d_h <= 128 the kernel is built for two waves per SIMD (256 registers per
+// lane), so two workgroups share a CU and each one's barriers and
+// post-barrier fragment waits fall while the other computes. At d_h = 256
+// one wave per SIMD (O alone takes 128 registers).
 // kCache: keys and values come straight from the caches ([B, S_cache, H_kv,
 // d_h] each, V key-major, as a chunk of a longer prefill finds them). K rows
 // land in LDS as in the workspace layout; a V tile lands key-major and the
@@ -164,7 +173,7 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
 // transposing LDS read of gfx950 (two 4-key halves). Rows at or past the
 // valid length are loaded as copies of the last valid row, so whatever the
 // slots beyond it hold (NaN included) never reaches the arithmetic.
-template <int D, int RB, bool kCache>
+template <int D, bool kCache>
 __global__ void __launch_bounds__(kThreads, D <= 128 ? 2 : 1)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
@@ -182,7 +191,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // XCD.
   const int bid = remap ? xcd_remap(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int split = bid % n_split;
-  constexpr int kRB = RB, kRPW = 32 * RB;
+  constexpr int kRPW = 16 * kQB;  // query rows per wave
   const Geo geo = geometry(a, kv_len, bid / n_split, gp, n_qtiles, n_hgrp, chunk_keys, kRPW);
   if (split >= geo.n_active) return;  // uniform per block
   const int b = geo.b, kh = geo.kh;
@@ -197,19 +206,19 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int my_begin = geo.tile_begin + split * chunk_keys;
   const int my_end = geo.kv_end > geo.kv_begin ? min(geo.kv_end, my_begin + chunk_keys) : my_begin;
 
-  const int col = lane & 31, hh = lane >> 5;
-  int my_t[kRB];  // this lane's query row in each row block
+  const int qc = lane & 15, q4 = lane >> 4;  // query within a row block; key octet of a half
+  int my_t[kQB];  // this lane's query row in each row block
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) my_t[rb] = wq0 + 32 * rb + col;
+  for (int qb = 0; qb < kQB; ++qb) my_t[qb] = wq0 + 16 * qb + qc;
 
-  f32x16 acc_o[kRB][Cfg::kDB];
+  f32x4 acc_o[kQB][Cfg::kCB];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb)
+  for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-    for (int i = 0; i < Cfg::kDB; ++i) acc_o[rb][i] = f32x16{};
-  float l_run[kRB];
+    for (int i = 0; i < Cfg::kCB; ++i) acc_o[qb][i] = f32x4{};
+  float l_run[kQB];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) l_run[rb] = 0.f;
+  for (int qb = 0; qb < kQB; ++qb) l_run[qb] = 0.f;
 
   const char *kbase = kCache ? (const char *)(k + ((size_t)b * a.S_cache * a.Hk + kh) * D)
                              : (const char *)(k + ((size_t)b * a.Hk + kh) * a.T_pad * D);
@@ -225,36 +234,39 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // writes byte 16 l of it. K half h (tile h / 2, key block h % 2) sits in
   // slot h % 4; its row r, chunk position p holds logical chunk p ^ swz_k(r).
   // Global addresses split into a wave-uniform base and a per-lane 32-bit
-  // offset. The swizzle pattern of K pieces repeats every 2 pieces (V: every
-  // piece), and pieces i and i + 2 (V: i + 1) are a fixed number of rows apart,
-  // so two (one) lane offsets plus a uniform step cover every piece.
+  // offset: one lane offset per K piece of a half (the K swizzle depends on
+  // row bits 0-4, which differ between them), one for every V^T piece (pieces
+  // 32 rows apart, which swz_v ignores).
   // With kCache a lane keeps its row within the piece and its chunk offset
   // instead; each load clamps the row to the last valid key and addresses it
   // from the tile's first row (wave-uniform base, 32-bit lane offset). A V
   // tile is then key-major: piece i holds keys 4 i (1024 / (2 d_h)) + ..., row
-  // r with chunk position p holding logical chunk p ^ swz_vc(r); the swizzle
-  // depends on r mod 4 only, which is the same for every piece of a lane.
+  // r with chunk position p holding logical chunk p ^ swz_vc(r); swz_vc
+  // depends on row bits 0, 1 and 3, so pieces an odd multiple of 8 rows apart
+  // (d_h = 256) take a second lane offset.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  uint32_t k_lane[2];
-  int k_row[2];
+  uint32_t k_lane[Cfg::kKHalfLoads];
+  int k_row[Cfg::kKHalfLoads];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < Cfg::kKHalfLoads; ++i) {
     const int byte = (w + 4 * i) * 1024 + 16 * lane;
     const int r = byte / Cfg::kKRowBytes, pch = (byte % Cfg::kKRowBytes) / 16;
     k_lane[i] = (uint32_t)((kCache ? 0 : r * Cfg::kKRowBytes) + 16 * (pch ^ swz_k<D>(r)));
     k_row[i] = r;
   }
-  uint32_t v_lane;
+  constexpr int kVRowStep = 4096 / (2 * D);  // cache mode: key rows between a wave's V pieces
+  uint32_t v_lane[2];
   int v_row;
   {
     const int byte = w * 1024 + 16 * lane;
     if constexpr (kCache) {
       const int r = byte / (2 * D), pch = (byte % (2 * D)) / 16;
-      v_lane = (uint32_t)(16 * (pch ^ swz_vc<D>(r)));
+#pragma unroll
+      for (int p = 0; p < 2; ++p) v_lane[p] = (uint32_t)(16 * (pch ^ swz_vc<D>(r + p * kVRowStep)));
       v_row = r;
     } else {
       const int r = byte / Cfg::kVRowBytes, pch = (byte % Cfg::kVRowBytes) / 16;
-      v_lane = (uint32_t)(r * a.T_pad * 2 + 16 * (pch ^ swz_v(r)));
+      v_lane[0] = v_lane[1] = (uint32_t)(r * a.T_pad * 2 + 16 * (pch ^ swz_v(r)));
       v_row = 0;
     }
   }
@@ -266,12 +278,11 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const uint32_t dst = lds0 + slot * Cfg::kKHalfBytes + (wu + 4 * i) * 1024;
     if constexpr (kCache) {
       const int s0 = tile_s0(t);
-      const int r = 32 * kbh + k_row[i & 1] + (i >> 1) * (8192 / Cfg::kKRowBytes);
-      load_lds16(kbase + (size_t)s0 * cache_pitch, clamped(s0, r) + k_lane[i & 1], dst);
+      load_lds16(kbase + (size_t)s0 * cache_pitch, clamped(s0, 32 * kbh + k_row[i]) + k_lane[i],
+                 dst);
     } else {
-      const char *src =
-          kbase + (size_t)(tile_s0(t) + 32 * kbh) * Cfg::kKRowBytes + (size_t)(i >> 1) * 8192;
-      load_lds16(src, k_lane[i & 1], dst);
+      const char *src = kbase + (size_t)(tile_s0(t) + 32 * kbh) * Cfg::kKRowBytes;
+      load_lds16(src, k_lane[i], dst);
     }
   };
   // V^T columns of tile t into V buffer `buf` (piece i: channel rows 32 i + ...),
@@ -281,10 +292,10 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if constexpr (kCache) {
       const int s0 = tile_s0(t);
       load_lds16(vbase + (size_t)s0 * cache_pitch,
-                 clamped(s0, v_row + i * (4096 / (2 * D))) + v_lane, dst);
+                 clamped(s0, v_row + i * kVRowStep) + v_lane[i & 1], dst);
     } else {
       const char *src = vbase + (size_t)tile_s0(t) * 2 + (size_t)i * 32 * a.T_pad * 2;
-      load_lds16(src, v_lane, dst);
+      load_lds16(src, v_lane[0], dst);
     }
   };
 
@@ -300,15 +311,15 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // The first tiles go out before the Q fragments: the fragment selects below
   // wait for the Q data, and the tiles' loads then already overlap them.
   issue_prologue();
-  // Q^T fragments (B operand): query my_t, channels 16 ks + 8 hh + [0, 8).
-  bf16x8 qf[kRB][Cfg::kKS];
+  // Q^T fragments (B operand): query my_t, channels 32 ks + 8 q4 + [0, 8).
+  bf16x8 qf[kQB][Cfg::kKS];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const bool ok = my_t[rb] < a.T;
-    const bf16 *qp = q + (((size_t)b * a.H + h) * a.T + (ok ? my_t[rb] : 0)) * D + 8 * hh;
+  for (int qb = 0; qb < kQB; ++qb) {
+    const bool ok = my_t[qb] < a.T;
+    const bf16 *qp = q + (((size_t)b * a.H + h) * a.T + (ok ? my_t[qb] : 0)) * D + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
-      qf[rb][ks] = ok ? *reinterpret_cast<const bf16x8 *>(qp + 16 * ks) : bf16x8{};
+      qf[qb][ks] = ok ? *reinterpret_cast<const bf16x8 *>(qp + 32 * ks) : bf16x8{};
   }
 
   // max_c |1 + gamma_k[c]| (bounds the key norms, below); its loads, the Q
@@ -320,47 +331,51 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   publish_tiles();
 
   // Per-lane LDS byte offsets of the MFMA fragments. K: lane feeds row
-  // kappa(col) of a 32-key half and reads logical chunk 2 ks + hh; the swizzle
-  // only flips the low chunk bits, so 8 (4 at d_h = 64) base offsets plus
-  // compile-time immediates cover every k-step. V^T: row 32 db + col, chunk
-  // 2 kk + hh; 4 bases, db in the immediate.
-  constexpr int kKBases = Cfg::kKS < 8 ? Cfg::kKS : 8;
-  int koff[kKBases];
-  {
-    const int krow = kappa(col), ksw = swz_k<D>(krow);
+  // pi_row(j, qc) of a 32-key half and reads logical chunk 4 ks + q4; the
+  // swizzle flips chunk bits 0-3 (0-2 at d_h = 64), so one base per
+  // (sub-tile, ks mod 4) and compile-time immediates cover every k-step. V^T:
+  // row 16 cb + qc, chunk 4 kb + q4 (kb: the half); one base per half, cb in
+  // the immediate.
+  constexpr int kKSB = Cfg::kKS < 4 ? Cfg::kKS : 4;
+  int koff[2][kKSB];
 #pragma unroll
-    for (int j = 0; j < kKBases; ++j) koff[j] = krow * Cfg::kKRowBytes + 16 * ((2 * j + hh) ^ ksw);
+  for (int j = 0; j < 2; ++j) {
+    const int krow = pi_row(j, qc), ksw = swz_k<D>(krow);
+#pragma unroll
+    for (int s = 0; s < kKSB; ++s) koff[j][s] = krow * Cfg::kKRowBytes + 16 * ((4 * s + q4) ^ ksw);
   }
-  int voff[4];
+  int voff[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    voff[kk] = 4 * Cfg::kKHalfBytes + col * Cfg::kVRowBytes + 16 * ((2 * kk + hh) ^ swz_v(col));
-  auto kfrag = [&](int slot, int ks) {
-    return *reinterpret_cast<const bf16x8 *>(lds + slot * Cfg::kKHalfBytes + koff[ks % kKBases] +
-                                             (ks / kKBases) * 32 * kKBases);
+  for (int kb = 0; kb < 2; ++kb)
+    voff[kb] = 4 * Cfg::kKHalfBytes + qc * Cfg::kVRowBytes + 16 * ((4 * kb + q4) ^ swz_v(qc));
+  auto kfrag = [&](int slot, int j, int ks) {
+    return *reinterpret_cast<const bf16x8 *>(lds + slot * Cfg::kKHalfBytes + koff[j][ks % kKSB] +
+                                             (ks / kKSB) * 256);
   };
   // kCache: the PV operand from a key-major V tile by two transposing reads.
   // Within each 16 lanes, element e of lane i of such a read is element i & 3
-  // at the address of lane 4 e + (i >> 2). So lane 16 G + 4 e + u points at
-  // channels 32 db + 16 (G & 1) + 4 u .. + 3 of key 16 kk + 8 (G >> 1) + 4 r + e
-  // (r: which 4-key half), and lane 16 G + i receives keys 16 kk + 8 hh + 4 r +
-  // 0..3 of channel 32 db + (lane & 31). The key row's swizzle XORs the 8-byte
-  // unit index with 8 (e or e >> 1), which permutes 64-byte blocks of the row:
-  // per-lane bases for db mod 4, the rest immediates.
-  constexpr int kTB = Cfg::kDB < 4 ? Cfg::kDB : 4;
+  // at the address of lane 4 e + (i >> 2). So lane 16 q4 + 4 e + u points at
+  // channels 16 cb + 4 u .. + 3 of key 32 kb + 8 q4 + 4 r + e (r: which 4-key
+  // half), and lane 16 q4 + i receives keys 32 kb + 8 q4 + 4 r + 0..3 of
+  // channel 16 cb + i. The key row's swizzle XORs the 32-byte unit index (cb
+  // mod 8, mod 4 at d_h = 64) with swz_vc_unit of the key, which depends on
+  // bits 0, 1, 3 of the key only: per-lane bases for cb mod 8, the rest
+  // immediates.
+  constexpr int kUnits = D >= 128 ? 8 : 4;  // 32-byte units per 256 bytes of a row
+  constexpr int kTB = Cfg::kCB < kUnits ? Cfg::kCB : kUnits;
   int vtr[kTB];
   {
-    const int G = lane >> 4, e = (lane >> 2) & 3, u = lane & 3;
-    const int f = D >= 128 ? e : ((e >> 1) & 1);
+    const int e = (lane >> 2) & 3, u = lane & 3;
+    const int key = 8 * q4 + e, f = swz_vc_unit<D>(key);
 #pragma unroll
-    for (int dl = 0; dl < kTB; ++dl)
-      vtr[dl] = 4 * Cfg::kKHalfBytes + (8 * hh + e) * (2 * D) + 8 * (8 * (dl ^ f) + 4 * (G & 1) + u);
+    for (int cl = 0; cl < kTB; ++cl)
+      vtr[cl] = 4 * Cfg::kKHalfBytes + key * (2 * D) + 32 * (cl ^ f) + 8 * u;
   }
-  auto vfrag = [&](int buf, int db, int kk) {
+  auto vfrag = [&](int buf, int cb, int kb) {
     if constexpr (kCache) {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
       typedef short s16x8 __attribute__((ext_vector_type(8)));
-      char *p = lds + buf * Cfg::kVTileBytes + vtr[db % kTB] + (db / kTB) * 256 + 16 * kk * (2 * D);
+      char *p = lds + buf * Cfg::kVTileBytes + vtr[cb % kTB] + (cb / kTB) * 256 + 32 * kb * (2 * D);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4 *)p);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -368,7 +383,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     } else {
       return *reinterpret_cast<const bf16x8 *>(lds + buf * Cfg::kVTileBytes +
-                                               db * 32 * Cfg::kVRowBytes + voff[kk]);
+                                               cb * 16 * Cfg::kVRowBytes + voff[kb]);
     }
   };
 
@@ -387,118 +402,127 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   if (lane == 0) red4[w] = gmax;
   __syncthreads();
   gmax = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
-  float m_ref[kRB];
-  float negu[kRB];  // -U_t (0 for a row without keys), the S accumulators' start
-  auto neg_ref = [&](int rb) { return m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb]; };
-  // The 16-register start vector of an S accumulator, formed next to the
-  // MFMA that takes it: the empty asm makes the value opaque, so the compiler
-  // writes the 16 copies where they are used instead of keeping them live
-  // through the loop (16 registers per row block freed, which keeps the loop
-  // of the two-block variant free of register spills).
-  auto splat_ref = [&](int rb) {
-    float u = negu[rb];
+  float m_ref[kQB];
+  float negu[kQB];  // -U_t (0 for a row without keys), the S accumulators' start
+  auto neg_ref = [&](int qb) { return m_ref[qb] == -INFINITY ? 0.f : -m_ref[qb]; };
+  // The start vector of an S accumulator, formed next to the MFMA that takes
+  // it: the empty asm makes the value opaque, so the compiler writes the
+  // copies where they are used instead of keeping them live through the loop.
+  auto splat_ref = [&](int qb) {
+    float u = negu[qb];
     asm volatile("" : "+v"(u));
-    f32x16 r;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) r[e] = u;
-    return r;
+    return f32x4{u, u, u, u};
+  };
+  // the 4 lanes holding the same query (q4 = 0..3) combine their partials
+  auto quad_sum = [&](float x) {
+    x += __shfl_xor(x, 16, kWave);
+    return x + __shfl_xor(x, 32, kWave);
+  };
+  auto quad_max = [&](float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, kWave));
+    return fmaxf(x, __shfl_xor(x, 32, kWave));
   };
   bool bound_ok = true;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int qb = 0; qb < kQB; ++qb) {
     float qq = 0.f;
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float v = (float)qf[rb][ks][j];
+        const float v = (float)qf[qb][ks][j];
         qq = fmaf(v, v, qq);
       }
-    qq += __shfl_xor(qq, 32, kWave);
+    qq = quad_sum(qq);
     // 1% margin covers the bf16 rounding of the stored keys
-    m_ref[rb] = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f;
-    bound_ok = bound_ok && 2.f * m_ref[rb] <= 100.f;
-    negu[rb] = neg_ref(rb);
+    m_ref[qb] = sqrtf(qq) * sqrtf((float)D) * gmax * 1.01f;
+    bound_ok = bound_ok && 2.f * m_ref[qb] <= 100.f;
+    negu[qb] = neg_ref(qb);
   }
 
-  // Which logits of a 32-key half starting at key s0 are allowed (bit e of
-  // the result for element e); blocked ones become -inf. Allowed keys of this
-  // lane's row form one interval; relative to the lane's first key s0 + 8 hh,
-  // element e sits at the compile-time offset 16 (g >> 1) + 4 (g & 1) + r, so
-  // one unsigned compare per element tests lo <= offset <= hi.
-  auto mask_bits = [&](int s0, int rb) {
-    const int base = s0 + 8 * hh;
-    const int ta = a.q0 + my_t[rb];  // absolute index of the query
-    int hi = min(ta, len - 1) - base;
-    int lo = (a.local ? ta - a.window + 1 : -(1 << 30)) - base;
-    if (hi < lo) {  // nothing allowed
-      lo = 1 << 30;
-      hi = lo;
-    }
-    const uint32_t span = (uint32_t)(hi - lo);
+  // S of a 32-key half: 4 accumulators, quad qd = 2 qb + j (row block qb,
+  // sub-tile j); lane element r of quad qd is key 8 q4 + 4 j + r of the half.
+  using SHalf = f32x4[4];
+  // Which logits of a 32-key half starting at key s0 are allowed (bit 4 qd + r
+  // for element r of quad qd); blocked ones become -inf. Allowed keys of a
+  // row form one interval; relative to the lane's first key s0 + 8 q4, element
+  // r of sub-tile j sits at offset 4 j + r, so one unsigned compare per
+  // element tests lo <= offset <= hi.
+  auto mask_bits = [&](int s0) {
+    const int base = s0 + 8 * q4;
     uint32_t bits = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int g = e >> 2, r = e & 3;
-      const int off = 16 * (g >> 1) + 4 * (g & 1) + r;
-      bits |= ((uint32_t)(off - lo) <= span ? 1u : 0u) << e;
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int ta = a.q0 + my_t[qb];  // absolute index of the query
+      int hi = min(ta, len - 1) - base;
+      int lo = (a.local ? ta - a.window + 1 : -(1 << 30)) - base;
+      if (hi < lo) {  // nothing allowed
+        lo = 1 << 30;
+        hi = lo;
+      }
+      const uint32_t span = (uint32_t)(hi - lo);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bits |= ((uint32_t)(e - lo) <= span ? 1u : 0u) << (8 * qb + e);
     }
     return bits;
   };
-  auto mask_half = [&](f32x16 &sv, int s0, int rb) {
-    const uint32_t bits = mask_bits(s0, rb);
+  auto qk_half = [&](int slot, SHalf &sv, bool from_ref) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = (bits >> e) & 1 ? sv[e] : -INFINITY;
-  };
-  auto qk_half = [&](int slot, const f32x16 &init, int rb) {
-    f32x16 acc = init;
+    for (int qd = 0; qd < 4; ++qd) sv[qd] = from_ref ? splat_ref(qd >> 1) : f32x4{};
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(slot, ks), qf[rb][ks], acc, 0, 0, 0);
-    return acc;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 kf = kfrag(slot, j, ks);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          sv[2 * qb + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sv[2 * qb + j], 0, 0, 0);
+      }
   };
 
   // One step per 64-key tile it, as two 32-key halves (K halves u = 2 it and
   // 2 it + 1). While the softmax and PV of half u run, the S of half u + 1
   // goes to the matrix pipe. The work is a fixed sequence of groups of 4
-  // MFMAs: for each half, kNG groups of S MFMAs then kPG groups of PV MFMAs.
-  // The fragments of group i + 1 are read from LDS while group i runs (across
-  // the halves; only the tile's first group waits for its reads), each group
-  // carries its share of the softmax arithmetic, and the first half issues
-  // the tile's prefetches (K halves 2 it + 3, 2 it + 4 and V tile it + 1, into
-  // buffers last read before the previous barrier), a few per group.
-  // The code follows that order and the compiler schedules across it: fences
-  // that pinned it group by group (sched_group_barrier, written for one wave
-  // per SIMD) measured 1-1.5% slower on the global layers once two
-  // workgroups share each CU. par_tag: the parity of `it` when known at
-  // compile time (then every LDS slot and buffer index is an immediate), else -1.
+  // fragments (8 MFMAs, each fragment feeding both row blocks): for each
+  // half, kNG groups of S MFMAs then kPG groups of PV MFMAs. The fragments of
+  // group i + 1 are read from LDS while group i runs (across the halves; only
+  // the tile's first group waits for its reads), each group carries its
+  // share of the softmax arithmetic, and the first half issues the tile's
+  // prefetches (K halves 2 it + 3, 2 it + 4 and V tile it + 1, into buffers
+  // last read before the previous barrier), a few per group. A scheduling
+  // fence closes each group: scheduled across groups, the 16x16x32 form held
+  // more registers than the budget allows (spills at d_h = 128 and 256) and
+  // ran slower. par_tag: the parity of `it` when known at compile time (then
+  // every LDS slot and buffer index is an immediate), else -1.
   using Sc = TileSched<D>;
   constexpr int kG = Sc::kG, kNG = Sc::kNG, kNGT = Sc::kNGT, kPieces = Sc::kPieces, kPPG = Sc::kPPG;
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  auto tile_step = [&](auto masked_tag, auto next_tag, auto par_tag, int it,
-                       f32x16 (&s_a)[kRB], f32x16 (&s_b)[kRB]) {
+  auto tile_step = [&](auto masked_tag, auto next_tag, auto par_tag, int it, SHalf &s_a,
+                       SHalf &s_b) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;  // S of half 2 it + 2 is needed
     constexpr int kPar = decltype(par_tag)::value;
     const int par = kPar >= 0 ? kPar : (it & 1);
     const int s_tile = my_begin + it * kBN;
 
-    // fragments of group gi of the tile (4 of them)
+    // fragments of group gi of the tile (4 of them): S group gl, fragment j
+    // is K sub-tile (4 gl + j) % 2 at k-step (4 gl + j) / 2; PV group gl,
+    // fragment j is channel block 4 (gl - kNG) + j
     auto read_frags = [&](auto gi_tag, bf16x8 (&fr)[4]) {
       constexpr int gi = decltype(gi_tag)::value;
       constexpr int kb = gi / kNGT, gl = gi % kNGT;
       if constexpr (gl < kNG) {
         if constexpr (kb == 0 || kNext) {
 #pragma unroll
-          for (int j = 0; j < kG; ++j) fr[j] = kfrag((2 * par + kb + 1) & 3, gl * kG + j);
+          for (int j = 0; j < kG; ++j) {
+            const int f = gl * kG + j;
+            fr[j] = kfrag((2 * par + kb + 1) & 3, f & 1, f >> 1);
+          }
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = 4 * (gl - kNG) + j;  // PV MFMA m: channel block m % kDB, keys 16 (m / kDB) +
-          fr[j] = vfrag(par, m % Cfg::kDB, 2 * kb + m / Cfg::kDB);
-        }
+        for (int j = 0; j < kG; ++j) fr[j] = vfrag(par, kG * (gl - kNG) + j, kb);
       }
     };
     auto issue_piece = [&](int pc) {
@@ -510,76 +534,70 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         issue_v_piece(it + 1, par ^ 1, pc - 2 * Cfg::kKHalfLoads);
     };
 
-    float ex[kRB][16];
-    bf16x8 pf[kRB][2];
-    float psum[kRB][4];
+    float ex[16];
+    bf16x8 pf[kQB];
+    float psum[4];
     bf16x8 fr[4], frn[4];
     // masked tiles: allowed-logit bits of the current half (applied as the
     // exponentials read the S accumulators)
-    uint32_t mb[kRB];
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) mb[rb] = kMasked ? mask_bits(s_tile, rb) : 0xFFFFu;
+    uint32_t mb = kMasked ? mask_bits(s_tile) : 0xFFFFu;
     read_frags(std::integral_constant<int, 0>{}, fr);
     static_for<2 * kNGT>([&](auto g_tag) {
       constexpr int gi = decltype(g_tag)::value;
       constexpr int kb = gi / kNGT, g = gi % kNGT;
       constexpr bool kS = g < kNG;
       constexpr bool kSActive = kS && (kb == 0 || kNext);
-      f32x16(&s_cur)[kRB] = kb == 0 ? s_a : s_b;
-      f32x16(&s_nxt)[kRB] = kb == 0 ? s_b : s_a;
+      SHalf &s_cur = kb == 0 ? s_a : s_b;
+      SHalf &s_nxt = kb == 0 ? s_b : s_a;
       if constexpr (g == 0) {
+        if (kb == 1 && kMasked) mb = mask_bits(s_tile + 32);
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
-          if (kb == 1 && kMasked) mb[rb] = mask_bits(s_tile + 32, rb);
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) psum[rb][qd] = 0.f;
-        }
+        for (int qd = 0; qd < 4; ++qd) psum[qd] = 0.f;
       }
       if constexpr (gi + 1 < 2 * kNGT) read_frags(std::integral_constant<int, gi + 1>{}, frn);
-      // LDS read instructions of the next group (a cache-mode V fragment takes two)
-      constexpr bool kNextS = (gi + 1) % kNGT < kNG;
       if constexpr (kSActive) {
 #pragma unroll
-        for (int j = 0; j < kG; ++j)
+        for (int j = 0; j < kG; ++j) {
+          constexpr int f0 = g * kG;
+          const int f = f0 + j, sj = f & 1, ks = f >> 1;
 #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb)
-            s_nxt[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                fr[j], qf[rb][g * kG + j], (g == 0 && j == 0) ? splat_ref(rb) : s_nxt[rb], 0, 0, 0);
+          for (int qb = 0; qb < kQB; ++qb)
+            s_nxt[2 * qb + sj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                fr[j], qf[qb][ks], ks == 0 ? splat_ref(qb) : s_nxt[2 * qb + sj], 0, 0, 0);
+        }
       } else if constexpr (!kS) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = 4 * (g - kNG) + j;
+        for (int j = 0; j < kG; ++j) {
+          const int cb = kG * (g - kNG) + j;
 #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb)
-            acc_o[rb][m % Cfg::kDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                fr[j], pf[rb][m / Cfg::kDB], acc_o[rb][m % Cfg::kDB], 0, 0, 0);
+          for (int qb = 0; qb < kQB; ++qb)
+            acc_o[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j], pf[qb], acc_o[qb][cb],
+                                                                   0, 0, 0);
         }
       }
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
+      for (int qd = 0; qd < 4; ++qd) {
+        if (Sc::e_grp(qd) == g) {
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          if (Sc::e_grp(qd) == g) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float x = s_cur[rb][4 * qd + i];
-              ex[rb][4 * qd + i] =
-                  __builtin_amdgcn_exp2f(!kMasked || ((mb[rb] >> (4 * qd + i)) & 1) ? x : -INFINITY);
-            }
-          }
-          if (Sc::c_grp(qd) == g) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pf[rb][qd >> 1][4 * (qd & 1) + i] = (bf16)ex[rb][4 * qd + i];
-          }
-          if (Sc::d_grp(qd) == g) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-              const bf16x2 pr = {pf[rb][qd >> 1][4 * (qd & 1) + 2 * i],
-                                 pf[rb][qd >> 1][4 * (qd & 1) + 2 * i + 1]};
-              psum[rb][qd] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[rb][qd], false);
-            }
+          for (int i = 0; i < 4; ++i) {
+            const float x = s_cur[qd][i];
+            ex[4 * qd + i] =
+                __builtin_amdgcn_exp2f(!kMasked || ((mb >> (4 * qd + i)) & 1) ? x : -INFINITY);
           }
         }
+        if (Sc::c_grp(qd) == g) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pf[qd >> 1][4 * (qd & 1) + i] = (bf16)ex[4 * qd + i];
+        }
+        if (Sc::d_grp(qd) == g) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const bf16x2 pr = {pf[qd >> 1][4 * (qd & 1) + 2 * i],
+                               pf[qd >> 1][4 * (qd & 1) + 2 * i + 1]};
+            psum[qd] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[qd], false);
+          }
+        }
+      }
       if constexpr (kb == 0) {
 #pragma unroll
         for (int i = 0; i < kPPG; ++i)
@@ -587,13 +605,13 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       }
       if constexpr (g == kNGT - 1) {
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb)
-          l_run[rb] += (psum[rb][0] + psum[rb][1]) + (psum[rb][2] + psum[rb][3]);
+        for (int qb = 0; qb < kQB; ++qb) l_run[qb] += psum[2 * qb] + psum[2 * qb + 1];
       }
       if constexpr (gi + 1 < 2 * kNGT) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) fr[j] = frn[j];
       }
+      __builtin_amdgcn_sched_barrier(0);
     });
     publish_tiles();  // this tile's prefetches have landed
   };
@@ -610,10 +628,10 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (hi_s0 >= my_begin) it_hi = (hi_s0 - my_begin) / kBN;
     if (lo_s0 > my_begin) it_lo = div_up(lo_s0 - my_begin, kBN);
   }
-  auto run = [&](f32x16 (&s_a)[kRB]) {
+  auto run = [&](SHalf &s_a) {
     using T_ = std::true_type;
     using F_ = std::false_type;
-    f32x16 s_b[kRB];
+    SHalf s_b;
     using PR = std::integral_constant<int, -1>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
@@ -643,15 +661,19 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
   // S of K half 0; the barrier after it orders these reads before any later
   // write to slot 0
-  f32x16 s0_first[kRB];
+  SHalf s0_first;
+  if (n_tiles > 0) {
+    qk_half(0, s0_first, true);
+  } else {
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) s0_first[rb] = n_tiles > 0 ? qk_half(0, splat_ref(rb), rb) : f32x16{};
+    for (int qd = 0; qd < 4; ++qd) s0_first[qd] = f32x4{};
+  }
   if (!__syncthreads_and(bound_ok) || force_exact_max) {
     // Exact row maxima (log2 units) over the allowed keys: each tile's two K
     // halves go to slots 0 and 1, S MFMAs only. Rare; kept simple.
-    float mx[kRB];
+    float mx[kQB];
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) mx[rb] = -INFINITY;
+    for (int qb = 0; qb < kQB; ++qb) mx[qb] = -INFINITY;
     for (int it = 0; it < n_tiles; ++it) {
 #pragma unroll
       for (int kbh = 0; kbh < 2; ++kbh)
@@ -659,71 +681,68 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int i = 0; i < Cfg::kKHalfLoads; ++i) issue_k_piece(it, kbh, kbh, i);
       publish_tiles();
 #pragma unroll
-      for (int kbh = 0; kbh < 2; ++kbh)
+      for (int kbh = 0; kbh < 2; ++kbh) {
+        SHalf sv;
+        qk_half(kbh, sv, false);
+        const uint32_t bits = mask_bits(my_begin + it * kBN + 32 * kbh);
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
-          f32x16 sv = qk_half(kbh, f32x16{}, rb);
-          mask_half(sv, my_begin + it * kBN + 32 * kbh, rb);
+        for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx[rb] = fmaxf(mx[rb], sv[e]);
-        }
+          for (int r = 0; r < 4; ++r)
+            mx[qd >> 1] = fmaxf(mx[qd >> 1], (bits >> (4 * qd + r)) & 1 ? sv[qd][r] : -INFINITY);
+      }
       __syncthreads();  // reads done before the next tile overwrites the slots
     }
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      m_ref[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32, kWave));
-      negu[rb] = neg_ref(rb);
+    for (int qb = 0; qb < kQB; ++qb) {
+      m_ref[qb] = quad_max(mx[qb]);
+      negu[qb] = neg_ref(qb);
     }
     issue_prologue();
     publish_tiles();
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
-      s0_first[rb] = n_tiles > 0 ? qk_half(0, splat_ref(rb), rb) : f32x16{};
+    if (n_tiles > 0) qk_half(0, s0_first, true);
     __syncthreads();
   }
   run(s0_first);
 
   // Normalise; write the output rows (single chunk) or partials (several
   // chunks). The K/V buffers are free after the last tile's barrier: each wave
-  // stages a 32-row block (bf16, a 16-byte pad per row) in a region of its
-  // own, then writes it back as whole rows of 16-byte pieces. A lane holds
-  // channels 32 db + 8 g + 4 hh + [0, 4) of its row.
+  // stages its 32 rows (bf16, a 16-byte pad per row) in a region of its own,
+  // then writes them back as whole rows of 16-byte pieces. A lane holds
+  // channels 16 cb + 4 q4 + [0, 4) of row 16 qb + qc.
   constexpr int kPitch = 2 * D + 16;
   static_assert(4 * 32 * kPitch <= Cfg::kLdsBytes, "output staging fits the tile buffers");
   char *stage = lds + w * 32 * kPitch;
   constexpr int kPieces16 = D / 8;  // 16-byte pieces per row
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, kWave);
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float l_tot = quad_sum(l_run[qb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-    for (int db = 0; db < Cfg::kDB; ++db)
+    for (int cb = 0; cb < Cfg::kCB; ++cb) {
+      bf16x4 v;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc_o[rb][db][4 * g + r] * inv);
-        *reinterpret_cast<bf16x4 *>(stage + col * kPitch + 2 * (32 * db + 8 * g + 4 * hh)) = v;
-      }
-    if (geo.n_active > 1 && hh == 0 && my_t[rb] < a.T) {
-      const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t[rb];
-      part_ml[2 * row] = m_ref[rb];
+      for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc_o[qb][cb][r] * inv);
+      *reinterpret_cast<bf16x4 *>(stage + (16 * qb + qc) * kPitch + 2 * (16 * cb + 4 * q4)) = v;
+    }
+    if (geo.n_active > 1 && q4 == 0 && my_t[qb] < a.T) {
+      const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t[qb];
+      part_ml[2 * row] = m_ref[qb];
       part_ml[2 * row + 1] = l_tot;
     }
-    // the same wave reads its region back (LDS keeps a wave's accesses in
-    // order), and the next block's writes come after these reads
+  }
+  // the same wave reads its region back (LDS keeps a wave's accesses in order)
 #pragma unroll
-    for (int i = 0; i < 32 * kPieces16 / kWave; ++i) {
-      const int item = i * kWave + lane;
-      const int r = item / kPieces16, c = item % kPieces16;
-      const int t = wq0 + 32 * rb + r;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + 16 * c);
-      if (t >= a.T) continue;
-      bf16 *dst = geo.n_active == 1
-                      ? o + ((size_t)b * a.T + t) * ((size_t)a.H * D) + (size_t)h * D
-                      : part_o + ((((size_t)split * a.B + b) * a.H + h) * a.T + t) * D;
-      *reinterpret_cast<u32x4 *>(dst + 8 * c) = v;
-    }
+  for (int i = 0; i < 32 * kPieces16 / kWave; ++i) {
+    const int item = i * kWave + lane;
+    const int r = item / kPieces16, c = item % kPieces16;
+    const int t = wq0 + r;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + 16 * c);
+    if (t >= a.T) continue;
+    bf16 *dst = geo.n_active == 1
+                    ? o + ((size_t)b * a.T + t) * ((size_t)a.H * D) + (size_t)h * D
+                    : part_o + ((((size_t)split * a.B + b) * a.H + h) * a.T + t) * D;
+    *reinterpret_cast<u32x4 *>(dst + 8 * c) = v;
   }
 }
 
@@ -804,7 +823,7 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
 }
 
 struct Plan {
-  int rb, gp, n_qtiles, n_hgrp, n_split, chunk_keys, remap;
+  int gp, n_qtiles, n_hgrp, n_split, chunk_keys, remap;
   long n_base;
 };
 
@@ -823,9 +842,8 @@ Plan plan(const AttnArgs &a) {
   const int G = a.H / a.Hk;
   p.gp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   // (a window covering every key takes the global layer's plan and bits)
-  p.rb = 1;
   const int slots = kCUs * wgs_per_cu(a.d_h);  // workgroups running at once
-  const int TQ = 32 * p.rb * (4 / p.gp);
+  const int TQ = 16 * kQB * (4 / p.gp);
   p.n_qtiles = div_up_h(a.T, TQ);
   p.n_hgrp = G / p.gp;
   const long n_groups = (long)a.B * a.Hk * p.n_hgrp;
@@ -870,12 +888,12 @@ Plan plan(const AttnArgs &a) {
   return p;
 }
 
-template <int D, int RB, bool kCache>
-hipError_t launch_rb(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
+template <int D, bool kCache>
+hipError_t launch_kernels(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
                      const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml,
                      const AttnArgs &a, const Plan &p, int force, hipStream_t s) {
   using Cfg = AttnCfg<D>;
-  auto kern = flash_attn_fwd_bf16<D, RB, kCache>;
+  auto kern = flash_attn_fwd_bf16<D, kCache>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
@@ -888,7 +906,7 @@ hipError_t launch_rb(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t
   hipLaunchKernelGGL(flash_combine<D>, dim3((unsigned)p.n_base, kCombineSlices), dim3(256), 0, s,
                      kv_len,
                      o, part_o, part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys,
-                     32 * RB);
+                     16 * kQB);
   return hipGetLastError();
 }
 
@@ -896,10 +914,10 @@ template <int D>
 hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
                     const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
                     int force, hipStream_t s) {
-  const Plan p = plan(a);  // p.rb == 1
+  const Plan p = plan(a);
   if (a.S_cache > 0)
-    return launch_rb<D, 1, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
-  return launch_rb<D, 1, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+    return launch_kernels<D, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+  return launch_kernels<D, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
 }
 
 }  // namespace
