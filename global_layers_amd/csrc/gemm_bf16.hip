@@ -391,6 +391,69 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
   // barrier: a load landing after the barrier would overwrite staged rows.
   auto drain_loads = [&]() { __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm); };
 
+  // Ping-pong schedule (two tile rows of waves, two stages): the waves of
+  // tile row wm = 0 (one per SIMD) and those of wm = 1 alternate between a
+  // memory phase (every fragment of a slice read from LDS, their share of a
+  // later slice's direct loads issued) and a compute phase (the slice's
+  // MFMAs on registers only), one phase apart, handing over at workgroup
+  // barriers, so each SIMD has one wave issuing MFMAs while its other wave
+  // waits on memory (measured 1-1.5% faster than both waves interleaving
+  // reads and MFMAs in step).
+  //
+  // Barrier j ends interval j. Group 0 reads slice k in interval 2k and
+  // multiplies in 2k + 1; group 1 reads it in 2k + 1 and multiplies in
+  // 2k + 2 (it enters the loop one barrier later, group 0 passes one extra
+  // barrier after it, so both pass the same number). Both issue slice k + 1
+  // in interval 2k (group 0 in its memory phase, group 1 among its MFMAs)
+  // into the stage slice k - 1 used, which both groups finished reading
+  // (each waits for its own reads before the barrier that ends its memory
+  // phase) before barrier 2k; every wave waits for its own loads of slice
+  // k + 1 before the even barrier 2k + 2 after which group 0 reads it.
+  constexpr bool kPingPong = WM == 2 && NST == 2;
+  if constexpr (kPingPong) {
+    const int grp = __builtin_amdgcn_readfirstlane(wm);  // wave-uniform: barriers sit in its branches
+    bf16x8 fa[kKK][Cfg::kFM], fb[kKK][Cfg::kFN];
+    auto mem_phase = [&](int st) {
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) read_frags(st, kk, fa[kk], fb[kk]);
+    };
+    auto compute_phase = [&]() {
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk)
+#pragma unroll
+        for (int i = 0; i < Cfg::kFM; ++i)
+#pragma unroll
+          for (int j = 0; j < Cfg::kFN; ++j) acc[i][j] = Mf::mma(fb[kk][j], fa[kk][i], acc[i][j]);
+    };
+    constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0), vmcnt and expcnt unconstrained
+    auto barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm);  // slice 0 (issued above by every wave)
+    barrier();                                     // B0
+    if (grp == 1) {
+      if (1 < nk) issue(1, 1);
+      barrier();  // B1
+    }
+    for (int k = 0; k < nk; ++k) {
+      const int st = k & 1;
+      mem_phase(st);
+      if (grp == 0) {
+        if (k + 1 < nk) issue(k + 1, st ^ 1);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      } else {
+        __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm & ~(0xF << 8));  // lgkmcnt(0), vmcnt(0)
+      }
+      barrier();  // group 0: B(2k+1), group 1: B(2k+2)
+      if (grp == 1 && k + 2 < nk) issue(k + 2, st);
+      compute_phase();
+      if (grp == 0) __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm);
+      barrier();  // group 0: B(2k+2), group 1: B(2k+3)
+    }
+    if (grp == 0) barrier();  // B(2nk+1)
+  } else {
   for (int kt = 0; kt < nk; ++kt) {
     // k-tile kt has landed for every wave; the MFMAs of the previous slice's
     // last step are still in the pipe while this slice's first reads go out
@@ -413,6 +476,7 @@ gemm_bf16_nt(const bf16 *__restrict__ A, const bf16 *__restrict__ B0, const bf16
       __builtin_amdgcn_sched_group_barrier(0x008, Cfg::kFM * Cfg::kFN, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
   }
   static_assert(kKK % 2 == 0, "step 0 of every slice reads into buffer 0");
 
