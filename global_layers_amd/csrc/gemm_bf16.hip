@@ -4,12 +4,13 @@
 // B an output-major weight, accumulated in fp32.
 //
 //  * gemm_bf16_nt: prefill. Block tile BM x BN, K in slices of BK, waves
-//    arranged WM x WN, 32x32x16 bf16 MFMAs. Slices move global -> LDS with
-//    direct loads (no staging registers) into NST stages, several slices ahead
-//    of the MFMAs; each slice waits only for its own loads (explicit vmcnt)
-//    before the barrier. The MFMA is issued with the weight fragment as its
-//    first operand so that each lane ends up holding 4 consecutive output
-//    columns (one 8-byte store).
+//    arranged WM x WN, 16x16x32 bf16 MFMAs (32x32x16 selectable). Slices move
+//    global -> LDS with direct loads (no staging registers) into NST stages,
+//    ahead of the MFMAs; each slice waits only for its own loads (explicit
+//    vmcnt) before the barrier; the 256x256 tile alternates its two rows of
+//    waves between memory and MFMA phases (ping-pong). The MFMA is issued
+//    with the weight fragment as its first operand so that each lane ends up
+//    holding 4 consecutive output columns (one 8-byte store).
 //  * gemv16_bf16_wg: decode (M = batch <= 16 per M block). Weight-streaming
 //    16x16x32 MFMAs, each workgroup one or two 16-column blocks over the whole
 //    K range split among its 8 waves, added through LDS; fp32 or bf16 output.
