@@ -4,7 +4,11 @@ both dtypes, every head size with kernels, random RoPE (theta, scale), and
 the query scales the model uses (d_h^-1/2 or (D/H)^-1/2; D >= H d_h as in the
 workloads). Each case is compared element by element with the fp64 oracle
 (bf16: 2e-2 + 1e-2 |ref|, fp32: 1e-4). The shapes are drawn once from a fixed
-seed, so the sweep is the same on every run."""
+seed, so the sweep is the same on every run. GEMMA3_SWEEP_SCALE=k draws k
+times as many cases of each kind and GEMMA3_SWEEP_SEED=s shifts the seeds,
+for an extended run (the default run keeps both at 1 and 0)."""
+
+import os
 
 import numpy as np
 import pytest
@@ -19,6 +23,8 @@ import oracle as O
 pytestmark = pytest.mark.gpu
 
 L, G = "LOCAL_SLIDING", "GLOBAL"
+SCALE = int(os.environ.get("GEMMA3_SWEEP_SCALE", "1"))
+SEED = int(os.environ.get("GEMMA3_SWEEP_SEED", "0"))
 
 
 def _prefill_cases(n=16, seed=2026):
@@ -50,7 +56,7 @@ def _prefill_cases(n=16, seed=2026):
     return cases
 
 
-PREFILL = _prefill_cases()
+PREFILL = _prefill_cases(16 * SCALE, 2026 + SEED)
 
 
 @pytest.mark.parametrize("case", PREFILL, ids=[f"p{i}" for i in range(len(PREFILL))])
@@ -94,7 +100,7 @@ def _narrow_cases(n=6, seed=2028):
     return cases
 
 
-NARROW = _narrow_cases()
+NARROW = _narrow_cases(6 * SCALE, 2028 + SEED)
 
 
 @pytest.mark.parametrize("case", NARROW, ids=[f"n{i}" for i in range(len(NARROW))])
@@ -131,7 +137,7 @@ def _decode_cases(n=8, seed=2027):
     return cases
 
 
-DECODE = _decode_cases()
+DECODE = _decode_cases(8 * SCALE, 2027 + SEED)
 
 
 @pytest.mark.parametrize("case", DECODE, ids=[f"d{i}" for i in range(len(DECODE))])
