@@ -258,7 +258,9 @@ int prefill_impl(const gemma3_attn_desc *d, const void *x, const int32_t *pos,
       RUN(launch_flash_attn_bf16((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, kv_len,
                                  (const bf16 *)w->gamma_k, (bf16 *)o,
                                  L.attn_part ? base + L.attn_part : nullptr, a,
-                                 (stages & GEMMA3_STAGE_FORCE_EXACT_MAX) != 0, s));
+                                 ((stages & GEMMA3_STAGE_FORCE_EXACT_MAX) ? kRefExactMax : 0) |
+                                     ((stages & GEMMA3_STAGE_FORCE_BOUND_REF) ? kRefNoZero : 0),
+                                 s));
     else
       RUN(launch_attn_f32((const float *)q, (const float *)k, (const float *)vt, kv_len,
                           (float *)o, a, s));
@@ -536,7 +538,7 @@ int gemma3_attn_prefill_chunk(const gemma3_attn_desc *desc, const void *x,
     RUN(launch_flash_attn_bf16((const bf16 *)(base + L.q), (const bf16 *)k_cache,
                                (const bf16 *)v_cache, kv_valid_len, (const bf16 *)w->gamma_k,
                                (bf16 *)(base + L.o), C.part < C.total ? base + C.part : nullptr,
-                               a, false, s));
+                               a, 0, s));
     return prefill_impl<bf16>(desc, x, segment_pos, kv_valid_len, w, y, workspace, L, s,
                               GEMMA3_STAGE_OUT_PROJ);
   }

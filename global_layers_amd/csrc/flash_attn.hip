@@ -180,7 +180,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ gamma_k, bf16 *__restrict__ o,
                     bf16 *__restrict__ part_o, float *__restrict__ part_ml, AttnArgs a, int gp,
                     int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int remap,
-                    int force_exact_max) {
+                    int ref_flags) {
   using Cfg = AttnCfg<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -439,6 +439,23 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     bound_ok = bound_ok && 2.f * m_ref[qb] <= 100.f;
     negu[qb] = neg_ref(qb);
   }
+  // Zero reference: when U_t <= kZeroRefMax for every row of the wave, the
+  // weights are taken as p = 2^x without any shift. They then lie in
+  // [2^-kZeroRefMax, 2^kZeroRefMax] (|x| <= U_t), so neither p, l nor O can
+  // overflow or lose their scale (O would need |V| > 2^(128 - kZeroRefMax - 17)
+  // over 2^17 keys), and the S accumulators of the full tiles start from the
+  // MFMA's inline zero instead of a per-row splat that costs four moves per
+  // accumulator. The choice is per wave (every row of a wave takes the same
+  // code path); the reference of its rows is 0 then, which the split-KV merge
+  // sees in (m, l).
+  constexpr float kZeroRefMax = 40.f;
+  // d_h = 256 keeps a single copy of the tile loop: there the second copy
+  // cost more in spilled registers than the moves it saves.
+  constexpr bool kZeroRefCopy = D <= 128;
+  bool zero_ok = (ref_flags & (kRefExactMax | kRefNoZero)) == 0;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) zero_ok = zero_ok && m_ref[qb] <= kZeroRefMax;
+  bool zero_ref = kZeroRefCopy && __all(zero_ok);
 
   // S of a 32-key half: 4 accumulators, quad qd = 2 qb + j (row block qb,
   // sub-tile j); lane element r of quad qd is key 8 q4 + 4 j + r of the half.
@@ -498,9 +515,10 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int kG = Sc::kG, kNG = Sc::kNG, kNGT = Sc::kNGT, kPieces = Sc::kPieces, kPPG = Sc::kPPG;
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  auto tile_step = [&](auto masked_tag, auto next_tag, auto par_tag, int it, SHalf &s_a,
-                       SHalf &s_b) {
+  auto tile_step = [&](auto masked_tag, auto next_tag, auto par_tag, auto zero_tag, int it,
+                       SHalf &s_a, SHalf &s_b) {
     constexpr bool kMasked = decltype(masked_tag)::value;
+    constexpr bool kZero = decltype(zero_tag)::value;  // S accumulators start at 0
     constexpr bool kNext = decltype(next_tag)::value;  // S of half 2 it + 2 is needed
     constexpr int kPar = decltype(par_tag)::value;
     const int par = kPar >= 0 ? kPar : (it & 1);
@@ -536,7 +554,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
     float ex[16];
     bf16x8 pf[kQB];
-    float psum[4];
     bf16x8 fr[4], frn[4];
     // masked tiles: allowed-logit bits of the current half (applied as the
     // exponentials read the S accumulators)
@@ -551,8 +568,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       SHalf &s_nxt = kb == 0 ? s_b : s_a;
       if constexpr (g == 0) {
         if (kb == 1 && kMasked) mb = mask_bits(s_tile + 32);
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) psum[qd] = 0.f;
       }
       if constexpr (gi + 1 < 2 * kNGT) read_frags(std::integral_constant<int, gi + 1>{}, frn);
       if constexpr (kSActive) {
@@ -563,7 +578,8 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb)
             s_nxt[2 * qb + sj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                fr[j], qf[qb][ks], ks == 0 ? splat_ref(qb) : s_nxt[2 * qb + sj], 0, 0, 0);
+                fr[j], qf[qb][ks],
+                ks == 0 ? (kZero ? f32x4{} : splat_ref(qb)) : s_nxt[2 * qb + sj], 0, 0, 0);
         }
       } else if constexpr (!kS) {
 #pragma unroll
@@ -594,7 +610,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int i = 0; i < 2; ++i) {
             const bf16x2 pr = {pf[qd >> 1][4 * (qd & 1) + 2 * i],
                                pf[qd >> 1][4 * (qd & 1) + 2 * i + 1]};
-            psum[qd] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[qd], false);
+            l_run[qd >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qd >> 1], false);
           }
         }
       }
@@ -602,10 +618,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int i = 0; i < kPPG; ++i)
           if (g * kPPG + i < kPieces) issue_piece(g * kPPG + i);
-      }
-      if constexpr (g == kNGT - 1) {
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) l_run[qb] += psum[2 * qb] + psum[2 * qb + 1];
       }
       if constexpr (gi + 1 < 2 * kNGT) {
 #pragma unroll
@@ -628,18 +640,20 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (hi_s0 >= my_begin) it_hi = (hi_s0 - my_begin) / kBN;
     if (lo_s0 > my_begin) it_lo = div_up(lo_s0 - my_begin, kBN);
   }
-  auto run = [&](SHalf &s_a) {
+  auto run = [&](auto zero_tag, SHalf &s_a) {
     using T_ = std::true_type;
     using F_ = std::false_type;
     SHalf s_b;
     using PR = std::integral_constant<int, -1>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // Masked tiles always form the S of the next half (one code copy, fewer
-    // registers); after the last tile that reads a K slot holding a clamped
-    // copy of the last tile, and the result is unused.
-    auto masked_tile = [&](int it) { tile_step(T_{}, T_{}, PR{}, it, s_a, s_b); };
-    auto full_tile = [&](auto par_tag, int it) { tile_step(F_{}, T_{}, par_tag, it, s_a, s_b); };
+    // Masked tiles always form the S of the next half (one code copy per
+    // reference mode, fewer registers); after the last tile that reads a K
+    // slot holding a clamped copy of the last tile, and the result is unused.
+    auto masked_tile = [&](int it) { tile_step(T_{}, T_{}, PR{}, zero_tag, it, s_a, s_b); };
+    auto full_tile = [&](auto par_tag, int it) {
+      tile_step(F_{}, T_{}, par_tag, zero_tag, it, s_a, s_b);
+    };
     const int head_end = min(it_lo, n_tiles);
     const int full_end = min(it_hi + 1, n_tiles - 1);
     // One masked loop (one copy of its code): the head segment, then the full
@@ -663,12 +677,12 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // write to slot 0
   SHalf s0_first;
   if (n_tiles > 0) {
-    qk_half(0, s0_first, true);
+    qk_half(0, s0_first, !zero_ref);
   } else {
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) s0_first[qd] = f32x4{};
   }
-  if (!__syncthreads_and(bound_ok) || force_exact_max) {
+  if (!__syncthreads_and(bound_ok) || (ref_flags & kRefExactMax)) {
     // Exact row maxima (log2 units) over the allowed keys: each tile's two K
     // halves go to slots 0 and 1, S MFMAs only. Rare; kept simple.
     float mx[kQB];
@@ -698,12 +712,22 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       m_ref[qb] = quad_max(mx[qb]);
       negu[qb] = neg_ref(qb);
     }
+    zero_ref = false;
     issue_prologue();
     publish_tiles();
     if (n_tiles > 0) qk_half(0, s0_first, true);
     __syncthreads();
   }
-  run(s0_first);
+  bool ran = false;
+  if constexpr (kZeroRefCopy) {
+    if (zero_ref) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) m_ref[qb] = 0.f;
+      run(std::true_type{}, s0_first);
+      ran = true;
+    }
+  }
+  if (!ran) run(std::false_type{}, s0_first);
 
   // Normalise; write the output rows (single chunk) or partials (several
   // chunks). The K/V buffers are free after the last tile's barrier: each wave
@@ -891,7 +915,7 @@ Plan plan(const AttnArgs &a) {
 template <int D, bool kCache>
 hipError_t launch_kernels(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
                      const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml,
-                     const AttnArgs &a, const Plan &p, int force, hipStream_t s) {
+                     const AttnArgs &a, const Plan &p, int ref_flags, hipStream_t s) {
   using Cfg = AttnCfg<D>;
   auto kern = flash_attn_fwd_bf16<D, kCache>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -900,7 +924,7 @@ hipError_t launch_kernels(const bf16 *q, const bf16 *k, const bf16 *vt, const in
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.n_base * p.n_split)),
                      dim3(kThreads), Cfg::kLdsBytes, s, q, k, vt, kv_len, gamma_k, o, part_o,
                      part_ml, a, p.gp, p.n_qtiles, p.n_hgrp, p.n_split, p.chunk_keys, p.remap,
-                     force);
+                     ref_flags);
   e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   hipLaunchKernelGGL(flash_combine<D>, dim3((unsigned)p.n_base, kCombineSlices), dim3(256), 0, s,
@@ -913,11 +937,13 @@ hipError_t launch_kernels(const bf16 *q, const bf16 *k, const bf16 *vt, const in
 template <int D>
 hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
                     const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
-                    int force, hipStream_t s) {
+                    int ref_flags, hipStream_t s) {
   const Plan p = plan(a);
   if (a.S_cache > 0)
-    return launch_kernels<D, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
-  return launch_kernels<D, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, force, s);
+    return launch_kernels<D, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p,
+                                   ref_flags, s);
+  return launch_kernels<D, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, ref_flags,
+                                  s);
 }
 
 }  // namespace
@@ -938,16 +964,15 @@ size_t flash_attn_partial_bytes_bound(const AttnArgs &a) {
 
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
                                   const int32_t *kv_len, const bf16 *gamma_k, bf16 *o,
-                                  void *partial, const AttnArgs &a, bool force_exact_max,
+                                  void *partial, const AttnArgs &a, int ref_flags,
                                   hipStream_t s) {
-  const int force = force_exact_max ? 1 : 0;
   const size_t rows = (size_t)plan(a).n_split * a.B * a.H * a.T;
   bf16 *part_o = (bf16 *)partial;
   float *part_ml = partial ? (float *)((char *)partial + rows * a.d_h * 2) : nullptr;
   switch (a.d_h) {
-    case 64: return launch_d<64>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, force, s);
-    case 128: return launch_d<128>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, force, s);
-    case 256: return launch_d<256>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, force, s);
+    case 64: return launch_d<64>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, ref_flags, s);
+    case 128: return launch_d<128>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, ref_flags, s);
+    case 256: return launch_d<256>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, ref_flags, s);
     default: return hipErrorInvalidValue;
   }
 }

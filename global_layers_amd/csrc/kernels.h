@@ -82,11 +82,13 @@ struct AttnArgs {
 size_t flash_attn_partial_bytes(const AttnArgs &a);
 size_t flash_attn_partial_bytes_bound(const AttnArgs &a);
 // gamma_k [d_h] bounds the key norms (fixed softmax reference).
-// force_exact_max: every workgroup takes the exact-row-maximum pass that
-// normally runs only where the logit bound is too loose.
+// ref_flags (diagnostics, normally 0): kRefExactMax makes every workgroup
+// take the exact-row-maximum pass that normally runs only where the logit
+// bound is too loose; kRefNoZero keeps every wave off the zero reference.
+constexpr int kRefExactMax = 1, kRefNoZero = 2;
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
                                   const int32_t *kv_len, const bf16 *gamma_k, bf16 *o,
-                                  void *partial, const AttnArgs &a, bool force_exact_max,
+                                  void *partial, const AttnArgs &a, int ref_flags,
                                   hipStream_t s);
 
 // K4 + K4c (decode attention): split-KV partials then combine into o [B, H*d_h].

@@ -35,6 +35,7 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_WINDOW", 4: "ERR_DTYPE
 
 STAGE_QKV_PROJ, STAGE_QK_NORM, STAGE_ATTN, STAGE_OUT_PROJ, STAGE_ALL = 1, 2, 4, 8, 15
 STAGE_FORCE_EXACT_MAX = 16  # diagnostic: attention takes the exact-row-maximum pass
+STAGE_FORCE_BOUND_REF = 32  # diagnostic: attention never takes the zero reference
 DSTAGE_QKV_PROJ, DSTAGE_QK_NORM, DSTAGE_ATTN, DSTAGE_OUT_PROJ, DSTAGE_ALL = 1, 2, 4, 8, 15
 
 _ATTN_TYPES = {"GLOBAL": GLOBAL, "LOCAL_SLIDING": LOCAL_SLIDING, GLOBAL: GLOBAL,

@@ -30,6 +30,11 @@ extern "C" {
  * large for a fixed reference), so tests can check that path on ordinary
  * inputs. Same results up to rounding. */
 #define GEMMA3_STAGE_FORCE_EXACT_MAX 0x10u
+/* Diagnostic option of the attention stage: no wave takes the zero softmax
+ * reference (weights 2^x unshifted, used where every logit bound of the wave
+ * is small); the per-row bound is the reference instead, so tests can check
+ * that path on ordinary inputs. Same results up to rounding. */
+#define GEMMA3_STAGE_FORCE_BOUND_REF 0x20u
 
 /* Decode stages ("Gemma 3 Attention Block", How it works, Cache). */
 #define GEMMA3_DSTAGE_QKV_PROJ 0x1u /* raw fp32 projections of the B new tokens              */

@@ -94,6 +94,51 @@ def test_prefill_bf16_exact_max_pass(gpu_lib, case):
     assert_bf16_close(f64(y), oracle_prefill(inp, kw), "y")
 
 
+@pytest.mark.parametrize("case", EXACT_MAX, ids=[str(c[:8]) for c in EXACT_MAX])
+def test_prefill_bf16_bound_ref_pass(gpu_lib, case):
+    """The per-row logit bound as the softmax reference (the path of waves
+    whose bound is too large for the zero reference), forced for every wave:
+    masked and full tiles, padding, local windows, split key ranges."""
+    B, T, D, H, Hk, d_h, t, Wn, lens = case
+    log(f"case {case}")
+    inp = small_prefill_inputs(8, B, T, D, H, Hk, d_h, "bf16", lens)
+    kw = _kw(H, Hk, d_h, t, Wn)
+    y = gpu_prefill(gpu_lib, inp, kw, stages=gpu_lib.STAGE_ALL | gpu_lib.STAGE_FORCE_BOUND_REF)
+    assert_bf16_close(f64(y), oracle_prefill(inp, kw), "y")
+
+
+@pytest.mark.parametrize("d_h", [64, 128, 256])
+def test_softmax_reference_choice(gpu_lib, d_h):
+    """Which reference a wave takes follows its rows' logit bounds
+    U_t = |q_t| sqrt(d_h) max|1 + gamma_k| (base-2 units, 1% margin). All
+    U_t <= 40 (ordinary query scales): the zero reference at d_h <= 128, which
+    differs from the forced bound reference in rounding only (d_h = 256 has
+    no zero-reference copy of its tile loop: bit for bit the bound reference).
+    U_t in (40, 50]: the bound reference, bit for bit what forcing it gives.
+    Every result against the oracle."""
+    B, T, D, H, Hk = 1, 260, 512, 4, 2
+    kw_of = lambda alpha: _kw(H, Hk, d_h, L, 90, alpha=alpha)
+    inp = small_prefill_inputs(11, B, T, D, H, Hk, d_h, "bf16")
+    gmax = np.max(np.abs(1.0 + f64(inp["gamma_k"])))
+    _, it1 = oracle_prefill(inp, kw_of(1.0), return_intermediates=True)
+    u1 = np.linalg.norm(it1["q_tilde"], axis=-1) * math.log2(math.e) * math.sqrt(d_h) * gmax * 1.01
+    alpha = 45.0 / float(np.median(u1))
+    assert 40.5 < (u1 * alpha).min() and (u1 * alpha).max() < 49.5
+    kw = kw_of(alpha)
+    y_nat = gpu_prefill(gpu_lib, inp, kw)
+    y_bnd = gpu_prefill(gpu_lib, inp, kw, stages=gpu_lib.STAGE_ALL | gpu_lib.STAGE_FORCE_BOUND_REF)
+    assert torch.equal(y_nat, y_bnd)
+    assert_bf16_close(f64(y_nat), oracle_prefill(inp, kw), "y (bound reference)")
+    kw0 = kw_of(None)
+    assert (u1 * kw0["query_scale"]).max() < 39.5
+    y0 = gpu_prefill(gpu_lib, inp, kw0)
+    y0b = gpu_prefill(gpu_lib, inp, kw0, stages=gpu_lib.STAGE_ALL | gpu_lib.STAGE_FORCE_BOUND_REF)
+    assert torch.equal(y0, y0b) == (d_h == 256)
+    ref0 = oracle_prefill(inp, kw0)
+    assert_bf16_close(f64(y0), ref0, "y (zero reference)")
+    assert_bf16_close(f64(y0b), ref0, "y (forced bound reference)")
+
+
 @pytest.mark.parametrize("d_h", [64, 128, 256])
 def test_large_logits_take_exact_max_pass(gpu_lib, d_h):
     """alpha = 1 puts every row's logit bound beyond the fixed-reference range:
