@@ -36,8 +36,8 @@
 //    four 32-key slots and V^T in two tile buffers; one barrier per tile.
 //  * Split-KV: when (rows x heads) give too few workgroups to fill the chip,
 //    the key range of each query tile is cut into chunks handled by separate
-//    workgroups; a query tile with several chunks writes normalised partial
-//    outputs with their (m, l), merged by flash_combine.
+//    workgroups; a query tile with several chunks writes normalised fp32
+//    partial outputs with their (m, l), merged by flash_combine.
 #include <climits>
 #include <type_traits>
 #include <utility>
@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(kThreads, D <= 128 ? 2 : 1)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
                     const bf16 *__restrict__ gamma_k, bf16 *__restrict__ o,
-                    bf16 *__restrict__ part_o, float *__restrict__ part_ml, AttnArgs a, int gp,
+                    float *__restrict__ part_o, float *__restrict__ part_ml, AttnArgs a, int gp,
                     int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int remap,
                     int ref_flags) {
   using Cfg = AttnCfg<D>;
@@ -729,11 +729,30 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
   if (!ran) run(std::false_type{}, s0_first);
 
-  // Normalise; write the output rows (single chunk) or partials (several
-  // chunks). The K/V buffers are free after the last tile's barrier: each wave
-  // stages its 32 rows (bf16, a 16-byte pad per row) in a region of its own,
-  // then writes them back as whole rows of 16-byte pieces. A lane holds
-  // channels 16 cb + 4 q4 + [0, 4) of row 16 qb + qc.
+  // Normalise. Several chunks: each lane stores its fp32 partial output (4
+  // channels 16 cb + 4 q4 + [0, 4) of row 16 qb + qc per accumulator) and the
+  // row's (m, l) straight from registers; the merge reads them at full
+  // precision. A single chunk writes the bf16 output rows: the K/V buffers are
+  // free after the last tile's barrier, so each wave stages its 32 rows (a
+  // 16-byte pad per row) in a region of its own, then writes them back as
+  // whole rows of 16-byte pieces.
+  if (geo.n_active > 1) {  // uniform per block
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float l_tot = quad_sum(l_run[qb]);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (my_t[qb] >= a.T) continue;
+      const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t[qb];
+#pragma unroll
+      for (int cb = 0; cb < Cfg::kCB; ++cb)
+        *reinterpret_cast<f32x4 *>(part_o + row * D + 16 * cb + 4 * q4) = acc_o[qb][cb] * inv;
+      if (q4 == 0) {
+        part_ml[2 * row] = m_ref[qb];
+        part_ml[2 * row + 1] = l_tot;
+      }
+    }
+    return;
+  }
   constexpr int kPitch = 2 * D + 16;
   static_assert(4 * 32 * kPitch <= Cfg::kLdsBytes, "output staging fits the tile buffers");
   char *stage = lds + w * 32 * kPitch;
@@ -749,11 +768,6 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc_o[qb][cb][r] * inv);
       *reinterpret_cast<bf16x4 *>(stage + (16 * qb + qc) * kPitch + 2 * (16 * cb + 4 * q4)) = v;
     }
-    if (geo.n_active > 1 && q4 == 0 && my_t[qb] < a.T) {
-      const size_t row = (((size_t)split * a.B + b) * a.H + h) * a.T + my_t[qb];
-      part_ml[2 * row] = m_ref[qb];
-      part_ml[2 * row + 1] = l_tot;
-    }
   }
   // the same wave reads its region back (LDS keeps a wave's accesses in order)
 #pragma unroll
@@ -763,9 +777,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int t = wq0 + r;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + 16 * c);
     if (t >= a.T) continue;
-    bf16 *dst = geo.n_active == 1
-                    ? o + ((size_t)b * a.T + t) * ((size_t)a.H * D) + (size_t)h * D
-                    : part_o + ((((size_t)split * a.B + b) * a.H + h) * a.T + t) * D;
+    bf16 *dst = o + ((size_t)b * a.T + t) * ((size_t)a.H * D) + (size_t)h * D;
     *reinterpret_cast<u32x4 *>(dst + 8 * c) = v;
   }
 }
@@ -775,15 +787,15 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // workgroups per query tile (blockIdx.x in the attention kernel's base
 // order); tiles with a single chunk were written by the attention kernel and
 // exit at once. A thread handles 8 channels of a row per item: every chunk's
-// 16-byte piece and (m, l) pair of the item are loaded before any
-// arithmetic, several items at a time (one round trip per batch).
+// 32 bytes of fp32 partial output and (m, l) pair of the item are loaded
+// before any arithmetic, several items at a time (one round trip per batch).
 constexpr int kCombineItems = 2;   // items in flight per thread
 constexpr int kCombineSlices = 8;  // workgroups per query tile
 
 template <int D>
 __global__ void __launch_bounds__(256)
 flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
-              const bf16 *__restrict__ part_o, const float *__restrict__ part_ml, AttnArgs a,
+              const float *__restrict__ part_o, const float *__restrict__ part_ml, AttnArgs a,
               int gp, int n_qtiles, int n_hgrp, int n_split, int chunk_keys, int rpw) {
   const Geo geo = geometry(a, kv_len, blockIdx.x, gp, n_qtiles, n_hgrp, chunk_keys, rpw);
   if (geo.n_active <= 1) return;  // uniform per block
@@ -796,7 +808,7 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
   for (int base = blockIdx.y * 256 + threadIdx.x; base < n_items;
        base += 256 * kCombineSlices * kCombineItems) {
     float w[kCombineItems][8], lw[kCombineItems][8];
-    u32x4 v[kCombineItems][8];
+    f32x4 v[kCombineItems][8][2];
 #pragma unroll
     for (int u = 0; u < kCombineItems; ++u) {
       const int item = base + 256 * kCombineSlices * u;
@@ -807,13 +819,15 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
       for (int j = 0; j < 8; ++j) {
         w[u][j] = -INFINITY;
         lw[u][j] = 0.f;
-        v[u][j] = u32x4{0, 0, 0, 0};
+        v[u][j][0] = v[u][j][1] = f32x4{};
         if (ok && j < na) {
           const size_t row = (((size_t)j * a.B + geo.b) * a.H + h) * a.T + t;
           const float2 ml = *reinterpret_cast<const float2 *>(part_ml + 2 * row);
           w[u][j] = ml.x;  // m_j
           lw[u][j] = ml.y; // l_j
-          v[u][j] = *reinterpret_cast<const u32x4 *>(part_o + row * D + 8 * c8);
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            v[u][j][e] = *reinterpret_cast<const f32x4 *>(part_o + row * D + 8 * c8 + 4 * e);
         }
       }
     }
@@ -833,9 +847,8 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
         if (j >= na) break;
         const float wl = exp2f(w[u][j] - mu) * lw[u][j];
         den += wl;
-        const bf16x8 pv = __builtin_bit_cast(bf16x8, v[u][j]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) num[i] = fmaf(wl, (float)pv[i], num[i]);
+        for (int i = 0; i < 8; ++i) num[i] = fmaf(wl, v[u][j][i >> 2][i & 3], num[i]);
       }
       bf16x8 out;
 #pragma unroll
@@ -914,7 +927,7 @@ Plan plan(const AttnArgs &a) {
 
 template <int D, bool kCache>
 hipError_t launch_kernels(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
-                     const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml,
+                     const bf16 *gamma_k, bf16 *o, float *part_o, float *part_ml,
                      const AttnArgs &a, const Plan &p, int ref_flags, hipStream_t s) {
   using Cfg = AttnCfg<D>;
   auto kern = flash_attn_fwd_bf16<D, kCache>;
@@ -936,7 +949,7 @@ hipError_t launch_kernels(const bf16 *q, const bf16 *k, const bf16 *vt, const in
 
 template <int D>
 hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
-                    const bf16 *gamma_k, bf16 *o, bf16 *part_o, float *part_ml, const AttnArgs &a,
+                    const bf16 *gamma_k, bf16 *o, float *part_o, float *part_ml, const AttnArgs &a,
                     int ref_flags, hipStream_t s) {
   const Plan p = plan(a);
   if (a.S_cache > 0)
@@ -951,7 +964,7 @@ hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t 
 size_t flash_attn_partial_bytes(const AttnArgs &a) {
   const Plan p = plan(a);
   if (p.n_split == 1) return 0;
-  return (size_t)p.n_split * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8);
+  return (size_t)p.n_split * a.B * a.H * a.T * ((size_t)a.d_h * 4 + 8);
 }
 
 size_t flash_attn_partial_bytes_bound(const AttnArgs &a) {
@@ -959,7 +972,7 @@ size_t flash_attn_partial_bytes_bound(const AttnArgs &a) {
   // alone leave CUs idle, and that count does not depend on q0
   const Plan p = plan(a);
   if (p.n_base >= (long)kCUs * wgs_per_cu(a.d_h)) return 0;
-  return (size_t)8 * a.B * a.H * a.T * ((size_t)a.d_h * 2 + 8);
+  return (size_t)8 * a.B * a.H * a.T * ((size_t)a.d_h * 4 + 8);
 }
 
 hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
@@ -967,8 +980,8 @@ hipError_t launch_flash_attn_bf16(const bf16 *q, const bf16 *k, const bf16 *vt,
                                   void *partial, const AttnArgs &a, int ref_flags,
                                   hipStream_t s) {
   const size_t rows = (size_t)plan(a).n_split * a.B * a.H * a.T;
-  bf16 *part_o = (bf16 *)partial;
-  float *part_ml = partial ? (float *)((char *)partial + rows * a.d_h * 2) : nullptr;
+  float *part_o = (float *)partial;
+  float *part_ml = partial ? (float *)((char *)partial + rows * a.d_h * 4) : nullptr;
   switch (a.d_h) {
     case 64: return launch_d<64>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, ref_flags, s);
     case 128: return launch_d<128>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, ref_flags, s);
