@@ -26,7 +26,9 @@
 //  * Softmax reference: a per-row upper bound of the logits from the query
 //    and key norms, fixed for the whole row, so there is no running maximum
 //    and no rescale of O (rows where that bound is too loose take the exact
-//    row maxima from a first pass over their keys). l and O share the
+//    row maxima from a first pass over their keys; at d_h <= 128 a wave
+//    whose bounds are all small takes the reference 0, which lets its S
+//    accumulators start from the MFMA's inline zero). l and O share the
 //    reference, which cancels in O / l.
 //  * Tiles move global -> LDS with direct loads (16 bytes per lane, no
 //    staging registers) into XOR-swizzled, unpadded layouts that keep the
