@@ -462,14 +462,19 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // S of a 32-key half: 4 accumulators, quad qd = 2 qb + j (row block qb,
   // sub-tile j); lane element r of quad qd is key 8 q4 + 4 j + r of the half.
   using SHalf = f32x4[4];
-  // Which logits of a 32-key half starting at key s0 are allowed (bit 4 qd + r
-  // for element r of quad qd); blocked ones become -inf. Allowed keys of a
-  // row form one interval; relative to the lane's first key s0 + 8 q4, element
-  // r of sub-tile j sits at offset 4 j + r, so one unsigned compare per
-  // element tests lo <= offset <= hi.
-  auto mask_bits = [&](int s0) {
+  // Which logits of a 32-key half starting at key s0 are allowed; blocked
+  // ones become -inf. Allowed keys of a row form one interval; relative to
+  // the lane's first key s0 + 8 q4, element r of sub-tile j sits at offset
+  // e = 4 j + r, so one subtraction and one unsigned compare per element test
+  // lo <= e <= hi: allowed(qb, e) = (unsigned)(e - lo[qb]) <= span[qb].
+  struct HalfMask {
+    int lo[kQB];
+    uint32_t span[kQB];
+    DEVI bool allowed(int qb, int e) const { return (uint32_t)(e - lo[qb]) <= span[qb]; }
+  };
+  auto mask_range = [&](int s0) {
     const int base = s0 + 8 * q4;
-    uint32_t bits = 0;
+    HalfMask hm;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const int ta = a.q0 + my_t[qb];  // absolute index of the query
@@ -479,11 +484,10 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         lo = 1 << 30;
         hi = lo;
       }
-      const uint32_t span = (uint32_t)(hi - lo);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bits |= ((uint32_t)(e - lo) <= span ? 1u : 0u) << (8 * qb + e);
+      hm.lo[qb] = lo;
+      hm.span[qb] = (uint32_t)(hi - lo);
     }
-    return bits;
+    return hm;
   };
   auto qk_half = [&](int slot, SHalf &sv, bool from_ref) {
 #pragma unroll
@@ -559,7 +563,8 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     bf16x8 fr[4], frn[4];
     // masked tiles: allowed-logit bits of the current half (applied as the
     // exponentials read the S accumulators)
-    uint32_t mb = kMasked ? mask_bits(s_tile) : 0xFFFFu;
+    HalfMask hm;
+    if constexpr (kMasked) hm = mask_range(s_tile);
     read_frags(std::integral_constant<int, 0>{}, fr);
     static_for<2 * kNGT>([&](auto g_tag) {
       constexpr int gi = decltype(g_tag)::value;
@@ -569,7 +574,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       SHalf &s_cur = kb == 0 ? s_a : s_b;
       SHalf &s_nxt = kb == 0 ? s_b : s_a;
       if constexpr (g == 0) {
-        if (kb == 1 && kMasked) mb = mask_bits(s_tile + 32);
+        if constexpr (kb == 1 && kMasked) hm = mask_range(s_tile + 32);
       }
       if constexpr (gi + 1 < 2 * kNGT) read_frags(std::integral_constant<int, gi + 1>{}, frn);
       if constexpr (kSActive) {
@@ -600,7 +605,8 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int i = 0; i < 4; ++i) {
             const float x = s_cur[qd][i];
             ex[4 * qd + i] =
-                __builtin_amdgcn_exp2f(!kMasked || ((mb >> (4 * qd + i)) & 1) ? x : -INFINITY);
+                __builtin_amdgcn_exp2f(!kMasked || hm.allowed(qd >> 1, 4 * (qd & 1) + i) ? x
+                                                                                 : -INFINITY);
           }
         }
         if (Sc::c_grp(qd) == g) {
@@ -700,12 +706,13 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int kbh = 0; kbh < 2; ++kbh) {
         SHalf sv;
         qk_half(kbh, sv, false);
-        const uint32_t bits = mask_bits(my_begin + it * kBN + 32 * kbh);
+        const HalfMask hk = mask_range(my_begin + it * kBN + 32 * kbh);
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            mx[qd >> 1] = fmaxf(mx[qd >> 1], (bits >> (4 * qd + r)) & 1 ? sv[qd][r] : -INFINITY);
+            mx[qd >> 1] = fmaxf(mx[qd >> 1],
+                                hk.allowed(qd >> 1, 4 * (qd & 1) + r) ? sv[qd][r] : -INFINITY);
       }
       __syncthreads();  // reads done before the next tile overwrites the slots
     }
