@@ -208,9 +208,15 @@ DEVI void qkv_epilogue_impl(const typename Mfma<kMf>::Acc (&acc)[kFM][kFN], char
     }
   } else {
     // V^T: one lane per (tile column, 8 consecutive rows); 16-byte stores when
-    // the 8 tokens sit in one batch row at an 8-aligned position.
-    for (int item = tid; item < BN * (BM / 8); item += kThreads) {
-      const int c = item % BN, rg = item / BN;
+    // the 8 tokens sit in one batch row at an 8-aligned position. Eight
+    // consecutive lanes take eight consecutive row groups of one column, so a
+    // store instruction writes whole 128-byte lines of 8 V^T rows (consecutive
+    // lanes on consecutive columns wrote 64 lines 16 bytes each).
+    constexpr int kRG = BM / 8;  // row groups of the tile
+    static_assert(kRG % 8 == 0, "row groups in runs of eight");
+    for (int item = tid; item < BN * kRG; item += kThreads) {
+      const int rg_lo = item & 7, cr = item >> 3;  // cr = c + BN (rg / 8)
+      const int c = cr % BN, rg = 8 * (cr / BN) + rg_lo;
       const int row = rg * 8, m = m0 + row;
       if (m >= M) continue;
       const int head = head0 + c / d_h, ch = c % d_h, kh = head - ep.H - ep.Hk;
