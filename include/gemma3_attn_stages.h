@@ -57,8 +57,9 @@ extern "C" {
  *                                 alpha log2(e), the attention kernel's base-2 logit scale)
  *   k    [B, H_kv, T_pad, d_h]    normalised, rotated (rows T..T_pad-1 zero)
  *   vt   [B, H_kv, d_h, T_pad]    V transposed (columns T..T_pad-1 zero)
- *   attn_part                     split-KV partial outputs of the attention stage
- *                                 (only when the grid is too small to fill the GPU)
+ *   attn_part fp32                split-KV partial outputs of the attention stage,
+ *                                 [chunks, B, H, T, d_h] then (m, l) per row (only
+ *                                 when the grid is too small to fill the GPU)
  *   T_pad = T rounded up to a multiple of 64.
  * Decode (S > 0):
  *   qkv  fp32 [ksplit_qkv, B, (H + 2 H_kv) d_h]  projections (ksplit_qkv is 1)
