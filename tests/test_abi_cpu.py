@@ -33,6 +33,16 @@ def test_library_exports_every_declared_symbol():
     assert set(lib.EXPORTED) == names
 
 
+def test_stage_constants_match_the_header():
+    """Every GEMMA3_STAGE_* / GEMMA3_DSTAGE_* bit of the stages header has the
+    same value in the Python binding (STAGE_* / DSTAGE_*)."""
+    text = open(os.path.join(ROOT, "include", "gemma3_attn_stages.h")).read()
+    defs = re.findall(r"#define GEMMA3_(D?STAGE_\w+)\s+(0x[0-9A-Fa-f]+)u", text)
+    assert len(defs) >= 12
+    for name, val in defs:
+        assert getattr(lib, name) == int(val, 16), name
+
+
 def test_abi_version_and_status_strings():
     assert lib.abi_version() == 3
     for st in range(10):
