@@ -7,15 +7,16 @@
 //  * Blocked logits get exactly zero weight, as K_MASK does in fp32 whenever a
 //    row has an allowed key; the fill value itself is never formed. Tiles that
 //    no row of the workgroup may see are never visited.
-//  * One workgroup = 4 waves = 128 query rows of one KV head: the query heads
-//    of a GQA group (up to 4) are packed into the workgroup, so each K/V tile
-//    staged in LDS feeds every query head that reads it. At d_h <= 128 two
-//    workgroups share each CU (registers capped at 256 per lane).
-//  * A wave owns 32 query rows as two blocks of 16 and computes S^T = K Q^T
-//    with 16x16x32 bf16 MFMAs (gfx950 sustains a higher shader clock on them
-//    than on 32x32x16 ones: 2.2-2.3 against 1.75-1.95 GHz measured under a
-//    dense load). Each K fragment (16 keys x 32 channels) feeds both row
-//    blocks. Lane l owns query l % 16 of each block and, of every 32-key
+//  * One workgroup = 4 waves = 128 query rows of one KV head (64 with one
+//    row block per wave): the query heads of a GQA group (up to 4) are packed
+//    into the workgroup, so each K/V tile staged in LDS feeds every query
+//    head that reads it. At d_h <= 128 two workgroups share each CU
+//    (registers capped at 256 per lane).
+//  * A wave owns 32 query rows as two blocks of 16 (one block where two
+//    would leave half the chip idle) and computes S^T = K Q^T with 16x16x32
+//    bf16 MFMAs (gfx950 sustains a higher shader clock on them than on
+//    32x32x16 ones: 2.2-2.3 against 1.75-1.95 GHz measured under a dense
+//    load). Each K fragment (16 keys x 32 channels) feeds every row block. Lane l owns query l % 16 of each block and, of every 32-key
 //    half, the 8 keys 8 (l / 16) .. + 7: the K rows of a half are fed as two
 //    16-key sub-tiles in the order pi(j, i) (sub-tile j, MFMA row i), so that
 //    a lane's S^T accumulators of the two sub-tiles are, in register order,
@@ -51,7 +52,6 @@ namespace {
 
 constexpr int kBN = 64;       // keys per tile
 constexpr int kThreads = 256; // 4 waves
-constexpr int kQB = 2;        // 16-row query blocks per wave
 
 template <int D> struct AttnCfg {
   static constexpr int kKRowBytes = 2 * D;            // one key row of K
@@ -118,25 +118,25 @@ template <int N, typename F> DEVI void static_for(F &&f) {
 // Group schedule of one 64-key tile (see the tile step in the attention
 // kernel): for each 32-key half, kNG groups of 4 K fragments (8 S MFMAs) then
 // kPG groups of 4 V^T fragments (8 PV MFMAs).
-template <int D> struct TileSched {
+template <int D, int kQB> struct TileSched {
   using Cfg = AttnCfg<D>;
+  static constexpr int kNQ = 2 * kQB;            // weight quads of a half
   static constexpr int kG = 4;                   // fragments per group
   static constexpr int kNG = 2 * Cfg::kKS / kG;  // S groups per half
   static constexpr int kPG = Cfg::kCB / kG;      // PV groups per half
   static constexpr int kNGT = kNG + kPG;         // groups per half
-  static constexpr int kQPG = 4 / kNG;           // weight quads whose exponentials share an S group
   static constexpr int kPieces = 2 * Cfg::kKHalfLoads + Cfg::kVLoads;  // prefetch loads per tile
   static constexpr int kPPG = (kPieces + kNGT - 1) / kNGT;             // of them per first-half group
-  // The 16 weights of a half (4 quads of 4: quad 2 b + j holds row block b,
-  // sub-tile j) pass three stages: exp2, packing to bf16 (the PV B operand of
-  // row block b), and the row sum of the packed values (l sums the
-  // bf16-rounded weights the PV MFMAs use, so numerator and denominator of
-  // O / l carry the same rounding). Exps of quad q and their packing sit in
-  // S group q / kQPG (every PV group takes both row blocks' operands, so all
-  // packing precedes the first PV group; packing right after the exps keeps
-  // the exponentials' registers short-lived), its sum one group later.
-  static constexpr int e_grp(int qd) { return qd / kQPG; }
-  static constexpr int c_grp(int qd) { return qd / kQPG; }
+  // The 8 kQB weights of a lane's half (kNQ quads of 4: quad 2 b + j holds
+  // row block b, sub-tile j) pass three stages: exp2, packing to bf16 (the PV
+  // B operand of row block b), and the row sum of the packed values (l sums
+  // the bf16-rounded weights the PV MFMAs use, so numerator and denominator
+  // of O / l carry the same rounding). Exps of quad q and their packing sit
+  // in S group q kNG / kNQ (every PV group takes all row blocks' operands, so
+  // all packing precedes the first PV group; packing right after the exps
+  // keeps the exponentials' registers short-lived), its sum one group later.
+  static constexpr int e_grp(int qd) { return qd * kNG / kNQ; }
+  static constexpr int c_grp(int qd) { return e_grp(qd); }
   static constexpr int d_grp(int qd) { return c_grp(qd) + 1 < kNGT ? c_grp(qd) + 1 : kNGT - 1; }
 };
 
@@ -175,7 +175,9 @@ DEVI Geo geometry(const AttnArgs &a, const int32_t *kv_len, int base_id, int gp,
 // transposing LDS read of gfx950 (two 4-key halves). Rows at or past the
 // valid length are loaded as copies of the last valid row, so whatever the
 // slots beyond it hold (NaN included) never reaches the arithmetic.
-template <int D, bool kCache>
+// kQB: 16-row query blocks per wave (two, or one for grids too small to fill
+// the chip with two).
+template <int D, bool kCache, int kQB>
 __global__ void __launch_bounds__(kThreads, D <= 128 ? 2 : 1)
 flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const bf16 *__restrict__ vt, const int32_t *__restrict__ kv_len,
@@ -461,7 +463,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // S of a 32-key half: 4 accumulators, quad qd = 2 qb + j (row block qb,
   // sub-tile j); lane element r of quad qd is key 8 q4 + 4 j + r of the half.
-  using SHalf = f32x4[4];
+  using SHalf = f32x4[2 * kQB];
   // Which logits of a 32-key half starting at key s0 are allowed; blocked
   // ones become -inf. Allowed keys of a row form one interval; relative to
   // the lane's first key s0 + 8 q4, element r of sub-tile j sits at offset
@@ -491,7 +493,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
   auto qk_half = [&](int slot, SHalf &sv, bool from_ref) {
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) sv[qd] = from_ref ? splat_ref(qd >> 1) : f32x4{};
+    for (int qd = 0; qd < 2 * kQB; ++qd) sv[qd] = from_ref ? splat_ref(qd >> 1) : f32x4{};
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
 #pragma unroll
@@ -517,7 +519,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // more registers than the budget allows (spills at d_h = 128 and 256) and
   // ran slower. par_tag: the parity of `it` when known at compile time (then
   // every LDS slot and buffer index is an immediate), else -1.
-  using Sc = TileSched<D>;
+  using Sc = TileSched<D, kQB>;
   constexpr int kG = Sc::kG, kNG = Sc::kNG, kNGT = Sc::kNGT, kPieces = Sc::kPieces, kPPG = Sc::kPPG;
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
@@ -558,7 +560,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         issue_v_piece(it + 1, par ^ 1, pc - 2 * Cfg::kKHalfLoads);
     };
 
-    float ex[16];
+    float ex[8 * kQB];
     bf16x8 pf[kQB];
     bf16x8 fr[4], frn[4];
     // masked tiles: allowed-logit bits of the current half (applied as the
@@ -599,7 +601,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
       }
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
+      for (int qd = 0; qd < 2 * kQB; ++qd) {
         if (Sc::e_grp(qd) == g) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -688,7 +690,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     qk_half(0, s0_first, !zero_ref);
   } else {
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) s0_first[qd] = f32x4{};
+    for (int qd = 0; qd < 2 * kQB; ++qd) s0_first[qd] = f32x4{};
   }
   if (!__syncthreads_and(bound_ok) || (ref_flags & kRefExactMax)) {
     // Exact row maxima (log2 units) over the allowed keys: each tile's two K
@@ -708,7 +710,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         qk_half(kbh, sv, false);
         const HalfMask hk = mask_range(my_begin + it * kBN + 32 * kbh);
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
+        for (int qd = 0; qd < 2 * kQB; ++qd)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             mx[qd >> 1] = fmaxf(mx[qd >> 1],
@@ -763,8 +765,8 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     return;
   }
   constexpr int kPitch = 2 * D + 16;
-  static_assert(4 * 32 * kPitch <= Cfg::kLdsBytes, "output staging fits the tile buffers");
-  char *stage = lds + w * 32 * kPitch;
+  static_assert(4 * kRPW * kPitch <= Cfg::kLdsBytes, "output staging fits the tile buffers");
+  char *stage = lds + w * kRPW * kPitch;
   constexpr int kPieces16 = D / 8;  // 16-byte pieces per row
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -780,7 +782,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
   // the same wave reads its region back (LDS keeps a wave's accesses in order)
 #pragma unroll
-  for (int i = 0; i < 32 * kPieces16 / kWave; ++i) {
+  for (int i = 0; i < kRPW * kPieces16 / kWave; ++i) {
     const int item = i * kWave + lane;
     const int r = item / kPieces16, c = item % kPieces16;
     const int t = wq0 + r;
@@ -869,7 +871,7 @@ flash_combine(const int32_t *__restrict__ kv_len, bf16 *__restrict__ o,
 }
 
 struct Plan {
-  int gp, n_qtiles, n_hgrp, n_split, chunk_keys, remap;
+  int qb, gp, n_qtiles, n_hgrp, n_split, chunk_keys, remap;
   long n_base;
 };
 
@@ -883,13 +885,14 @@ constexpr int kCUs = 256;  // MI355X compute units
 // 256 registers per lane each), one at d_h = 256 (131 KB, 512 registers)
 constexpr int wgs_per_cu(int d_h) { return d_h <= 128 ? 2 : 1; }
 
-Plan plan(const AttnArgs &a) {
+Plan plan_qb(const AttnArgs &a, int qb) {
   Plan p;
+  p.qb = qb;
   const int G = a.H / a.Hk;
   p.gp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   // (a window covering every key takes the global layer's plan and bits)
   const int slots = kCUs * wgs_per_cu(a.d_h);  // workgroups running at once
-  const int TQ = 16 * kQB * (4 / p.gp);
+  const int TQ = 16 * qb * (4 / p.gp);
   p.n_qtiles = div_up_h(a.T, TQ);
   p.n_hgrp = G / p.gp;
   const long n_groups = (long)a.B * a.Hk * p.n_hgrp;
@@ -934,12 +937,26 @@ Plan plan(const AttnArgs &a) {
   return p;
 }
 
-template <int D, bool kCache>
+// One row block per wave (twice the workgroups, each with half the rows)
+// where two blocks leave at least half the chip idle on a sliding-window layer
+// at d_h = 256 (one workgroup per CU): its query tiles all take about the
+// same number of keys, so the doubled grid fills the CUs in one round.
+// Measured on the 1B-shaped local layer: 25.5 -> 20.3 us. On causal global
+// layers of that size the split plan with two blocks stays faster (61
+// against 72 us unsplit with one block).
+Plan plan(const AttnArgs &a) {
+  const Plan p2 = plan_qb(a, 2);
+  if (a.local && a.d_h == 256 && 2 * p2.n_base <= (long)kCUs * wgs_per_cu(a.d_h))
+    return plan_qb(a, 1);
+  return p2;
+}
+
+template <int D, bool kCache, int kQB>
 hipError_t launch_kernels(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t *kv_len,
                      const bf16 *gamma_k, bf16 *o, float *part_o, float *part_ml,
                      const AttnArgs &a, const Plan &p, int ref_flags, hipStream_t s) {
   using Cfg = AttnCfg<D>;
-  auto kern = flash_attn_fwd_bf16<D, kCache>;
+  auto kern = flash_attn_fwd_bf16<D, kCache, kQB>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
@@ -961,11 +978,17 @@ hipError_t launch_d(const bf16 *q, const bf16 *k, const bf16 *vt, const int32_t 
                     const bf16 *gamma_k, bf16 *o, float *part_o, float *part_ml, const AttnArgs &a,
                     int ref_flags, hipStream_t s) {
   const Plan p = plan(a);
-  if (a.S_cache > 0)
-    return launch_kernels<D, true>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p,
-                                   ref_flags, s);
-  return launch_kernels<D, false>(q, k, vt, kv_len, gamma_k, o, part_o, part_ml, a, p, ref_flags,
-                                  s);
+  if constexpr (D == 256) {
+    if (p.qb == 1)
+      return a.S_cache > 0 ? launch_kernels<D, true, 1>(q, k, vt, kv_len, gamma_k, o, part_o,
+                                                        part_ml, a, p, ref_flags, s)
+                           : launch_kernels<D, false, 1>(q, k, vt, kv_len, gamma_k, o, part_o,
+                                                         part_ml, a, p, ref_flags, s);
+  }
+  return a.S_cache > 0 ? launch_kernels<D, true, 2>(q, k, vt, kv_len, gamma_k, o, part_o,
+                                                    part_ml, a, p, ref_flags, s)
+                       : launch_kernels<D, false, 2>(q, k, vt, kv_len, gamma_k, o, part_o,
+                                                     part_ml, a, p, ref_flags, s);
 }
 
 }  // namespace
@@ -979,8 +1002,7 @@ size_t flash_attn_partial_bytes(const AttnArgs &a) {
 size_t flash_attn_partial_bytes_bound(const AttnArgs &a) {
   // key ranges are split (into at most 8 chunks) only when the query tiles
   // alone leave CUs idle, and that count does not depend on q0
-  const Plan p = plan(a);
-  if (p.n_base >= (long)kCUs * wgs_per_cu(a.d_h)) return 0;
+  if (plan_qb(a, 2).n_base >= (long)kCUs * wgs_per_cu(a.d_h)) return 0;
   return (size_t)8 * a.B * a.H * a.T * ((size_t)a.d_h * 4 + 8);
 }
 
