@@ -508,7 +508,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // One step per 64-key tile it, as two 32-key halves (K halves u = 2 it and
   // 2 it + 1). While the softmax and PV of half u run, the S of half u + 1
   // goes to the matrix pipe. The work is a fixed sequence of groups of 4
-  // fragments (8 MFMAs, each fragment feeding both row blocks): for each
+  // fragments (one MFMA per row block for each fragment): for each
   // half, kNG groups of S MFMAs then kPG groups of PV MFMAs. The fragments of
   // group i + 1 are read from LDS while group i runs (across the halves; only
   // the tile's first group waits for its reads), each group carries its
@@ -744,7 +744,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // channels 16 cb + 4 q4 + [0, 4) of row 16 qb + qc per accumulator) and the
   // row's (m, l) straight from registers; the merge reads them at full
   // precision. A single chunk writes the bf16 output rows: the K/V buffers are
-  // free after the last tile's barrier, so each wave stages its 32 rows (a
+  // free after the last tile's barrier, so each wave stages its 16 kQB rows (a
   // 16-byte pad per row) in a region of its own, then writes them back as
   // whole rows of 16-byte pieces.
   if (geo.n_active > 1) {  // uniform per block
