@@ -326,10 +326,12 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       qf[qb][ks] = ok ? *reinterpret_cast<const bf16x8 *>(qp + 32 * ks) : bf16x8{};
   }
 
-  // max_c |1 + gamma_k[c]| (bounds the key norms, below); its loads, the Q
-  // fragments and the first tiles are in flight together
+  // max_c |1 + gamma_k[c]| (bounds the key norms, below), every wave over all
+  // d_h channels (no workgroup barrier for it); its loads, the Q fragments
+  // and the first tiles are in flight together
   float gmax = 0.f;
-  for (int c = tid; c < D; c += kThreads) gmax = fmaxf(gmax, fabsf(1.f + (float)gamma_k[c]));
+#pragma unroll
+  for (int c = lane; c < D; c += kWave) gmax = fmaxf(gmax, fabsf(1.f + (float)gamma_k[c]));
   // Every outstanding load (Q fragments, first tiles) lands before the loop,
   // so inside it only the newest prefetches are ever pending.
   publish_tiles();
@@ -401,11 +403,7 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // in a pass over its key tiles and uses those instead. Either way O and l
   // share the reference, which cancels in O / l. The S accumulators start at
   // -U_t, so the MFMAs deliver x - U_t directly.
-  __shared__ float red4[4];
   gmax = wave_max(gmax);
-  if (lane == 0) red4[w] = gmax;
-  __syncthreads();
-  gmax = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
   float m_ref[kQB];
   float negu[kQB];  // -U_t (0 for a row without keys), the S accumulators' start
   auto neg_ref = [&](int qb) { return m_ref[qb] == -INFINITY ? 0.f : -m_ref[qb]; };
@@ -429,13 +427,13 @@ flash_attn_fwd_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   bool bound_ok = true;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
-    float qq = 0.f;
+    float qq = 0.f;  // |q_t|^2: bf16 pairs squared and summed in fp32
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKS; ++ks)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = (float)qf[qb][ks][j];
-        qq = fmaf(v, v, qq);
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 pr = {qf[qb][ks][2 * j], qf[qb][ks][2 * j + 1]};
+        qq = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, qq, false);
       }
     qq = quad_sum(qq);
     // 1% margin covers the bf16 rounding of the stored keys
