@@ -28,7 +28,12 @@
 
 namespace {
 
-constexpr int kDecThreads = 256;
+// threads of a partial workgroup: 4 waves, or 8 on sliding-window layers
+// (bf16, at most two query heads per workgroup), whose few workgroups (one
+// per (row, chunk, KV head group), about one per CU) then keep twice the
+// loads in flight (the 12B-like local attention stage 38.3 -> 37.2 us; the
+// many-workgroup global layer is slower so)
+constexpr int kDecThreadsGlobal = 256, kDecThreadsLocal = 512;
 constexpr int kDecUnroll = 4;  // slots per slot group per iteration
 constexpr int kChansPerLane = 16;
 
@@ -86,7 +91,7 @@ DEVI void row_range(const int32_t *pos, int b, int S, int local, int window, int
 // forms the step's own key and value, writes them to that cache slot (head
 // group 0 only) and uses them for that slot. The first round of cache loads is
 // issued before this set-up, so its latency hides the norm and RoPE work.
-template <typename T, int D, int GQ>
+template <typename T, int D, int GQ, int kDecThreads>
 __global__ void __launch_bounds__(kDecThreads)
 decode_attn_partial(const float *__restrict__ qkv, const T *__restrict__ gamma_q,
                     const T *__restrict__ gamma_k, T *__restrict__ k_cache,
@@ -409,8 +414,20 @@ hipError_t launch_dec(const float *qkv, const T *gq, const T *gk, T *kc, T *vc,
   const int G = a.H / a.Hk;
   const int n_hgrp = G / GQ;
   dim3 grid(a.n_chunks, a.B, a.Hk * n_hgrp);
-  hipLaunchKernelGGL((decode_attn_partial<T, D, GQ>), grid, dim3(kDecThreads), 0, s, qkv, gq, gk,
-                     kc, vc, pos, part, a, n_hgrp);
+  // (8 waves only where a wave's registers fit two waves per SIMD: bf16 and
+  // at most two query heads per workgroup)
+  constexpr bool kWide = std::is_same<T, bf16>::value && GQ <= 2;
+  bool launched = false;
+  if constexpr (kWide) {
+    if (a.local) {
+      hipLaunchKernelGGL((decode_attn_partial<T, D, GQ, kDecThreadsLocal>), grid,
+                         dim3(kDecThreadsLocal), 0, s, qkv, gq, gk, kc, vc, pos, part, a, n_hgrp);
+      launched = true;
+    }
+  }
+  if (!launched)
+    hipLaunchKernelGGL((decode_attn_partial<T, D, GQ, kDecThreadsGlobal>), grid,
+                       dim3(kDecThreadsGlobal), 0, s, qkv, gq, gk, kc, vc, pos, part, a, n_hgrp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // rows of many chunks: four chunk groups per (row, head)
