@@ -219,7 +219,7 @@ def bench_prefill(args, torch, W, I, lib, dev, wid, cpu_copy=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the "
+        print(f"bench.py: the benchmark runs on one GPU only (got --gpus {args.gpus}); the "
               "multi-GPU sharding is a design note, not an implemented path.", file=sys.stderr)
         sys.exit(2)
 

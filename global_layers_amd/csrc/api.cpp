@@ -414,7 +414,7 @@ const char *gemma3_attn_status_string(int status) {
     case GEMMA3_ERR_DTYPE: return "unknown dtype or attention type";
     case GEMMA3_ERR_ROPE: return "rope_theta and rope_scale must be finite and > 0, query_scale finite";
     case GEMMA3_ERR_WORKSPACE: return "workspace is NULL or smaller than gemma3_attn_workspace_bytes()";
-    case GEMMA3_ERR_UNSUPPORTED: return "shape has no kernel in this build";
+    case GEMMA3_ERR_UNSUPPORTED: return "shape has no kernel in this library";
     case GEMMA3_ERR_HIP: return "a HIP kernel launch failed";
     case GEMMA3_ERR_ALIGN: return "pointer is not 16-byte aligned";
     case GEMMA3_ERR_SCRATCH:

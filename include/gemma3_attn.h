@@ -88,7 +88,7 @@ typedef enum {
   GEMMA3_ERR_DTYPE = 4,       /* unknown dtype or attention type */
   GEMMA3_ERR_ROPE = 5,        /* theta <= 0, scale <= 0, or a non-finite theta/scale/alpha */
   GEMMA3_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gemma3_attn_workspace_bytes */
-  GEMMA3_ERR_UNSUPPORTED = 7, /* valid shape this build has no kernel for (see below) */
+  GEMMA3_ERR_UNSUPPORTED = 7, /* valid shape this library has no kernel for (see below) */
   GEMMA3_ERR_HIP = 8,         /* a kernel launch failed */
   GEMMA3_ERR_ALIGN = 9,       /* a pointer is not 16-byte aligned */
   GEMMA3_ERR_SCRATCH = 10     /* workspace need exceeds GEMMA3_STATIC_SCRATCH_BYTES (static entry points) */
@@ -115,7 +115,7 @@ typedef struct {
 } gemma3_attn_weights;
 
 /*
- * Shapes with kernels in this build:
+ * Shapes with kernels in this library:
  *   GEMMA3_BF16: d_h in {64, 128, 256}; D % 64 == 0; H*d_h % 64 == 0;
  *                B*T < 2^31 / max(D, (H + 2 H_kv) d_h).
  *   GEMMA3_F32:  d_h in {16, 32, 64, 128, 256}; any D, H, H_kv, B, T within int32.
